@@ -1,0 +1,281 @@
+// C ABI of libidxsparse.so (declared in include/idxsparse.h): host-side
+// argument checks, workspace layout and kernel dispatch.  Nothing here
+// touches device memory contents or synchronises the device.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/idxsparse.h"
+#include "kernels.h"
+
+namespace idxs {
+
+namespace {
+
+struct Timer {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+Timer g_timers[IDX_KERNEL_COUNT];
+
+constexpr size_t WS_ALIGN = 256;
+size_t align_up(size_t v) { return (v + WS_ALIGN - 1) & ~(WS_ALIGN - 1); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+int log2i(int v) { int s = 0; while ((1 << s) < v) ++s; return s; }
+
+// Rows of the score workspace are padded to a multiple of 64 floats.
+int64_t score_stride(const idx_seqs* s) { return ((int64_t)s->max_ctx_len + 63) / 64 * 64; }
+
+int check_seqs(const idx_seqs* s) {
+  if (!s) return IDX_ERR_INVALID_ARG;
+  if (s->num_seqs < 1 || s->num_seqs > 65535) return IDX_ERR_INVALID_ARG;
+  if (s->num_tokens < 0) return IDX_ERR_INVALID_ARG;
+  if (!s->ctx_len || !aligned4(s->ctx_len)) return IDX_ERR_INVALID_ARG;
+  if (s->max_q_len < 1 || s->max_ctx_len < 1 || s->max_q_len > s->max_ctx_len) return IDX_ERR_INVALID_ARG;
+  if (s->cu_q == nullptr) {
+    if (s->num_tokens != s->num_seqs || s->max_q_len != 1) return IDX_ERR_INVALID_ARG;
+  } else if (!aligned4(s->cu_q)) {
+    return IDX_ERR_INVALID_ARG;
+  }
+  if (s->block_table) {
+    if (!aligned4(s->block_table) || s->bt_stride < 1) return IDX_ERR_INVALID_ARG;
+    if (!pow2(s->page_size) || s->page_size > 65536) return IDX_ERR_INVALID_ARG;
+    if ((int64_t)s->bt_stride * s->page_size < s->max_ctx_len) return IDX_ERR_INVALID_ARG;
+  } else if (s->seq_stride < s->max_ctx_len) {
+    return IDX_ERR_INVALID_ARG;
+  }
+  return IDX_OK;
+}
+
+SeqView make_view(const idx_seqs* s) {
+  SeqView v;
+  v.num_seqs = s->num_seqs;
+  v.num_tokens = s->num_tokens;
+  v.cu_q = s->cu_q;
+  v.ctx_len = s->ctx_len;
+  v.block_table = s->block_table;
+  v.bt_stride = s->bt_stride;
+  v.page_shift = s->block_table ? log2i(s->page_size) : 0;
+  v.seq_stride = s->seq_stride;
+  v.max_q_len = s->max_q_len;
+  v.max_ctx_len = s->max_ctx_len;
+  return v;
+}
+
+int check_indexer(const idx_seqs* seqs, const void* q_idx, int q_dtype, const void* k_idx, int k_dtype,
+                  const float* k_scale, const float* head_w, int H_I, int d_I, int top_k) {
+  int rc = check_seqs(seqs);
+  if (rc) return rc;
+  if (!q_idx || !k_idx || !head_w) return IDX_ERR_INVALID_ARG;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned4(head_w)) return IDX_ERR_INVALID_ARG;
+  if (k_scale && !aligned4(k_scale)) return IDX_ERR_INVALID_ARG;
+  if (H_I < 1 || top_k < 1) return IDX_ERR_INVALID_ARG;
+  if (q_dtype != IDX_BF16) return IDX_ERR_UNSUPPORTED;
+  if (k_dtype != IDX_BF16 && k_dtype != IDX_E4M3) return IDX_ERR_UNSUPPORTED;
+  if (H_I > 64 || (d_I != 64 && d_I != 128) || top_k > 2048) return IDX_ERR_UNSUPPORTED;
+  return IDX_OK;
+}
+
+int check_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, int kv_dtype, int top_k,
+               float softmax_scale, const float* out, const float* lse) {
+  int rc = check_seqs(seqs);
+  if (rc) return rc;
+  if (!q || !kv || !out) return IDX_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return IDX_ERR_INVALID_ARG;
+  if (lse && !aligned4(lse)) return IDX_ERR_INVALID_ARG;
+  if (H < 1 || top_k < 1) return IDX_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+    return IDX_ERR_INVALID_ARG;
+  if (kv_dtype != IDX_BF16 && kv_dtype != IDX_KV_FP8_656) return IDX_ERR_UNSUPPORTED;
+  if (H > 128 || top_k > 2048) return IDX_ERR_UNSUPPORTED;
+  return IDX_OK;
+}
+
+size_t score_ws_bytes(const idx_seqs* s) {
+  return align_up((size_t)std::max(s->num_tokens, 0) * (size_t)score_stride(s) * sizeof(float));
+}
+
+size_t attn_ws_bytes(const idx_seqs* s, int H, int top_k) {
+  const int S = attn_num_splits(s->num_tokens, H, top_k);
+  if (S <= 1) return 0;
+  const size_t parts = (size_t)std::max(s->num_tokens, 0) * S * H;
+  return align_up(parts * 512 * sizeof(float)) + align_up(parts * sizeof(float));
+}
+
+size_t idx_buf_bytes(const idx_seqs* s, int top_k) {
+  return align_up((size_t)std::max(s->num_tokens, 0) * top_k * sizeof(int32_t));
+}
+
+int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int k_dtype, const float* k_scale,
+                const float* head_w, int H_I, int d_I, int top_k, int32_t* out_idx, void* ws,
+                hipStream_t stream) {
+  ScoreParams sp;
+  sp.sv = make_view(seqs);
+  sp.q_idx = static_cast<const uint16_t*>(q_idx);
+  sp.k_idx = static_cast<const uint8_t*>(k_idx);
+  sp.k_scale = k_scale;
+  sp.head_w = head_w;
+  sp.H_I = H_I;
+  sp.d_I = d_I;
+  sp.scores = static_cast<float*>(ws);
+  sp.score_stride = score_stride(seqs);
+  if (launch_score(sp, k_dtype == IDX_E4M3, stream) != hipSuccess) return IDX_ERR_HIP;
+  TopkParams tp;
+  tp.sv = sp.sv;
+  tp.scores = sp.scores;
+  tp.score_stride = sp.score_stride;
+  tp.top_k = top_k;
+  tp.out_idx = out_idx;
+  if (launch_topk(tp, stream) != hipSuccess) return IDX_ERR_HIP;
+  return IDX_OK;
+}
+
+int run_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, int kv_dtype, const int32_t* idx,
+             int top_k, float softmax_scale, float* out, float* lse, void* ws, hipStream_t stream) {
+  AttnParams ap;
+  ap.sv = make_view(seqs);
+  ap.q = static_cast<const uint16_t*>(q);
+  ap.H = H;
+  ap.kv = static_cast<const uint8_t*>(kv);
+  ap.idx = idx;
+  ap.top_k = top_k;
+  ap.scale_log2 = softmax_scale * 1.4426950408889634f;
+  ap.out = out;
+  ap.lse = lse;
+  ap.num_splits = attn_num_splits(seqs->num_tokens, H, top_k);
+  ap.split_len = (top_k + ap.num_splits - 1) / ap.num_splits;
+  ap.split_len = (ap.split_len + ATTN_TILE - 1) / ATTN_TILE * ATTN_TILE;
+  ap.part_o = nullptr;
+  ap.part_lse = nullptr;
+  if (ap.num_splits > 1) {
+    const size_t parts = (size_t)seqs->num_tokens * ap.num_splits * H;
+    ap.part_o = static_cast<float*>(ws);
+    ap.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up(parts * 512 * sizeof(float)));
+  }
+  if (launch_attn(ap, kv_dtype == IDX_KV_FP8_656, stream) != hipSuccess) return IDX_ERR_HIP;
+  return IDX_OK;
+}
+
+}  // namespace
+
+void timer_before(int kernel, hipStream_t stream) {
+  if (g_timers[kernel].start) (void)hipEventRecord(g_timers[kernel].start, stream);
+}
+
+void timer_after(int kernel, hipStream_t stream) {
+  if (g_timers[kernel].stop) {
+    (void)hipEventRecord(g_timers[kernel].stop, stream);
+    g_timers[kernel] = Timer{};
+  }
+}
+
+}  // namespace idxs
+
+using namespace idxs;
+
+extern "C" {
+
+const char* idx_status_string(int status) {
+  switch (status) {
+    case IDX_OK: return "IDX_OK";
+    case IDX_ERR_INVALID_ARG: return "IDX_ERR_INVALID_ARG: null or misaligned pointer, or a size/bound out of range";
+    case IDX_ERR_UNSUPPORTED: return "IDX_ERR_UNSUPPORTED: dtype or dimension outside the supported set";
+    case IDX_ERR_WORKSPACE: return "IDX_ERR_WORKSPACE: workspace missing or smaller than required";
+    case IDX_ERR_HIP: return "IDX_ERR_HIP: a HIP kernel launch failed";
+    default: return "unknown idx_status";
+  }
+}
+
+size_t idx_score_topk_workspace(const idx_seqs* seqs, int H_I, int d_I, int top_k) {
+  (void)H_I; (void)d_I; (void)top_k;
+  if (check_seqs(seqs)) return 0;
+  return score_ws_bytes(seqs);
+}
+
+size_t sparse_mla_attn_workspace(const idx_seqs* seqs, int H, int top_k) {
+  if (check_seqs(seqs) || H < 1 || top_k < 1) return 0;
+  return attn_ws_bytes(seqs, H, top_k);
+}
+
+size_t idx_sparse_attn_workspace(const idx_seqs* seqs, int H_I, int d_I, int H, int top_k) {
+  if (check_seqs(seqs) || H < 1 || top_k < 1) return 0;
+  (void)H_I; (void)d_I;
+  return std::max(score_ws_bytes(seqs), attn_ws_bytes(seqs, H, top_k)) + idx_buf_bytes(seqs, top_k);
+}
+
+int idx_score_topk(const idx_seqs* seqs, const void* q_idx, int q_dtype, const void* k_idx, int k_dtype,
+                   const float* k_scale, const float* head_w, int H_I, int d_I, int top_k, int32_t* out_idx,
+                   void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_indexer(seqs, q_idx, q_dtype, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k);
+  if (rc) return rc;
+  if (!out_idx || !aligned4(out_idx)) return IDX_ERR_INVALID_ARG;
+  if (seqs->num_tokens == 0) return IDX_OK;
+  if (!ws || !aligned16(ws) || ws_bytes < score_ws_bytes(seqs)) return IDX_ERR_WORKSPACE;
+  return run_indexer(seqs, q_idx, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k, out_idx, ws,
+                     static_cast<hipStream_t>(stream));
+}
+
+int sparse_mla_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, int kv_dtype, const int32_t* idx,
+                    int top_k, float softmax_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_attn(seqs, q, H, kv, kv_dtype, top_k, softmax_scale, out, lse);
+  if (rc) return rc;
+  if (!idx || !aligned4(idx)) return IDX_ERR_INVALID_ARG;
+  if (seqs->num_tokens == 0) return IDX_OK;
+  const size_t need = attn_ws_bytes(seqs, H, top_k);
+  if (need && (!ws || !aligned16(ws) || ws_bytes < need)) return IDX_ERR_WORKSPACE;
+  return run_attn(seqs, q, H, kv, kv_dtype, idx, top_k, softmax_scale, out, lse, ws,
+                  static_cast<hipStream_t>(stream));
+}
+
+static int fused(const idx_seqs* seqs, const void* q_idx, int q_dtype, const void* k_idx, int k_dtype,
+                 const float* k_scale, const float* head_w, int H_I, int d_I, int top_k, const void* q, int H,
+                 const void* kv, int kv_dtype, float softmax_scale, float* out, float* lse, int32_t* out_idx,
+                 void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_indexer(seqs, q_idx, q_dtype, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k);
+  if (rc) return rc;
+  rc = check_attn(seqs, q, H, kv, kv_dtype, top_k, softmax_scale, out, lse);
+  if (rc) return rc;
+  if (out_idx && !aligned4(out_idx)) return IDX_ERR_INVALID_ARG;
+  if (seqs->num_tokens == 0) return IDX_OK;
+  const size_t need = idx_sparse_attn_workspace(seqs, H_I, d_I, H, top_k);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return IDX_ERR_WORKSPACE;
+  // workspace: [scratch shared by the score rows and the attention partials][indices]
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const size_t scratch = std::max(score_ws_bytes(seqs), attn_ws_bytes(seqs, H, top_k));
+  int32_t* idx = out_idx ? out_idx : reinterpret_cast<int32_t*>(base + scratch);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = run_indexer(seqs, q_idx, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k, idx, base, st);
+  if (rc) return rc;
+  return run_attn(seqs, q, H, kv, kv_dtype, idx, top_k, softmax_scale, out, lse, base, st);
+}
+
+int idx_sparse_attn_prefill(const idx_seqs* seqs, const void* q_idx, int q_dtype, const void* k_idx, int k_dtype,
+                            const float* k_scale, const float* head_w, int H_I, int d_I, int top_k, const void* q,
+                            int H, const void* kv, int kv_dtype, float softmax_scale, float* out, float* lse,
+                            int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
+  return fused(seqs, q_idx, q_dtype, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k, q, H, kv, kv_dtype,
+               softmax_scale, out, lse, out_idx, ws, ws_bytes, stream);
+}
+
+int idx_sparse_attn_decode(const idx_seqs* seqs, const void* q_idx, int q_dtype, const void* k_idx, int k_dtype,
+                           const float* k_scale, const float* head_w, int H_I, int d_I, int top_k, const void* q,
+                           int H, const void* kv, int kv_dtype, float softmax_scale, float* out, float* lse,
+                           int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
+  if (seqs && seqs->cu_q != nullptr) return IDX_ERR_INVALID_ARG;
+  return fused(seqs, q_idx, q_dtype, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k, q, H, kv, kv_dtype,
+               softmax_scale, out, lse, out_idx, ws, ws_bytes, stream);
+}
+
+int idx_timer_arm(int kernel, void* start_event, void* stop_event) {
+  if (kernel < 0 || kernel >= IDX_KERNEL_COUNT || !start_event || !stop_event) return IDX_ERR_INVALID_ARG;
+  g_timers[kernel].start = static_cast<hipEvent_t>(start_event);
+  g_timers[kernel].stop = static_cast<hipEvent_t>(stop_event);
+  return IDX_OK;
+}
+
+}  // extern "C"

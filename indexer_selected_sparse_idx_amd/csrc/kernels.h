@@ -1,0 +1,93 @@
+// Internal interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idxs {
+
+// Device-side view of a batch (see idx_seqs in include/idxsparse.h).
+struct SeqView {
+  int num_seqs;
+  int num_tokens;
+  const int32_t* cu_q;         // nullable: one token per sequence
+  const int32_t* ctx_len;
+  const int32_t* block_table;  // nullable: contiguous cache
+  int bt_stride;
+  int page_shift;              // log2(page_size)
+  int64_t seq_stride;
+  int max_q_len;
+  int max_ctx_len;
+};
+
+__device__ __forceinline__ int64_t cache_row(const SeqView& v, int b, int s) {
+  if (v.block_table == nullptr) return (int64_t)b * v.seq_stride + s;
+  const int page = v.block_table[(int64_t)b * v.bt_stride + (s >> v.page_shift)];
+  return ((int64_t)page << v.page_shift) + (s & ((1 << v.page_shift) - 1));
+}
+
+__device__ __forceinline__ int first_token(const SeqView& v, int b) { return v.cu_q ? v.cu_q[b] : b; }
+__device__ __forceinline__ int q_len(const SeqView& v, int b) { return v.cu_q ? v.cu_q[b + 1] - v.cu_q[b] : 1; }
+
+// Sequence holding token `tok` (binary search over cu_q).
+__device__ __forceinline__ int seq_of_token(const SeqView& v, int tok) {
+  if (v.cu_q == nullptr) return tok;
+  int lo = 0, hi = v.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (v.cu_q[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct ScoreParams {
+  SeqView sv;
+  const uint16_t* q_idx;   // bf16 [T, H_I, d_I]
+  const uint8_t* k_idx;    // rows of d_I bf16 (2 bytes) or e4m3 (1 byte)
+  const float* k_scale;    // nullable, per row
+  const float* head_w;     // [T, H_I]
+  int H_I;
+  int d_I;
+  float* scores;           // [T, score_stride]
+  int64_t score_stride;
+};
+
+struct TopkParams {
+  SeqView sv;
+  const float* scores;
+  int64_t score_stride;
+  int top_k;
+  int32_t* out_idx;        // [T, top_k]
+};
+
+struct AttnParams {
+  SeqView sv;
+  const uint16_t* q;       // bf16 [T, H, 576]
+  int H;
+  const uint8_t* kv;       // bf16 rows (1152 B) or packed fp8 rows (656 B)
+  const int32_t* idx;      // [T, top_k]
+  int top_k;
+  float scale_log2;        // softmax_scale * log2(e)
+  float* out;              // [T, H, 512]
+  float* lse;              // [T, H] nullable
+  int num_splits;
+  int split_len;           // index entries per split (multiple of the tile)
+  float* part_o;           // [T, num_splits, H, 512] when num_splits > 1
+  float* part_lse;         // [T, num_splits, H]
+};
+
+// Kernel launchers (asynchronous, on `stream`).  Each records the armed
+// timing events of its kernel, if any.
+hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream);
+hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+hipError_t launch_attn(const AttnParams& p, bool kv_fp8, hipStream_t stream);
+
+// Timing hook (api.cpp).
+void timer_before(int kernel, hipStream_t stream);
+void timer_after(int kernel, hipStream_t stream);
+
+// Attention split heuristic shared by the workspace query and the launcher.
+int attn_num_splits(int num_tokens, int H, int top_k);
+constexpr int ATTN_TILE = 32;
+
+}  // namespace idxs

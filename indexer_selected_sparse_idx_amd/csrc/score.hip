@@ -1,0 +1,185 @@
+// Lightweight-indexer score on gfx950.
+//
+// For a query at position t and every causal position s <= t:
+//   S[s] = sum_h w[h] * ReLU(k_scale[s] * (q_I[h, :] . k_I[s, :]))
+// (relevance scoring, then head-weight weighting: "Internal Fusion of the
+// Indexer" in Day 0 Inference Support for New LLM Architectures; section 3
+// of Day 0 Inference Acceleration for New LLM Architectures).
+//
+// The per-head dot products are one MFMA contraction per 16 keys: indexer
+// heads sit on the MFMA M dimension (16 per tile), keys on N and d_I on K.
+// Each lane then holds 4 heads x 1 key per tile, so ReLU, the head weights
+// and most of the head sum stay in registers; two cross-lane adds finish the
+// sum.  Per-head values never leave registers; only the fp32 score of each
+// key is written (to the workspace row that the selection kernel reads).
+//
+// Keys stream from HBM straight into the MFMA B-operand registers (16 bytes
+// per lane per load).  The contraction order over d_I is free, so the dims a
+// lane loads are chosen for wide loads: for bf16 keys lane group g = l/16
+// takes dims 32*ks + 8*g .. +8 at k-step ks; for e4m3 keys one 16-byte load
+// covers two k-steps (dims 64*j + 16*g .. +16).  The query operand uses the
+// same permutation.
+#include "common.h"
+#include "kernels.h"
+
+namespace idxs {
+
+namespace {
+
+constexpr int SCORE_WAVES = 4;
+constexpr int NT = 4;  // key tiles (16 keys each) per loop iteration
+
+// First dim of the 8-wide slice that lane group g holds at k-step ks.
+template <bool FP8>
+__device__ __forceinline__ int kdim(int ks, int g) {
+  return FP8 ? (ks >> 1) * 64 + g * 16 + (ks & 1) * 8 : ks * 32 + g * 8;
+}
+
+// MT: 16-head tiles (ceil(H_I / 16)); KS: 32-dim k-steps (d_I / 32).
+// decode: the 4 waves of a workgroup split one token's key block.
+// prefill: the 4 waves are 4 consecutive query tokens of one sequence and
+//          all scan the workgroup's key block (shared through L1/L2).
+template <int MT, int KS, bool FP8, bool DECODE>
+__global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_wg) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const SeqView& sv = p.sv;
+
+  int b, tok, t, key_lo, key_hi;  // wave's keys: [key_lo, key_hi]
+  if (DECODE) {
+    b = blockIdx.y;
+    tok = first_token(sv, b);
+    t = sv.ctx_len[b] - 1;
+    const int wg_lo = blockIdx.x * keys_per_wg;
+    const int per_wave = keys_per_wg / SCORE_WAVES;
+    key_lo = wg_lo + wave * per_wave;
+    key_hi = min(t, key_lo + per_wave - 1);
+  } else {
+    const int nqb = cdiv(sv.max_q_len, SCORE_WAVES);
+    b = blockIdx.y / nqb;
+    const int i = (blockIdx.y % nqb) * SCORE_WAVES + wave;
+    const int ql = q_len(sv, b);
+    if (i >= ql) return;
+    tok = first_token(sv, b) + i;
+    t = sv.ctx_len[b] - ql + i;
+    key_lo = blockIdx.x * keys_per_wg;
+    key_hi = min(t, key_lo + keys_per_wg - 1);
+  }
+  if (key_lo > key_hi) return;
+
+  // ---- query operand (A): Q[h = 16 mt + c][kdim(ks, g) .. +8] -------------
+  bf16x8 qa[MT][KS];
+  float w[MT][4];
+  const uint16_t* qrow = p.q_idx + (int64_t)tok * p.H_I * p.d_I;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = mt * 16 + c;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (h < p.H_I) v = *(const u32x4*)(qrow + (int64_t)h * p.d_I + kdim<FP8>(ks, g));
+      qa[mt][ks] = as_bf16x8(v);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hr = mt * 16 + g * 4 + r;
+      w[mt][r] = hr < p.H_I ? p.head_w[(int64_t)tok * p.H_I + hr] : 0.0f;
+    }
+  }
+
+  const int row_bytes = FP8 ? p.d_I : p.d_I * 2;
+  float* srow = p.scores + (int64_t)tok * p.score_stride;
+
+  for (int s0 = key_lo; s0 <= key_hi; s0 += 16 * NT) {
+    bf16x8 kb[NT][KS];
+    float ksc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int s = min(s0 + nt * 16 + c, key_hi);  // clamp: rows past key_hi are masked below
+      const int64_t row = cache_row(sv, b, s);
+      const uint8_t* krow = p.k_idx + row * row_bytes;
+      ksc[nt] = p.k_scale ? p.k_scale[row] : 1.0f;
+      if (FP8) {
+#pragma unroll
+        for (int j = 0; j < KS / 2; ++j) {
+          const u32x4 raw = *(const u32x4*)(krow + j * 64 + g * 16);
+          u32x4 lo, hi;
+          u32x2 a0 = e4m3x4_to_bf16(raw[0], 1.0f), a1 = e4m3x4_to_bf16(raw[1], 1.0f);
+          u32x2 a2 = e4m3x4_to_bf16(raw[2], 1.0f), a3 = e4m3x4_to_bf16(raw[3], 1.0f);
+          lo[0] = a0[0]; lo[1] = a0[1]; lo[2] = a1[0]; lo[3] = a1[1];
+          hi[0] = a2[0]; hi[1] = a2[1]; hi[2] = a3[0]; hi[3] = a3[1];
+          kb[nt][2 * j] = as_bf16x8(lo);
+          kb[nt][2 * j + 1] = as_bf16x8(hi);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kb[nt][ks] = as_bf16x8(*(const u32x4*)(krow + kdim<false>(ks, g) * 2));
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float v = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma16(qa[mt][ks], kb[nt][ks], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v += w[mt][r] * fmaxf(acc[r] * ksc[nt], 0.0f);
+      }
+      v += shfl_xor(v, 16);
+      v += shfl_xor(v, 32);
+      const int s = s0 + nt * 16 + c;
+      if (g == 0 && s <= key_hi) srow[s] = v;
+    }
+  }
+}
+
+template <int MT, int KS, bool FP8>
+hipError_t launch_mt(const ScoreParams& p, hipStream_t stream) {
+  const SeqView& sv = p.sv;
+  const bool decode = sv.max_q_len == 1;
+  if (decode) {
+    const int kpw = 1024;
+    dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs);
+    hipLaunchKernelGGL((score_kernel<MT, KS, FP8, true>), grid, dim3(256), 0, stream, p, kpw);
+  } else {
+    const int kpw = 256;
+    dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs * cdiv(sv.max_q_len, SCORE_WAVES));
+    hipLaunchKernelGGL((score_kernel<MT, KS, FP8, false>), grid, dim3(256), 0, stream, p, kpw);
+  }
+  return hipGetLastError();
+}
+
+template <bool FP8>
+hipError_t launch_dt(const ScoreParams& p, hipStream_t stream) {
+  const int mt = cdiv(p.H_I, 16);
+  if (p.d_I == 128) {
+    switch (mt) {
+      case 1: return launch_mt<1, 4, FP8>(p, stream);
+      case 2: return launch_mt<2, 4, FP8>(p, stream);
+      case 3: return launch_mt<3, 4, FP8>(p, stream);
+      default: return launch_mt<4, 4, FP8>(p, stream);
+    }
+  }
+  switch (mt) {
+    case 1: return launch_mt<1, 2, FP8>(p, stream);
+    case 2: return launch_mt<2, 2, FP8>(p, stream);
+    case 3: return launch_mt<3, 2, FP8>(p, stream);
+    default: return launch_mt<4, 2, FP8>(p, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream) {
+  timer_before(0, stream);
+  hipError_t e = k_fp8 ? launch_dt<true>(p, stream) : launch_dt<false>(p, stream);
+  timer_after(0, stream);
+  return e;
+}
+
+}  // namespace idxs

@@ -1,0 +1,175 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Top-K index sets must match bit for bit (integer-valued indexer inputs make
+the fp32 scores exact); attention must be within max-abs error <= tol * RMS
+of the oracle output (tol 2e-2 for a bf16 cache, 6e-2 for an FP8 cache).
+Sizes here keep the oracle to seconds while spanning several key blocks,
+several attention tiles, ragged tails and every code path (decode/prefill,
+bf16/e4m3 keys, bf16/FP8 latent rows, contiguous/paged caches).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from workloads import Workload, config, generate
+
+import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import indexer_selected_sparse_idx_amd as lib
+    lib.lib()
+    torch.manual_seed(0)
+
+
+def _parity_all(inp, tol, label):
+    """Every token of every call of `inp`, through the fused entry points."""
+    for ci, call in enumerate(inp.calls):
+        U.log("%s call %d: %d tokens, ctx max %d" % (label, ci, call.num_tokens, int(call.ctx_len.max())))
+        out, lse, idx = U.run_fused(inp, call)
+        torch.cuda.synchronize()
+        tokens = list(range(call.num_tokens))
+        w_idx, w_out, w_lse = U.oracle_rows(inp, call, tokens)
+        U.check_indices(idx.cpu().numpy(), w_idx, "%s call %d" % (label, ci))
+        err = U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), w_out, w_lse, tol,
+                                "%s call %d" % (label, ci))
+        U.log("  ok: attention err/RMS %.2e" % err)
+
+
+def test_tiny_prefill_scaled():
+    inp = generate(config(1, scale=1 / 8), "cuda")          # L = 256, K = 128, H = 8, H_I = 4
+    _parity_all(inp, U.TOL_BF16, "tiny-prefill/8")
+
+
+def test_decode_ragged_contexts():
+    wl = Workload("decode ragged", [2000, 64, 1, 3001, 2048, 2049], [{"seqs": list(range(6)), "q_len": None}],
+                  top_k=2048, seed=21)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "decode-ragged")
+
+
+def test_decode_small_topk():
+    wl = Workload("decode K=100", [5000, 777, 130], [{"seqs": [0, 1, 2], "q_len": None}], top_k=100, seed=22)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "decode-K100")
+
+
+def test_chunked_prefill_scaled():
+    inp = generate(config(3, scale=1 / 32), "cuda")          # L = 2048 in chunks of 128
+    for call in inp.calls[::5] + [inp.calls[-1]]:
+        sub = workloads.Inputs(inp.wl, [call], inp.q_idx, inp.head_w, inp.q, inp.k_idx, inp.k_scale,
+                               inp.kv, inp.seq_stride, inp.block_table)
+        _parity_all(sub, U.TOL_BF16, "long-prefill/32")
+
+
+def test_prefill_small_topk_many_ties():
+    # K = 64 over a 700-long causal sequence with keys in {-1, 0, 1}: heavy ties
+    wl = Workload("prefill ties", [700], [{"seqs": [0], "q_len": [700]}], top_k=64, H_I=20, d_I=64,
+                  H=20, k_range=1, q_range=1, seed=23)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "prefill-ties")
+
+
+def test_fp8_decode_scaled():
+    inp = generate(config(4, scale=1 / 32), "cuda")          # B = 4, ctx = 4096, e4m3 keys, FP8 rows
+    _parity_all(inp, U.TOL_FP8, "fp8-decode/32")
+
+
+def test_paged_mixed_scaled():
+    inp = generate(config(5, scale=1 / 16), "cuda")          # paged, prefill + decode calls
+    _parity_all(inp, U.TOL_BF16, "mixed-paged/16")
+
+
+def test_key_scale_and_d64():
+    wl = Workload("k_scale", [900, 333], [{"seqs": [0, 1], "q_len": [40, 7]}], top_k=96, d_I=64, H_I=33,
+                  H=48, k_scale=True, seed=24)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "k_scale")
+
+
+def test_all_equal_scores_take_lowest_positions():
+    wl = Workload("zeros", [3000], [{"seqs": [0], "q_len": [5]}], top_k=256, seed=25)
+    inp = generate(wl, "cuda")
+    inp.q_idx.zero_()                                          # every score is exactly 0
+    call = inp.calls[0]
+    out, lse, idx = U.run_fused(inp, call)
+    got = np.sort(idx.cpu().numpy(), axis=1)
+    assert np.array_equal(got, np.tile(np.arange(256, dtype=np.int32), (5, 1)))
+
+
+def test_separate_entry_points_match_fused():
+    import indexer_selected_sparse_idx_amd as lib
+    inp = generate(config(2, scale=1 / 16), "cuda")
+    call = inp.calls[0]
+    s = U.lib_seqs(inp, call)
+    out, lse, idx = U.run_fused(inp, call)
+    idx2 = lib.idx_score_topk(s, inp.q_idx, inp.k_idx, inp.head_w, inp.wl.top_k)
+    out2, lse2 = lib.sparse_mla_attn(s, inp.q, inp.kv, idx2, U.SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_attention_skips_invalid_entries_and_empty_rows():
+    import indexer_selected_sparse_idx_amd as lib
+    wl = Workload("attn-only", [100, 50], [{"seqs": [0, 1], "q_len": None}], H=32, top_k=70, seed=26)
+    inp = generate(wl, "cuda")
+    call = inp.calls[0]
+    s = U.lib_seqs(inp, call)
+    idx = torch.full((2, 70), -1, dtype=torch.int32)
+    idx[0, :5] = torch.tensor([3, 99, 100, 5000, 0])          # 100 and 5000 are outside ctx = 100
+    idx[0, 40:43] = torch.tensor([-7, 17, 3])                 # duplicates count twice
+    # row 1: no valid entry at all
+    idx = idx.cuda()
+    out, lse = lib.sparse_mla_attn(s, inp.q, inp.kv, idx, U.SCALE)
+    torch.cuda.synchronize()
+    osq = U.oracle_seqs(inp, call)
+    import oracle
+    w_out, w_lse = oracle.attention(osq, U.bits16(inp.q), U.host_raw(inp.kv), "bf16", idx.cpu().numpy(), U.SCALE)
+    U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), w_out, w_lse, U.TOL_BF16, "invalid entries")
+    assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
+
+
+def test_paged_equals_contiguous_bitwise():
+    wl_c = Workload("c", [1500, 700], [{"seqs": [0, 1], "q_len": None}], top_k=512, seed=27)
+    inp = generate(wl_c, "cuda")
+    call = inp.calls[0]
+    out_c, lse_c, idx_c = U.run_fused(inp, call)
+    # scatter the same rows into shuffled pages of 32
+    page = 32
+    rng = np.random.default_rng(5)
+    npg = [-(-int(c) // page) for c in wl_c.ctx_len]
+    perm = rng.permutation(sum(npg)).astype(np.int32)
+    bt = np.zeros((2, max(npg)), np.int32)
+    k_p = torch.zeros((sum(npg) * page, inp.k_idx.shape[1]), dtype=inp.k_idx.dtype, device="cuda")
+    kv_p = torch.zeros((sum(npg) * page, inp.kv.shape[1]), dtype=inp.kv.dtype, device="cuda")
+    k = 0
+    for b in range(2):
+        for j in range(npg[b]):
+            bt[b, j] = perm[k]
+            k += 1
+            lo, hi = j * page, min((j + 1) * page, wl_c.ctx_len[b])
+            src = b * inp.seq_stride
+            k_p[bt[b, j] * page: bt[b, j] * page + hi - lo] = inp.k_idx[src + lo: src + hi]
+            kv_p[bt[b, j] * page: bt[b, j] * page + hi - lo] = inp.kv[src + lo: src + hi]
+    import indexer_selected_sparse_idx_amd as lib
+    ctx = torch.tensor(wl_c.ctx_len, dtype=torch.int32, device="cuda")
+    btt = torch.from_numpy(bt).cuda()
+    s = lib.Seqs(ctx, None, max_q_len=1, max_ctx_len=1500, block_table=btt, page_size=page)
+    out_p, lse_p, idx_p = lib.idx_sparse_attn_decode(s, inp.q_idx, k_p, inp.head_w, 512, inp.q, kv_p, U.SCALE,
+                                                     out_idx=torch.empty_like(idx_c))
+    torch.cuda.synchronize()
+    assert torch.equal(idx_c, idx_p)
+    assert torch.equal(out_c, out_p) and torch.equal(lse_c, lse_p)
+
+
+def test_deterministic():
+    inp = generate(config(5, scale=1 / 32), "cuda")
+    for call in inp.calls:
+        a = U.run_fused(inp, call)
+        b = U.run_fused(inp, call)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
