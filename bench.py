@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Throughput of the fused indexer + sparse latent attention hot path.
+
+Workload: the decode batch of 64 requests, one new token each, 32768 cached
+positions per request (contiguous latent cache of 576 bf16 per row and
+index-key cache of 128 bf16 per row), 64 indexer heads, Top-K 2048,
+128 attention heads.  One step is one idx_sparse_attn_decode call over the
+batch: score every cached position, select the Top-K, gather the selected
+latent rows and attend.  Inputs are seeded synthetic data resident in HBM
+before timing starts.
+
+Prints one JSON line.  `roofline` describes the dominant kernel (the
+indexer score, HBM-bound): its algorithmic bytes per launch over its average
+launch time, measured with HIP events the library records on the launch
+stream during the timed steps.  `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the same workload (one thread).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-sample", type=int, default=64, help="decode tokens timed on the CPU oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="run this many steps with no timing or oracle (for rocprofv3)")
+    return ap.parse_args()
+
+
+def algorithmic_units(wl, ctx, T):
+    """Bytes / flops the method must move or compute (per step)."""
+    H_I, d_I, H, K = wl.H_I, wl.d_I, wl.H, wl.top_k
+    key_bytes = 2 if wl.k_dtype == "bf16" else 1
+    row_bytes = 1152 if wl.kv_dtype == "bf16" else 656
+    n_cand = ctx                                   # t + 1 = ctx for a decode token
+    sel = min(K, n_cand)
+    score_bytes = T * (n_cand * d_I * key_bytes + H_I * d_I * 2 + H_I * 4)
+    score_flops = T * 2 * H_I * d_I * n_cand
+    topk_bytes = T * K * 4
+    attn_bytes = T * (sel * row_bytes + H * 576 * 2 + H * 512 * 4 + H * 4 + K * 4)
+    attn_flops = T * 2176 * H * sel
+    return dict(score_bytes=score_bytes, score_flops=score_flops, topk_bytes=topk_bytes,
+                attn_bytes=attn_bytes, attn_flops=attn_flops)
+
+
+def score_source_digest():
+    h = hashlib.sha256()
+    for name in ("score.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "indexer_selected_sparse_idx_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per launch of the score kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, "score_kernel_decode_b64_ctx32768_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != score_source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, call, n_tokens):
+    """Time the oracle (indexer + Top-K + attention) on the first n_tokens
+    decode tokens, one BLAS thread, inputs already on the host."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from oracle import reference as R
+    import torch
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    n_tokens = max(1, min(n_tokens, call.num_tokens))
+    seq_ids = list(range(n_tokens))
+    stride = inp.seq_stride
+    k_host = bits(inp.k_idx[: n_tokens * stride])
+    kv_host = bits(inp.kv[: n_tokens * stride])
+    q_idx = bits(inp.q_idx[:n_tokens])
+    q = bits(inp.q[:n_tokens])
+    w = inp.head_w[:n_tokens].cpu().numpy()
+    seqs = R.Seqs(ctx_len=call.ctx_len[:n_tokens].astype(np.int64), seq_stride=stride)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        idx = oracle.score_topk(seqs, q_idx, k_host, "bf16", w, inp.wl.top_k)
+        oracle.attention(seqs, q, kv_host, "bf16", idx, 1.0 / math.sqrt(576.0))
+        dt = time.perf_counter() - t0
+    return dict(value=n_tokens / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample="%d of the %d decode tokens of one step (each: indexer over %d positions, "
+                       "Top-%d, attention over %d rows x %d heads); %.1f s on 1 thread"
+                       % (n_tokens, call.num_tokens, int(call.ctx_len[0]), inp.wl.top_k, inp.wl.top_k,
+                          inp.wl.H, dt))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(requests would shard across GPUs with no exchange; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import indexer_selected_sparse_idx_amd as lib
+    from workloads import config, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lib.lib()
+    dev = torch.device("cuda:0")
+    wl = config(2)
+    inp = generate(wl, dev)
+    call = inp.calls[0]
+    T = call.num_tokens
+    ctx_t = torch.from_numpy(call.ctx_len.astype(np.int32)).to(dev)
+    seqs = lib.Seqs(ctx_t, None, max_q_len=1, max_ctx_len=int(call.ctx_len.max()), seq_stride=inp.seq_stride)
+    out = torch.empty((T, wl.H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
+    ws = torch.empty(lib.idx_sparse_attn_workspace(seqs, wl.H_I, wl.d_I, wl.H, wl.top_k), dtype=torch.uint8,
+                     device=dev)
+    scale = 1.0 / math.sqrt(576.0)
+
+    def step():
+        lib.idx_sparse_attn_decode(seqs, inp.q_idx, inp.k_idx, inp.head_w, wl.top_k, inp.q, inp.kv, scale,
+                                   out=out, lse=lse, out_idx=idx, ws=ws)
+
+    torch.cuda.synchronize()
+    if args.profile_steps:
+        for i in range(args.profile_steps):
+            step()
+            torch.cuda.synchronize()
+            print("profile step %d done" % i, flush=True)
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+          for k in (lib.IDX_KERNEL_SCORE, lib.IDX_KERNEL_TOPK, lib.IDX_KERNEL_ATTN, lib.IDX_KERNEL_COMBINE)}
+    for pairs in ev.values():
+        for a, b in pairs:          # create the underlying HIP events before handing them over
+            a.record()
+            b.record()
+    torch.cuda.synchronize()
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        for k, pairs in ev.items():
+            lib.idx_timer_arm(k, pairs[i][0], pairs[i][1])
+        step()
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = t_start.elapsed_time(t_stop)
+    ms_per_step = gpu_ms / K
+
+    kern_ms = {}
+    names = {lib.IDX_KERNEL_SCORE: "score", lib.IDX_KERNEL_TOPK: "topk", lib.IDX_KERNEL_ATTN: "attn",
+             lib.IDX_KERNEL_COMBINE: "combine"}
+    for k, pairs in ev.items():
+        kern_ms[names[k]] = sum(a.elapsed_time(b) for a, b in pairs) / K
+
+    u = algorithmic_units(wl, int(call.ctx_len[0]), T)
+    score_us = kern_ms["score"] * 1e3
+    achieved = u["score_bytes"] / (kern_ms["score"] * 1e-3) / 1e9
+    traffic = counter_traffic()
+    attn_s = (kern_ms["attn"] + kern_ms["combine"]) * 1e-3
+
+    result = {
+        "metric": "fused indexer+sparse-attn tokens/sec; achieved HBM GB/s & MFMA % of peak",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode batch: 64 requests x 1 token, 32768-position contiguous bf16 caches, "
+                               "indexer 64 heads d_I=128, Top-K 2048, 128 attention heads, latent 576",
+                   "batch": T, "ctx": int(call.ctx_len[0]), "H_I": wl.H_I, "d_I": wl.d_I, "top_k": wl.top_k,
+                   "H": wl.H, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "indexer score", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": u["score_bytes"], "avg_launch_us": score_us},
+        "kernels_avg_us": {k: v * 1e3 for k, v in kern_ms.items()},
+        "secondary": {
+            "attention_hbm_gbs": u["attn_bytes"] / attn_s / 1e9,
+            "attention_hbm_frac": u["attn_bytes"] / attn_s / 1e9 / HBM_PEAK_GBS,
+            "attention_mfma_frac": u["attn_flops"] / attn_s / 1e12 / BF16_PEAK_TFLOPS,
+            "score_mfma_frac": u["score_flops"] / (kern_ms["score"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "step_hbm_gbs": (u["score_bytes"] + u["topk_bytes"] + u["attn_bytes"]) / (ms_per_step * 1e-3) / 1e9,
+            "wall_s_timed_region": wall,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, call, args.cpu_sample)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

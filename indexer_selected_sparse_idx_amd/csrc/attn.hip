@@ -10,9 +10,9 @@
 // Optimization for New Models).
 //
 // Work item: (token, group of 16*NW heads, split of the index list).  The
-// workgroup gathers 32 selected latent rows per tile into LDS (double
-// buffered; FP8 rows are dequantised to bf16 on the way), and each wave
-// owns 16 heads:
+// cache row of every index of the split is resolved once (block table
+// included) into LDS.  Selected latent rows are then gathered 32 per tile
+// into LDS, and each wave owns 16 heads:
 //   S^T[32 keys x 16 heads] = C_tile . Q^T   (MFMA 16x16x32, keys on M)
 //   online softmax in fp32 registers (each lane holds 8 keys of one head)
 //   O^T[512 x 16 heads]   += V^T . P^T       (MFMA, dv on M)
@@ -20,8 +20,16 @@
 // product once the key order inside the contraction is permuted to match;
 // the V^T operand comes from the key-major LDS tile through the gfx950
 // transposing LDS read (ds_read_b64_tr_b16), so V is stored only once.
-// Splits (for decode occupancy) are merged by combine_kernel.
+//
+// bf16 rows go from HBM straight into LDS (global_load_lds_dwordx4, one
+// wave instruction per 1 KiB latent row, chunks XOR-swizzled by row so the
+// MFMA operand reads are bank-conflict free) through an NBUF-deep ring, so
+// NBUF-1 tiles are in flight while one is computed.  FP8 rows (656 bytes)
+// are staged through registers and dequantised to bf16 on their way into
+// LDS.  Splits (for decode occupancy) are merged by combine_kernel.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "kernels.h"
@@ -31,231 +39,159 @@ namespace idxs {
 namespace {
 
 constexpr int TILE = ATTN_TILE;                 // selected rows per tile
-constexpr int LAT_TILE_BYTES = TILE * 1024;     // 512 bf16 per row
+constexpr int LAT_STRIDE = 1024 + 16;           // 512 bf16 per row, padded by one 16-byte chunk
+constexpr int LAT_TILE_BYTES = TILE * LAT_STRIDE;
 constexpr int ROPE_TILE_BYTES = TILE * 128;     // 64 bf16 per row
 constexpr int BUF_BYTES = LAT_TILE_BYTES + ROPE_TILE_BYTES;
+constexpr float RESCALE_SLACK = 8.0f;           // log2 growth of the running max tolerated before rescaling
+constexpr int EAGER_TILES = 4;                  // tiles with exact running-max normalisation
 constexpr float LN2 = 0.69314718055994530942f;
 
-// Swizzled LDS addresses: 16-byte chunk `ch` of row r.
-__device__ __forceinline__ int lat_off(int r, int ch) { return r * 1024 + ((ch ^ (r & 15)) << 4); }
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding; the
+// 6-bit vmcnt saturates at 63, and waiting for fewer is always safe).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_addr + 16 *
+// lane (lds_addr is wave-uniform).  Written as inline asm so that the
+// compiler does not turn later LDS reads of other ring slots into waits for
+// every outstanding gather: completion is tracked with wait_vmcnt().
+__device__ __forceinline__ void dma16(const uint8_t* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
+
+// LDS addresses of 16-byte chunk `ch` of tile row r.  Latent rows are padded
+// to 65 chunks, so 16 consecutive rows at one chunk hit 16 different bank
+// groups and every per-lane address is affine in ch (immediate offsets).
+// The rope part is XOR-swizzled instead.
+__device__ __forceinline__ int lat_off(int r, int ch) { return r * LAT_STRIDE + (ch << 4); }
 __device__ __forceinline__ int rope_off(int r, int ch) { return LAT_TILE_BYTES + r * 128 + ((ch ^ (r & 7)) << 4); }
 
-template <int NW, bool FP8>
-struct Stage {
-  static constexpr int THREADS = NW * WAVE;
-  // bf16 rows: 72 chunks of 16 B (64 latent + 8 rope); fp8 rows: 32 latent
-  // code chunks (16 codes each) + 8 rope chunks.
-  static constexpr int CHUNKS = FP8 ? 40 : 72;
-  static constexpr int JOBS = (TILE * CHUNKS + THREADS - 1) / THREADS;
-  u32x4 raw[JOBS];
-  float scale[FP8 ? JOBS : 1];
-
-  __device__ __forceinline__ void load(const AttnParams& p, const int32_t* idx_row, int e0, int e_hi,
-                                       int b, int ctx, int tid) {
-#pragma unroll
-    for (int k = 0; k < JOBS; ++k) {
-      const int j = tid + k * THREADS;
-      raw[k] = u32x4{0u, 0u, 0u, 0u};
-      if (FP8) scale[k] = 0.0f;
-      if (j < TILE * CHUNKS) {
-        const int r = j / CHUNKS, ch = j % CHUNKS;
-        const int e = e0 + r;
-        const int s = e < e_hi ? idx_row[e] : -1;
-        if (s >= 0 && s < ctx) {
-          const int64_t row = cache_row(p.sv, b, s);
-          if (FP8) {
-            const uint8_t* base = p.kv + row * FP8_ROW_BYTES;
-            if (ch < 32) {
-              raw[k] = *(const u32x4*)(base + ch * 16);
-              scale[k] = *(const float*)(base + LATENT + (ch >> 3) * 4);
-            } else {
-              raw[k] = *(const u32x4*)(base + LATENT + 16 + (ch - 32) * 16);
-            }
-          } else {
-            raw[k] = *(const u32x4*)(p.kv + row * (ROW * 2) + ch * 16);
-          }
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint8_t* buf, int tid) {
-#pragma unroll
-    for (int k = 0; k < JOBS; ++k) {
-      const int j = tid + k * THREADS;
-      if (j < TILE * CHUNKS) {
-        const int r = j / CHUNKS, ch = j % CHUNKS;
-        if (FP8) {
-          if (ch < 32) {
-            const float sc = scale[k];
-            u32x2 a0 = e4m3x4_to_bf16(raw[k][0], sc), a1 = e4m3x4_to_bf16(raw[k][1], sc);
-            u32x2 a2 = e4m3x4_to_bf16(raw[k][2], sc), a3 = e4m3x4_to_bf16(raw[k][3], sc);
-            *(u32x4*)(buf + lat_off(r, 2 * ch)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
-            *(u32x4*)(buf + lat_off(r, 2 * ch + 1)) = u32x4{a2[0], a2[1], a3[0], a3[1]};
-          } else {
-            *(u32x4*)(buf + rope_off(r, ch - 32)) = raw[k];
-          }
-        } else {
-          if (ch < 64) *(u32x4*)(buf + lat_off(r, ch)) = raw[k];
-          else *(u32x4*)(buf + rope_off(r, ch - 64)) = raw[k];
-        }
-      }
-    }
-  }
+// Per-wave state of the online softmax and the O^T accumulator.
+struct WaveAcc {
+  bf16x8 qb[18];   // Q^T operand: lane holds Q[h][32 ks + 8 g .. +8]
+  f32x4 o[32];     // O^T[dv = 16 nt + 4 g + r][head c]
+  float m_run, l_run;
+  int tiles;       // tiles processed so far
 };
 
-template <int NW, bool FP8>
-__global__ __launch_bounds__(NW * WAVE, 1) void attn_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF_BYTES];
-  __shared__ int valid_sh[2][TILE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g = lane >> 4;
-  const int c = lane & 15;
-  const SeqView& sv = p.sv;
-
-  // XCD-aware work mapping: workgroups are dispatched round-robin over the 8
-  // XCDs, so the head groups of one (token, split) pair are placed 8 blocks
-  // apart and share an XCD (and its L2) for the gathered rows.
-  const int nhg = cdiv(p.H, 16 * NW);
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int hg = slot % nhg;
-  const int pair = (slot / nhg) * 8 + xcd;
-  if (pair >= sv.num_tokens * p.num_splits) return;
-  const int tok = pair / p.num_splits;
-  const int split = pair % p.num_splits;
-
-  const int b = seq_of_token(sv, tok);
-  const int ctx = sv.ctx_len[b];
-  const int e_lo = split * p.split_len;
-  const int e_hi = min(p.top_k, e_lo + p.split_len);
-  const int ntiles = e_hi > e_lo ? cdiv(e_hi - e_lo, TILE) : 0;
-  const int32_t* idx_row = p.idx + (int64_t)tok * p.top_k;
-
-  const int h = hg * 16 * NW + wave * 16 + c;  // this lane's head (S, P, O columns)
-  const bool head_ok = h < p.H;
-
-  // Q^T operand: lane holds Q[h][32 ks + 8 g .. +8] for the 18 k-steps of 576.
-  bf16x8 qb[18];
-  {
-    const uint16_t* qrow = p.q + ((int64_t)tok * p.H + (head_ok ? h : 0)) * ROW;
+__device__ __forceinline__ void load_q(WaveAcc& a, const AttnParams& p, int tok, int h, bool head_ok, int g) {
+  const uint16_t* qrow = p.q + ((int64_t)tok * p.H + (head_ok ? h : 0)) * ROW;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (head_ok) v = *(const u32x4*)(qrow + ks * 32 + g * 8);
-      qb[ks] = as_bf16x8(v);
-    }
+  for (int ks = 0; ks < 18; ++ks) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (head_ok) v = *(const u32x4*)(qrow + ks * 32 + g * 8);
+    a.qb[ks] = as_bf16x8(v);
   }
-
-  f32x4 o[32];
 #pragma unroll
-  for (int nt = 0; nt < 32; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f;
+  for (int nt = 0; nt < 32; ++nt) a.o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  a.m_run = -INFINITY;
+  a.l_run = 0.0f;
+  a.tiles = 0;
+}
 
-  Stage<NW, FP8> st;
-  if (ntiles > 0) {
-    st.load(p, idx_row, e_lo, e_hi, b, ctx, tid);
-    st.store(smem, tid);
-    if (tid < TILE) {
-      const int e = e_lo + tid;
-      const int s = e < e_hi ? idx_row[e] : -1;
-      valid_sh[0][tid] = (s >= 0 && s < ctx);
-    }
-  }
-  __syncthreads();
-
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int cur = tile & 1;
-    const uint8_t* buf = smem + cur * BUF_BYTES;
-    const bool more = tile + 1 < ntiles;
-    const int e_next = e_lo + (tile + 1) * TILE;
-    if (more) st.load(p, idx_row, e_next, e_hi, b, ctx, tid);
-
-    // ---- S^T = C . Q^T ---------------------------------------------------
-    f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+// One tile of 32 keys from LDS buffer `buf`; valid8 bit j says whether key
+// 16 (j / 4) + 4 g + j % 4 of the tile is a real selected row.
+__device__ __forceinline__ void compute_tile(WaveAcc& a, const uint8_t* buf, uint32_t valid8, float scale_log2,
+                                             int g, int c) {
+  // ---- S^T = C . Q^T -----------------------------------------------------
+  f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+  constexpr int KB = 6;  // k-steps whose operands are read from LDS together
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
+  for (int k0 = 0; k0 < 18; k0 += KB) {
+    bf16x8 av[KB][2];
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const int ks = k0 + kk;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int r = mt * 16 + c;
         const int off = ks < 16 ? lat_off(r, ks * 4 + g) : rope_off(r, (ks - 16) * 4 + g);
-        const bf16x8 a = *(const bf16x8*)(buf + off);
-        sacc[mt] = mfma16(a, qb[ks], sacc[mt]);
+        av[kk][mt] = *(const bf16x8*)(buf + off);
       }
     }
-
-    // ---- online softmax (base 2) --------------------------------------------
-    float x[8];
-    float tmax = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = (j >> 2) * 16 + g * 4 + (j & 3);
-      x[j] = valid_sh[cur][key] ? sacc[j >> 2][j & 3] * p.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, x[j]);
+    for (int kk = 0; kk < KB; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma16(av[kk][mt], a.qb[k0 + kk], sacc[mt]);
     }
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    float alpha = 1.0f;
-    float pv[8];
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pv[j] = 0.0f;
-    } else {
-      alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pv[j] = exp2f(x[j] - m_new);
-    }
-    float psum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) psum += pv[j];
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    u32x4 pk;
-    pk[0] = pack_bf16x2(pv[0], pv[1]);
-    pk[1] = pack_bf16x2(pv[2], pv[3]);
-    pk[2] = pack_bf16x2(pv[4], pv[5]);
-    pk[3] = pack_bf16x2(pv[6], pv[7]);
-    const bf16x8 pb = as_bf16x8(pk);
-
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int nt = 0; nt < 32; ++nt) o[nt] *= alpha;
-    }
-
-    // ---- O^T += V^T . P^T ------------------------------------------------------
-    // k-slot j of lane group g is key 16 (j / 4) + 4 g + j % 4 (the S^T layout).
-    const int ra = 4 * g + (c >> 2), rb = ra + 16;
-    const int half = (c & 1) * 8;
-#pragma unroll
-    for (int nt = 0; nt < 32; ++nt) {
-      const int ch = nt * 2 + ((c & 3) >> 1);
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + lat_off(ra, ch) + half));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + lat_off(rb, ch) + half));
-      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[nt] = mfma16(a, pb, o[nt]);
-    }
-
-    if (more) {
-      st.store(smem + (cur ^ 1) * BUF_BYTES, tid);
-      if (tid < TILE) {
-        const int e = e_next + tid;
-        const int s = e < e_hi ? idx_row[e] : -1;
-        valid_sh[cur ^ 1][tid] = (s >= 0 && s < ctx);
-      }
-    }
-    __syncthreads();
   }
 
-  // ---- epilogue --------------------------------------------------------------
-  float l_tot = l_run;
+  // ---- online softmax (base 2) ---------------------------------------------
+  float x[8];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[j] = ((valid8 >> j) & 1u) ? sacc[j >> 2][j & 3] * scale_log2 : -INFINITY;
+    tmax = fmaxf(tmax, x[j]);
+  }
+  tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+  // Lazy rescaling: after the first EAGER_TILES tiles keep the running max
+  // unless the tile exceeds it by more than RESCALE_SLACK (p values then
+  // stay below 2^RESCALE_SLACK).  The early tiles, where the max moves most,
+  // normalise exactly so the dominant weights stay exact in bf16.
+  const bool first = a.m_run == -INFINITY;
+  const float slack = a.tiles < EAGER_TILES ? 0.0f : RESCALE_SLACK;
+  a.tiles++;
+  const bool grow = tmax > a.m_run + slack;
+  const float m_new = grow ? tmax : a.m_run;
+  const float alpha = (grow && !first) ? exp2f(a.m_run - m_new) : 1.0f;
+  float pv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pv[j] = m_new == -INFINITY ? 0.0f : exp2f(x[j] - m_new);
+  float psum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) psum += pv[j];
+  a.l_run = a.l_run * alpha + psum;
+  a.m_run = m_new;
+  u32x4 pk;
+  pk[0] = pack_bf16x2(pv[0], pv[1]);
+  pk[1] = pack_bf16x2(pv[2], pv[3]);
+  pk[2] = pack_bf16x2(pv[4], pv[5]);
+  pk[3] = pack_bf16x2(pv[6], pv[7]);
+  const bf16x8 pb = as_bf16x8(pk);
+
+  if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) a.o[nt] *= alpha;
+  }
+
+  // ---- O^T += V^T . P^T ----------------------------------------------------------
+  // k-slot j of lane group g is key 16 (j / 4) + 4 g + j % 4 (the S^T layout).
+  const int ra = 4 * g + (c >> 2), rb = ra + 16;
+  const int half = (c & 1) * 8;
+  constexpr int NB = 4;  // dv tiles whose V^T operands are read together
+#pragma unroll
+  for (int n0 = 0; n0 < 32; n0 += NB) {
+    bf16x8 av[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int ch = (n0 + j) * 2 + ((c & 3) >> 1);
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + lat_off(ra, ch) + half));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + lat_off(rb, ch) + half));
+      av[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) a.o[n0 + j] = mfma16(av[j], pb, a.o[n0 + j]);
+  }
+}
+
+__device__ __forceinline__ void write_result(const WaveAcc& a, const AttnParams& p, int tok, int split, int h,
+                                             bool head_ok, int g) {
+  float l_tot = a.l_run;
   l_tot += shfl_xor(l_tot, 16);
   l_tot += shfl_xor(l_tot, 32);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse_v = l_tot > 0.0f ? (m_run + log2f(l_tot)) * LN2 : -INFINITY;
+  const float lse_v = l_tot > 0.0f ? (a.m_run + log2f(l_tot)) * LN2 : -INFINITY;
   if (!head_ok) return;
   float* orow;
   float* lrow;
@@ -268,8 +204,214 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_kernel(AttnParams p) {
     lrow = p.part_lse + pi;
   }
 #pragma unroll
-  for (int nt = 0; nt < 32; ++nt) *(f32x4*)(orow + nt * 16 + g * 4) = o[nt] * inv;
+  for (int nt = 0; nt < 32; ++nt) *(f32x4*)(orow + nt * 16 + g * 4) = a.o[nt] * inv;
   if (g == 0 && lrow) *lrow = lse_v;
+}
+
+// Work mapping shared by both kernels.  Workgroups are dispatched
+// round-robin over the 8 XCDs, so the head groups of one (token, split) pair
+// are placed 8 blocks apart and share an XCD (and its L2) for the gathered
+// rows.
+struct Work {
+  int tok, split, hg, b, ctx, e_lo, e_hi, ntiles;
+};
+
+template <int NW>
+__device__ __forceinline__ bool map_work(const AttnParams& p, Work& w) {
+  const int nhg = cdiv(p.H, 16 * NW);
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3;
+  w.hg = slot % nhg;
+  const int pair = (slot / nhg) * 8 + xcd;
+  if (pair >= p.sv.num_tokens * p.num_splits) return false;
+  w.tok = pair / p.num_splits;
+  w.split = pair % p.num_splits;
+  w.b = seq_of_token(p.sv, w.tok);
+  w.ctx = p.sv.ctx_len[w.b];
+  w.e_lo = w.split * p.split_len;
+  w.e_hi = min(p.top_k, w.e_lo + p.split_len);
+  w.ntiles = w.e_hi > w.e_lo ? cdiv(w.e_hi - w.e_lo, TILE) : 0;
+  return true;
+}
+
+// Resolve the cache row of every index entry of the split into LDS:
+// rows[i] = row of entry e_lo + i, or ~row0 (negative) when the entry is not
+// a valid position (the dummy row0 keeps every gather in bounds).
+template <int THREADS>
+__device__ __forceinline__ void resolve_rows(const AttnParams& p, const Work& w, int* rows, int tid) {
+  const int32_t* idx_row = p.idx + (int64_t)w.tok * p.top_k;
+  const int row0 = (int)cache_row(p.sv, w.b, 0);
+  const int n = w.ntiles * TILE;
+  for (int i = tid; i < n; i += THREADS) {
+    const int e = w.e_lo + i;
+    const int s = e < w.e_hi ? idx_row[e] : -1;
+    rows[i] = (s >= 0 && s < w.ctx) ? (int)cache_row(p.sv, w.b, s) : ~row0;
+  }
+}
+
+__device__ __forceinline__ uint32_t tile_valid8(const int* rows, int g) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v |= (rows[(j >> 2) * 16 + g * 4 + (j & 3)] >= 0 ? 1u : 0u) << j;
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 rows: direct HBM -> LDS gathers through an NBUF-deep ring.
+// ---------------------------------------------------------------------------
+template <int NW, int NBUF, int MAXE>
+__global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF_BYTES];
+  __shared__ int rows_sh[MAXE];
+  constexpr int THREADS = NW * WAVE;
+  constexpr int LAT_PER_WAVE = TILE / NW;        // latent rows issued per wave per tile
+  constexpr int ROPE_INSTR = ROPE_TILE_BYTES / 1024;
+  constexpr int LOADS_PER_WAVE = LAT_PER_WAVE + (ROPE_INSTR + NW - 1) / NW;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  Work w;
+  if (!map_work<NW>(p, w)) return;
+  const int h = w.hg * 16 * NW + wave * 16 + c;
+  const bool head_ok = h < p.H;
+
+  resolve_rows<THREADS>(p, w, rows_sh, tid);
+  WaveAcc a;
+  load_q(a, p, w.tok, h, head_ok, g);
+  wait_vmcnt<0>();  // Q and index loads done: no compiler-inserted waits in the loop
+  __syncthreads();
+
+  // issue the gathers of tile k into ring slot k % NBUF
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
+  auto issue = [&](int k) {
+    const uint32_t buf = smem_base + (k % NBUF) * BUF_BYTES;
+    const int* rows = rows_sh + k * TILE;
+#pragma unroll
+    for (int j = 0; j < LAT_PER_WAVE; ++j) {
+      const int r = wave * LAT_PER_WAVE + j;
+      int row = rows[r];
+      row = row < 0 ? ~row : row;
+      dma16(p.kv + (int64_t)row * (ROW * 2) + (lane << 4), buf + r * LAT_STRIDE);
+    }
+#pragma unroll
+    for (int i = wave; i < ROPE_INSTR; i += NW) {
+      const int r = i * 8 + (lane >> 3);
+      int row = rows[r];
+      row = row < 0 ? ~row : row;
+      dma16(p.kv + (int64_t)row * (ROW * 2) + LATENT * 2 + (((lane & 7) ^ (r & 7)) << 4),
+            buf + LAT_TILE_BYTES + i * 1024);
+    }
+  };
+
+#pragma unroll
+  for (int k = 0; k < NBUF - 1; ++k)
+    if (k < w.ntiles) issue(k);
+
+  for (int k = 0; k < w.ntiles; ++k) {
+    // wait for this wave's gathers of tile k; later tiles stay in flight
+    const int later = min(NBUF - 2, w.ntiles - 1 - k);
+    if (later >= 2) wait_vmcnt<2 * LOADS_PER_WAVE>();
+    else if (later == 1) wait_vmcnt<LOADS_PER_WAVE>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // tile k visible to all waves; slot (k - 1) % NBUF is free
+    if (k + NBUF - 1 < w.ntiles) issue(k + NBUF - 1);
+    const int* rows = rows_sh + k * TILE;
+    compute_tile(a, smem + (k % NBUF) * BUF_BYTES, tile_valid8(rows, g), p.scale_log2, g, c);
+  }
+  write_result(a, p, w.tok, w.split, h, head_ok, g);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 rows: register staging with dequantisation, double-buffered LDS.
+// ---------------------------------------------------------------------------
+template <int NW>
+struct Fp8Stage {
+  static constexpr int THREADS = NW * WAVE;
+  // per row: 32 latent code chunks (16 codes each) + 8 rope chunks
+  static constexpr int CHUNKS = 40;
+  static constexpr int JOBS = (TILE * CHUNKS + THREADS - 1) / THREADS;
+  u32x4 raw[JOBS];
+  float scale[JOBS];
+
+  __device__ __forceinline__ void load(const AttnParams& p, const int* rows, int tid) {
+#pragma unroll
+    for (int k = 0; k < JOBS; ++k) {
+      const int j = tid + k * THREADS;
+      raw[k] = u32x4{0u, 0u, 0u, 0u};
+      scale[k] = 0.0f;
+      if (j < TILE * CHUNKS) {
+        const int r = j / CHUNKS, ch = j % CHUNKS;
+        const int row = rows[r];
+        if (row >= 0) {
+          const uint8_t* base = p.kv + (int64_t)row * FP8_ROW_BYTES;
+          if (ch < 32) {
+            raw[k] = *(const u32x4*)(base + ch * 16);
+            scale[k] = *(const float*)(base + LATENT + (ch >> 3) * 4);
+          } else {
+            raw[k] = *(const u32x4*)(base + LATENT + 16 + (ch - 32) * 16);
+          }
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* buf, int tid) {
+#pragma unroll
+    for (int k = 0; k < JOBS; ++k) {
+      const int j = tid + k * THREADS;
+      if (j < TILE * CHUNKS) {
+        const int r = j / CHUNKS, ch = j % CHUNKS;
+        if (ch < 32) {
+          const float sc = scale[k];
+          u32x2 a0 = e4m3x4_to_bf16(raw[k][0], sc), a1 = e4m3x4_to_bf16(raw[k][1], sc);
+          u32x2 a2 = e4m3x4_to_bf16(raw[k][2], sc), a3 = e4m3x4_to_bf16(raw[k][3], sc);
+          *(u32x4*)(buf + lat_off(r, 2 * ch)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+          *(u32x4*)(buf + lat_off(r, 2 * ch + 1)) = u32x4{a2[0], a2[1], a3[0], a3[1]};
+        } else {
+          *(u32x4*)(buf + rope_off(r, ch - 32)) = raw[k];
+        }
+      }
+    }
+  }
+};
+
+template <int NW, int MAXE>
+__global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF_BYTES];
+  __shared__ int rows_sh[MAXE];
+  constexpr int THREADS = NW * WAVE;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  Work w;
+  if (!map_work<NW>(p, w)) return;
+  const int h = w.hg * 16 * NW + wave * 16 + c;
+  const bool head_ok = h < p.H;
+
+  resolve_rows<THREADS>(p, w, rows_sh, tid);
+  WaveAcc a;
+  load_q(a, p, w.tok, h, head_ok, g);
+  __syncthreads();
+
+  Fp8Stage<NW> st;
+  if (w.ntiles > 0) {
+    st.load(p, rows_sh, tid);
+    st.store(smem, tid);
+  }
+  __syncthreads();
+  for (int k = 0; k < w.ntiles; ++k) {
+    const bool more = k + 1 < w.ntiles;
+    if (more) st.load(p, rows_sh + (k + 1) * TILE, tid);
+    compute_tile(a, smem + (k & 1) * BUF_BYTES, tile_valid8(rows_sh + k * TILE, g), p.scale_log2, g, c);
+    if (more) st.store(smem + ((k + 1) & 1) * BUF_BYTES, tid);
+    __syncthreads();
+  }
+  write_result(a, p, w.tok, w.split, h, head_ok, g);
 }
 
 // Merge split partials: lse = log sum_s exp(lse_s); O = sum_s exp(lse_s - lse) O_s.
@@ -285,10 +427,10 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnParams p) {
   if (mx != -INFINITY) {
     for (int s = 0; s < S; ++s) {
       const int64_t pi = base + (int64_t)s * p.H;
-      const float w = expf(p.part_lse[pi] - mx);
-      if (w > 0.0f) {
-        wsum += w;
-        acc += w * *(const f32x4*)(p.part_o + pi * LATENT + threadIdx.x * 4);
+      const float wgt = expf(p.part_lse[pi] - mx);
+      if (wgt > 0.0f) {
+        wsum += wgt;
+        acc += wgt * *(const f32x4*)(p.part_o + pi * LATENT + threadIdx.x * 4);
       }
     }
   }
@@ -298,20 +440,21 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnParams p) {
     p.lse[(int64_t)tok * p.H + h] = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
 }
 
-template <int NW, bool FP8>
-hipError_t launch_nw(const AttnParams& p, hipStream_t stream) {
-  const int nhg = cdiv(p.H, 16 * NW);
+template <typename K>
+hipError_t launch_grid(K kernel, const AttnParams& p, int nw, hipStream_t stream) {
+  const int nhg = cdiv(p.H, 16 * nw);
   const int pairs = p.sv.num_tokens * p.num_splits;
   const int blocks = cdiv(pairs, 8) * 8 * nhg;
-  hipLaunchKernelGGL((attn_kernel<NW, FP8>), dim3(blocks), dim3(NW * WAVE), 0, stream, p);
+  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(nw * WAVE), 0, stream, p);
   return hipGetLastError();
 }
 
-template <bool FP8>
-hipError_t launch_dt(const AttnParams& p, hipStream_t stream) {
-  if (p.H <= 16) return launch_nw<1, FP8>(p, stream);
-  if (p.H <= 32) return launch_nw<2, FP8>(p, stream);
-  return launch_nw<4, FP8>(p, stream);
+template <int NW>
+hipError_t launch_nw(const AttnParams& p, bool fp8, hipStream_t stream) {
+  const int tiles_per_split = cdiv(p.split_len, TILE);
+  if (fp8) return launch_grid(attn_fp8_kernel<NW, 2048>, p, NW, stream);
+  if (tiles_per_split * TILE <= 1024) return launch_grid(attn_bf16_kernel<NW, 4, 1024>, p, NW, stream);
+  return launch_grid(attn_bf16_kernel<NW, 3, 2048>, p, NW, stream);
 }
 
 }  // namespace
@@ -320,14 +463,17 @@ int attn_num_splits(int num_tokens, int H, int top_k) {
   const int nw = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
   const int nhg = cdiv(H, 16 * nw);
   const int items = num_tokens * nhg;
-  const int max_splits = std::max(1, cdiv(top_k, 2 * TILE));
-  int s = cdiv(1024, std::max(1, items));
+  const int max_splits = std::max(1, cdiv(top_k, 4 * TILE));
+  const int s = cdiv(256, std::max(1, items));
   return std::min(std::max(s, 1), max_splits);
 }
 
 hipError_t launch_attn(const AttnParams& p, bool kv_fp8, hipStream_t stream) {
   timer_before(2, stream);
-  hipError_t e = kv_fp8 ? launch_dt<true>(p, stream) : launch_dt<false>(p, stream);
+  hipError_t e;
+  if (p.H <= 16) e = launch_nw<1>(p, kv_fp8, stream);
+  else if (p.H <= 32) e = launch_nw<2>(p, kv_fp8, stream);
+  else e = launch_nw<4>(p, kv_fp8, stream);
   timer_after(2, stream);
   if (e != hipSuccess || p.num_splits == 1) return e;
   timer_before(3, stream);

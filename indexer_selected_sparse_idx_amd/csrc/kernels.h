@@ -58,6 +58,7 @@ struct TopkParams {
   int64_t score_stride;
   int top_k;
   int32_t* out_idx;        // [T, top_k]
+  int keys_in_lds;         // set by the launcher
 };
 
 struct AttnParams {
