@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run this many steps with no timing or oracle (for rocprofv3)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -138,6 +140,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for i in range(3):
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            print("copy %d: %d bytes read, %d bytes written" % (i, src.numel(), dst.numel()), flush=True)
+        return
     lib.lib()
     dev = torch.device("cuda:0")
     wl = config(2)

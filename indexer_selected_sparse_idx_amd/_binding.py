@@ -12,7 +12,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_HERE, "libidxsparse.so")
+# IDXSPARSE_LIB selects another build of the same library (e.g. a tuning
+# variant); by default the in-tree build is used.
+lib_path = os.environ.get("IDXSPARSE_LIB") or os.path.join(_HERE, "libidxsparse.so")
 
 IDX_OK = 0
 IDX_BF16, IDX_E4M3, IDX_KV_FP8_656 = 1, 2, 3

@@ -6,7 +6,7 @@
 
 #include <algorithm>
 
-#include "../../include/idxsparse.h"
+#include "idxsparse.h"
 #include "kernels.h"
 
 namespace idxs {

@@ -39,7 +39,7 @@ namespace idxs {
 namespace {
 
 constexpr int TILE = ATTN_TILE;                 // selected rows per tile
-constexpr int LAT_STRIDE = 1024 + 16;           // 512 bf16 per row, padded by one 16-byte chunk
+constexpr int LAT_STRIDE = 1024 + 32;           // 512 bf16 per row, padded by two 16-byte chunks
 constexpr int LAT_TILE_BYTES = TILE * LAT_STRIDE;
 constexpr int ROPE_TILE_BYTES = TILE * 128;     // 64 bf16 per row
 constexpr int BUF_BYTES = LAT_TILE_BYTES + ROPE_TILE_BYTES;
@@ -69,63 +69,86 @@ __device__ __forceinline__ void dma16(const uint8_t* gptr, uint32_t lds_addr) {
 }
 
 // LDS addresses of 16-byte chunk `ch` of tile row r.  Latent rows are padded
-// to 65 chunks, so 16 consecutive rows at one chunk hit 16 different bank
-// groups and every per-lane address is affine in ch (immediate offsets).
-// The rope part is XOR-swizzled instead.
-__device__ __forceinline__ int lat_off(int r, int ch) { return r * LAT_STRIDE + (ch << 4); }
+// to 66 chunks (rows 4 apart then share a bank window) and bit 0 of the
+// chunk index is flipped on rows with bit 2 set.  Then 8 consecutive rows at
+// one chunk (a 128-bit read of 8 lanes) cover all 32 banks, the 4 rows x 2
+// chunks of a transposing read of 16 lanes cover all 32 banks, and every
+// per-lane address stays affine in the chunk index (immediate offsets),
+// because the flip only touches the lane-dependent bit.  The rope part is
+// XOR-swizzled.
+__device__ __forceinline__ int lat_flip(int r) { return (r >> 2) & 1; }
+__device__ __forceinline__ int lat_off(int r, int ch) { return r * LAT_STRIDE + ((ch ^ lat_flip(r)) << 4); }
 __device__ __forceinline__ int rope_off(int r, int ch) { return LAT_TILE_BYTES + r * 128 + ((ch ^ (r & 7)) << 4); }
 
-// Per-wave state of the online softmax and the O^T accumulator.
-struct WaveAcc {
-  bf16x8 qb[18];   // Q^T operand: lane holds Q[h][32 ks + 8 g .. +8]
-  f32x4 o[32];     // O^T[dv = 16 nt + 4 g + r][head c]
+// Per-wave state of the online softmax and the O^T accumulator: the wave
+// holds NQ of the 18 k-steps of its Q^T operand (lane: Q[h][32 ks + 8 g .. +8])
+// and NT of the 32 dv tiles of O^T (lane: O^T[dv = 16 nt + 4 g + r][head c]).
+template <int NQ, int NT>
+struct WaveAccT {
+  bf16x8 qb[NQ];
+  f32x4 o[NT];
   float m_run, l_run;
   int tiles;       // tiles processed so far
 };
+typedef WaveAccT<18, 32> WaveAcc;
 
-__device__ __forceinline__ void load_q(WaveAcc& a, const AttnParams& p, int tok, int h, bool head_ok, int g) {
+template <int NQ, int NT>
+__device__ __forceinline__ void load_q(WaveAccT<NQ, NT>& a, const AttnParams& p, int tok, int h, bool head_ok, int g,
+                                       int ks0 = 0) {
   const uint16_t* qrow = p.q + ((int64_t)tok * p.H + (head_ok ? h : 0)) * ROW;
 #pragma unroll
-  for (int ks = 0; ks < 18; ++ks) {
+  for (int kk = 0; kk < NQ; ++kk) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (head_ok) v = *(const u32x4*)(qrow + ks * 32 + g * 8);
-    a.qb[ks] = as_bf16x8(v);
+    if (head_ok) v = *(const u32x4*)(qrow + (ks0 + kk) * 32 + g * 8);
+    a.qb[kk] = as_bf16x8(v);
   }
 #pragma unroll
-  for (int nt = 0; nt < 32; ++nt) a.o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int nt = 0; nt < NT; ++nt) a.o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   a.m_run = -INFINITY;
   a.l_run = 0.0f;
   a.tiles = 0;
 }
 
-// One tile of 32 keys from LDS buffer `buf`; valid8 bit j says whether key
-// 16 (j / 4) + 4 g + j % 4 of the tile is a real selected row.
-__device__ __forceinline__ void compute_tile(WaveAcc& a, const uint8_t* buf, uint32_t valid8, float scale_log2,
-                                             int g, int c) {
-  // ---- S^T = C . Q^T -----------------------------------------------------
-  f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-  constexpr int KB = 6;  // k-steps whose operands are read from LDS together
+// Per-lane addresses inside a tile buffer.
+struct TileAddr {
+  int s_lat[2];   // S-phase latent operand of key tiles mt = 0, 1 (chunk 4 ks + g added as offset)
+  int s_rope[2][2];
+  int v_lo, v_hi; // V^T operand rows 4 g + c / 4 and 16 + 4 g + c / 4
+  __device__ __forceinline__ void init(int g, int c) {
 #pragma unroll
-  for (int k0 = 0; k0 < 18; k0 += KB) {
-    bf16x8 av[KB][2];
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
-      const int ks = k0 + kk;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int r = mt * 16 + c;
-        const int off = ks < 16 ? lat_off(r, ks * 4 + g) : rope_off(r, (ks - 16) * 4 + g);
-        av[kk][mt] = *(const bf16x8*)(buf + off);
-      }
+    for (int mt = 0; mt < 2; ++mt) {
+      const int r = mt * 16 + c;
+      s_lat[mt] = lat_off(r, g);
+      s_rope[mt][0] = rope_off(r, g);
+      s_rope[mt][1] = rope_off(r, 4 + g);
     }
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma16(av[kk][mt], a.qb[k0 + kk], sacc[mt]);
-    }
+    const int ra = 4 * g + (c >> 2);
+    const int half = (c & 1) * 8;
+    v_lo = lat_off(ra, (c & 3) >> 1) + half;
+    v_hi = lat_off(ra + 16, (c & 3) >> 1) + half;
   }
+  __device__ __forceinline__ int s_off(int ks, int mt) const {
+    return ks < 16 ? s_lat[mt] + ks * 64 : s_rope[mt][ks - 16];
+  }
+};
 
-  // ---- online softmax (base 2) ---------------------------------------------
+__device__ __forceinline__ bf16x8 s_operand(const uint8_t* buf, const TileAddr& ad, int ks, int mt) {
+  return *(const bf16x8*)(buf + ad.s_off(ks, mt));
+}
+
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* buf, const TileAddr& ad, int nt) {
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + ad.v_lo + nt * 32));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + ad.v_hi + nt * 32));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Online softmax of one S^T tile (base 2).  valid8 bit j says whether key
+// 16 (j / 4) + 4 g + j % 4 of the tile is a real selected row.  Returns the
+// P^T operand of the tile and rescales the O^T accumulator when the running
+// max moves.
+template <int NQ, int NT>
+__device__ __forceinline__ bf16x8 softmax_tile(WaveAccT<NQ, NT>& a, const f32x4 (&sacc)[2], uint32_t valid8,
+                                               float scale_log2) {
   float x[8];
   float tmax = -INFINITY;
 #pragma unroll
@@ -153,40 +176,89 @@ __device__ __forceinline__ void compute_tile(WaveAcc& a, const uint8_t* buf, uin
   for (int j = 0; j < 8; ++j) psum += pv[j];
   a.l_run = a.l_run * alpha + psum;
   a.m_run = m_new;
+  if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) a.o[nt] *= alpha;
+  }
   u32x4 pk;
   pk[0] = pack_bf16x2(pv[0], pv[1]);
   pk[1] = pack_bf16x2(pv[2], pv[3]);
   pk[2] = pack_bf16x2(pv[4], pv[5]);
   pk[3] = pack_bf16x2(pv[6], pv[7]);
-  const bf16x8 pb = as_bf16x8(pk);
+  return as_bf16x8(pk);
+}
 
-  if (__ballot(alpha != 1.0f)) {
+// S^T[32 keys x 16 heads] = C_tile . Q^T over k-steps [ks0, ks0 + NQ).  The
+// operands of SB k-steps are read from LDS one batch ahead of the MFMAs
+// that use them, and even / odd k-steps accumulate into separate chains, so
+// neither LDS latency nor the MFMA dependency latency is exposed per step.
+template <int NQ, int NT>
+__device__ __forceinline__ void s_phase(const WaveAccT<NQ, NT>& a, const uint8_t* buf, const TileAddr& ad,
+                                        f32x4 (&sacc)[2], int ks0 = 0) {
+  constexpr int SB = NQ % 6 == 0 ? 6 : (NQ % 3 == 0 ? 3 : 1);
+  constexpr int NB = NQ / SB;
+  f32x4 acc[2][2];
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) a.o[nt] *= alpha;
-  }
-
-  // ---- O^T += V^T . P^T ----------------------------------------------------------
-  // k-slot j of lane group g is key 16 (j / 4) + 4 g + j % 4 (the S^T layout).
-  const int ra = 4 * g + (c >> 2), rb = ra + 16;
-  const int half = (c & 1) * 8;
-  constexpr int NB = 4;  // dv tiles whose V^T operands are read together
+  for (int mt = 0; mt < 2; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  bf16x8 op[2][SB][2];
 #pragma unroll
-  for (int n0 = 0; n0 < 32; n0 += NB) {
-    bf16x8 av[NB];
+  for (int kk = 0; kk < SB; ++kk)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int ch = (n0 + j) * 2 + ((c & 3) >> 1);
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + lat_off(ra, ch) + half));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + lat_off(rb, ch) + half));
-      av[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int mt = 0; mt < 2; ++mt) op[0][kk][mt] = s_operand(buf, ad, ks0 + kk, mt);
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi) {
+    if (bi + 1 < NB) {
+#pragma unroll
+      for (int kk = 0; kk < SB; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) op[(bi + 1) & 1][kk][mt] = s_operand(buf, ad, ks0 + (bi + 1) * SB + kk, mt);
     }
 #pragma unroll
-    for (int j = 0; j < NB; ++j) a.o[n0 + j] = mfma16(av[j], pb, a.o[n0 + j]);
+    for (int kk = 0; kk < SB; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        acc[mt][kk & 1] = mfma16(op[bi & 1][kk][mt], a.qb[bi * SB + kk], acc[mt][kk & 1]);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) sacc[mt] = acc[mt][0] + acc[mt][1];
+}
+
+// O^T += V^T . P^T over dv tiles [nt0, nt0 + NT); the k-slot j of lane group
+// g is key 16 (j / 4) + 4 g + j % 4 (the S^T register layout), which the
+// V^T operand rows follow.  Operands of VB tiles are read one batch ahead.
+template <int NQ, int NT>
+__device__ __forceinline__ void v_phase(WaveAccT<NQ, NT>& a, const uint8_t* buf, const TileAddr& ad, bf16x8 pb,
+                                        int nt0 = 0) {
+  constexpr int VB = 4;
+  constexpr int NB = NT / VB;
+  bf16x8 op[2][VB];
+#pragma unroll
+  for (int j = 0; j < VB; ++j) op[0][j] = v_operand(buf, ad, nt0 + j);
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi) {
+    if (bi + 1 < NB) {
+#pragma unroll
+      for (int j = 0; j < VB; ++j) op[(bi + 1) & 1][j] = v_operand(buf, ad, nt0 + (bi + 1) * VB + j);
+    }
+#pragma unroll
+    for (int j = 0; j < VB; ++j) a.o[bi * VB + j] = mfma16(op[bi & 1][j], pb, a.o[bi * VB + j]);
   }
 }
 
-__device__ __forceinline__ void write_result(const WaveAcc& a, const AttnParams& p, int tok, int split, int h,
-                                             bool head_ok, int g) {
+// One tile, start to finish (used by the FP8 path).
+__device__ __forceinline__ void compute_tile(WaveAcc& a, const uint8_t* buf, const TileAddr& ad, uint32_t valid8,
+                                             float scale_log2) {
+  f32x4 sacc[2];
+  s_phase(a, buf, ad, sacc);
+  const bf16x8 pb = softmax_tile(a, sacc, valid8, scale_log2);
+  v_phase(a, buf, ad, pb);
+}
+
+// Normalise and store the wave's O^T tiles (dv tiles nt0 .. nt0 + NT) and, if
+// write_lse, its lse.
+template <int NQ, int NT>
+__device__ __forceinline__ void write_result(const WaveAccT<NQ, NT>& a, const AttnParams& p, int tok, int split,
+                                             int h, bool head_ok, int g, int nt0 = 0, bool write_lse = true) {
   float l_tot = a.l_run;
   l_tot += shfl_xor(l_tot, 16);
   l_tot += shfl_xor(l_tot, 32);
@@ -204,8 +276,8 @@ __device__ __forceinline__ void write_result(const WaveAcc& a, const AttnParams&
     lrow = p.part_lse + pi;
   }
 #pragma unroll
-  for (int nt = 0; nt < 32; ++nt) *(f32x4*)(orow + nt * 16 + g * 4) = a.o[nt] * inv;
-  if (g == 0 && lrow) *lrow = lse_v;
+  for (int nt = 0; nt < NT; ++nt) *(f32x4*)(orow + (nt0 + nt) * 16 + g * 4) = a.o[nt] * inv;
+  if (write_lse && g == 0 && lrow) *lrow = lse_v;
 }
 
 // Work mapping shared by both kernels.  Workgroups are dispatched
@@ -294,7 +366,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
       const int r = wave * LAT_PER_WAVE + j;
       int row = rows[r];
       row = row < 0 ? ~row : row;
-      dma16(p.kv + (int64_t)row * (ROW * 2) + (lane << 4), buf + r * LAT_STRIDE);
+      dma16(p.kv + (int64_t)row * (ROW * 2) + ((lane ^ lat_flip(r)) << 4), buf + r * LAT_STRIDE);
     }
 #pragma unroll
     for (int i = wave; i < ROPE_INSTR; i += NW) {
@@ -306,20 +378,23 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
     }
   };
 
+  TileAddr ad;
+  ad.init(g, c);
 #pragma unroll
   for (int k = 0; k < NBUF - 1; ++k)
     if (k < w.ntiles) issue(k);
 
+  // Iteration k: wait for this wave's gathers of tile k (later tiles stay in
+  // flight), one barrier (tile k visible to every wave; ring slot
+  // (k - 1) % NBUF is free again), issue tile k + NBUF - 1, compute tile k.
   for (int k = 0; k < w.ntiles; ++k) {
-    // wait for this wave's gathers of tile k; later tiles stay in flight
     const int later = min(NBUF - 2, w.ntiles - 1 - k);
     if (later >= 2) wait_vmcnt<2 * LOADS_PER_WAVE>();
     else if (later == 1) wait_vmcnt<LOADS_PER_WAVE>();
     else wait_vmcnt<0>();
-    __syncthreads();  // tile k visible to all waves; slot (k - 1) % NBUF is free
+    __syncthreads();
     if (k + NBUF - 1 < w.ntiles) issue(k + NBUF - 1);
-    const int* rows = rows_sh + k * TILE;
-    compute_tile(a, smem + (k % NBUF) * BUF_BYTES, tile_valid8(rows, g), p.scale_log2, g, c);
+    compute_tile(a, smem + (k % NBUF) * BUF_BYTES, ad, tile_valid8(rows_sh + k * TILE, g), p.scale_log2);
   }
   write_result(a, p, w.tok, w.split, h, head_ok, g);
 }
@@ -398,6 +473,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
   load_q(a, p, w.tok, h, head_ok, g);
   __syncthreads();
 
+  TileAddr ad;
+  ad.init(g, c);
   Fp8Stage<NW> st;
   if (w.ntiles > 0) {
     st.load(p, rows_sh, tid);
@@ -407,7 +484,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
   for (int k = 0; k < w.ntiles; ++k) {
     const bool more = k + 1 < w.ntiles;
     if (more) st.load(p, rows_sh + (k + 1) * TILE, tid);
-    compute_tile(a, smem + (k & 1) * BUF_BYTES, tile_valid8(rows_sh + k * TILE, g), p.scale_log2, g, c);
+    compute_tile(a, smem + (k & 1) * BUF_BYTES, ad, tile_valid8(rows_sh + k * TILE, g), p.scale_log2);
     if (more) st.store(smem + ((k + 1) & 1) * BUF_BYTES, tid);
     __syncthreads();
   }
@@ -440,21 +517,22 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnParams p) {
     p.lse[(int64_t)tok * p.H + h] = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
 }
 
+// nhg16: 16-head groups per block; waves: waves per block
 template <typename K>
-hipError_t launch_grid(K kernel, const AttnParams& p, int nw, hipStream_t stream) {
-  const int nhg = cdiv(p.H, 16 * nw);
+hipError_t launch_grid(K kernel, const AttnParams& p, int nhg16, int waves, hipStream_t stream) {
+  const int nhg = cdiv(p.H, 16 * nhg16);
   const int pairs = p.sv.num_tokens * p.num_splits;
   const int blocks = cdiv(pairs, 8) * 8 * nhg;
-  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(nw * WAVE), 0, stream, p);
+  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(waves * WAVE), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int NW>
 hipError_t launch_nw(const AttnParams& p, bool fp8, hipStream_t stream) {
   const int tiles_per_split = cdiv(p.split_len, TILE);
-  if (fp8) return launch_grid(attn_fp8_kernel<NW, 2048>, p, NW, stream);
-  if (tiles_per_split * TILE <= 1024) return launch_grid(attn_bf16_kernel<NW, 4, 1024>, p, NW, stream);
-  return launch_grid(attn_bf16_kernel<NW, 3, 2048>, p, NW, stream);
+  if (fp8) return launch_grid(attn_fp8_kernel<NW, 2048>, p, NW, NW, stream);
+  if (tiles_per_split * TILE <= 1024) return launch_grid(attn_bf16_kernel<NW, 4, 1024>, p, NW, NW, stream);
+  return launch_grid(attn_bf16_kernel<NW, 3, 2048>, p, NW, NW, stream);
 }
 
 }  // namespace

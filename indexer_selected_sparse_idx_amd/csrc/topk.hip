@@ -9,17 +9,21 @@
 //
 // One workgroup (16 waves) per row:
 // 1. Rows of up to 32768 candidates are converted to keys once and kept in
-//    LDS; longer rows are re-read from the (L2-resident) score row.
+//    LDS; longer rows are re-read from the (L2-resident) score row.  Every
+//    pass reads 4 consecutive keys per lane with one vector access and keeps
+//    several such accesses in flight.
 // 2. Up to four 8-bit digit passes, most significant first, histogram the
-//    keys that share the digits chosen so far.  Histogram updates are
-//    aggregated per wavefront (ballot on the leading lane's bin) because
-//    integer-valued scores put most keys into a few bins.  A one-wave suffix
-//    scan picks the digit whose bucket holds the m-th largest key; when that
-//    bucket is taken whole the passes stop early.
+//    keys that share the digits chosen so far.  Every wave owns a private
+//    LDS histogram (merged after the pass): integer-valued scores put most
+//    keys into a few bins, and same-address atomics from different waves
+//    would serialise.  A one-wave suffix scan picks the digit whose bucket
+//    holds the m-th largest key; when that bucket is taken whole the passes
+//    stop early.
 // 3. Ordered compaction: each wave owns a contiguous segment of the row,
 //    counts its keys above / equal to the threshold, and after one exclusive
-//    scan over the waves emits them with ballot + popcount prefixes, so the
-//    equal keys are taken lowest position first.
+//    scan over the waves emits them in position order (a wavefront prefix
+//    sum over the per-lane counts), so equal keys are taken lowest position
+//    first.
 // Rows with t + 1 <= K skip the selection: every position is taken.
 #include <algorithm>
 
@@ -33,60 +37,84 @@ namespace {
 constexpr int TOPK_THREADS = 1024;
 constexpr int TOPK_WAVES = TOPK_THREADS / WAVE;
 constexpr int LDS_KEYS = 32768;
+constexpr int UNROLL = 4;  // 4-key vector accesses in flight per lane
 
-__device__ __forceinline__ uint64_t lanes_below(int lane) {
-  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
-}
-
-// hist[bin] += 1 for every active lane, one LDS atomic per distinct bin for
-// the first few bins, plain atomics for whatever remains.
-__device__ __forceinline__ void hist_add(uint32_t* hist, bool active, uint32_t bin, int lane) {
-  uint64_t act = __ballot(active);
-#pragma unroll 1
-  for (int it = 0; it < 4 && act; ++it) {
-    const int leader = __builtin_ctzll(act);
-    const uint32_t lbin = __shfl(bin, leader);
-    const uint64_t same = __ballot(active && bin == lbin);
-    if (lane == leader) atomicAdd(&hist[lbin], (uint32_t)__popcll(same));
-    if (bin == lbin) active = false;
-    act &= ~same;
+// Key source: the LDS copy of the row, or the fp32 score row itself.
+template <bool IN_LDS>
+struct Keys {
+  const uint32_t* lds;
+  const float* row;
+  int n;
+  // keys i .. i+3 (i % 4 == 0); positions >= n read as 0 (never selected)
+  __device__ __forceinline__ u32x4 get4(int i) const {
+    u32x4 k;
+    if (i + 3 < n) {
+      if (IN_LDS) {
+        k = *(const u32x4*)(lds + i);
+      } else {
+        const f32x4 f = *(const f32x4*)(row + i);
+        k = u32x4{score_key(f[0]), score_key(f[1]), score_key(f[2]), score_key(f[3])};
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) k[e] = i + e < n ? (IN_LDS ? lds[i + e] : score_key(row[i + e])) : 0u;
+    }
+    return k;
   }
-  if (active) atomicAdd(&hist[bin], 1u);
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
 }
 
 template <bool IN_LDS>
-__device__ __forceinline__ uint32_t key_at(const uint32_t* keys, const float* row, int i) {
-  return IN_LDS ? keys[i] : score_key(row[i]);
-}
-
-template <bool IN_LDS>
-__device__ void select_row(const float* row, int n, int m, int K, int32_t* out, uint32_t* keys, uint32_t* hist,
+__device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out, uint32_t* hist, uint32_t* whist,
                            uint32_t* wcnt) {
   __shared__ uint32_t sh_digit, sh_above, sh_whole;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  if (IN_LDS) {
-    for (int i = tid; i < n; i += TOPK_THREADS) keys[i] = score_key(row[i]);
-  }
   // ---- radix passes ----------------------------------------------------------
   uint32_t prefix = 0;  // digits chosen so far
   uint32_t rem = m;     // positions still to take inside the current bucket
   int level = 0;        // number of digits fixed
+  uint32_t* my_hist = whist + wave * 256;
+  const int n4 = (n + 3) / 4 * 4;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += TOPK_THREADS) hist[i] = 0;
-    __syncthreads();
-    const int n_pad = (n + TOPK_THREADS - 1) / TOPK_THREADS * TOPK_THREADS;
-    for (int i = tid; i < n_pad; i += TOPK_THREADS) {
-      uint32_t key = 0;
-      bool in = false;
-      if (i < n) {
-        key = key_at<IN_LDS>(keys, row, i);
-        in = pass == 0 || (key >> (shift + 8)) == prefix;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) my_hist[lane + 64 * j] = 0;
+    for (int i0 = 4 * tid; i0 < n4; i0 += 4 * TOPK_THREADS * UNROLL) {
+      u32x4 k[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int i = i0 + u * 4 * TOPK_THREADS;
+        k[u] = i < n4 ? keys.get4(i) : u32x4{0u, 0u, 0u, 0u};
       }
-      hist_add(hist, in, (key >> shift) & 255u, lane);
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int i = i0 + u * 4 * TOPK_THREADS;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = k[u][e];
+          const bool in = i + e < n && (pass == 0 || (key >> (shift + 8)) == prefix);
+          if (in) atomicAdd(&my_hist[(key >> shift) & 255u], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t tot = 0;
+#pragma unroll
+      for (int w = 0; w < TOPK_WAVES; ++w) tot += whist[w * 256 + tid];
+      hist[tid] = tot;
     }
     __syncthreads();
     if (wave == 0) {
@@ -128,52 +156,69 @@ __device__ void select_row(const float* row, int n, int m, int K, int32_t* out, 
   const uint32_t need = rem;       // prefix-equal positions to take
   const uint32_t n_gt = m - need;  // positions above the prefix
 
-  // ---- ordered compaction over per-wave segments ---------------------------------
-  const int seg = (n + TOPK_WAVES - 1) / TOPK_WAVES;
-  const int lo = wave * seg, hi = min(n, lo + seg);
+  // ---- ordered compaction over per-wave segments (multiples of 256 keys) ------
+  const int seg = (n4 + TOPK_WAVES * 256 - 1) / (TOPK_WAVES * 256) * 256;
+  const int lo = wave * seg, hi = min(n4, lo + seg);
   uint32_t c_gt = 0, c_eq = 0;
-  for (int i0 = lo; i0 < hi; i0 += 64) {
-    const int i = i0 + lane;
-    bool gt = false, eq = false;
+  for (int i0 = lo; i0 < hi; i0 += 256) {
+    const int i = i0 + 4 * lane;
     if (i < hi) {
-      const uint64_t k = (uint64_t)key_at<IN_LDS>(keys, row, i) >> cshift;
-      gt = k > prefix;
-      eq = k == prefix;
+      const u32x4 k = keys.get4(i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t kk = (uint64_t)k[e] >> cshift;
+        const bool valid = i + e < n;
+        c_gt += (valid && kk > prefix);
+        c_eq += (valid && kk == prefix);
+      }
     }
-    c_gt += __popcll(__ballot(gt));
-    c_eq += __popcll(__ballot(eq));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    c_gt += __shfl_xor(c_gt, off);
+    c_eq += __shfl_xor(c_eq, off);
   }
   if (lane == 0) { wcnt[wave] = c_gt; wcnt[TOPK_WAVES + wave] = c_eq; }
   __syncthreads();
   uint32_t base_gt = 0, base_eq = 0;
   for (int w = 0; w < wave; ++w) { base_gt += wcnt[w]; base_eq += wcnt[TOPK_WAVES + w]; }
   if (base_eq >= need && c_gt == 0) return;
-  const uint64_t below = lanes_below(lane);
-  for (int i0 = lo; i0 < hi; i0 += 64) {
-    const int i = i0 + lane;
-    bool gt = false, eq = false;
+  for (int i0 = lo; i0 < hi; i0 += 256) {
+    const int i = i0 + 4 * lane;
+    uint32_t fg = 0, fe = 0;  // per-element flags, bit e
     if (i < hi) {
-      const uint64_t k = (uint64_t)key_at<IN_LDS>(keys, row, i) >> cshift;
-      gt = k > prefix;
-      eq = k == prefix;
+      const u32x4 k = keys.get4(i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t kk = (uint64_t)k[e] >> cshift;
+        const bool valid = i + e < n;
+        fg |= (uint32_t)(valid && kk > prefix) << e;
+        fe |= (uint32_t)(valid && kk == prefix) << e;
+      }
     }
-    const uint64_t bg = __ballot(gt), be = __ballot(eq);
-    if (gt) {
-      const uint32_t slot = base_gt + __popcll(bg & below);
-      if (slot < n_gt) out[slot] = i;
+    const uint32_t ng = __popc(fg), ne = __popc(fe);
+    const uint32_t sg = wave_incl_scan(ng, lane), se = wave_incl_scan(ne, lane);
+    uint32_t pg = base_gt + sg - ng, pe = base_eq + se - ne;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if ((fg >> e) & 1u) {
+        if (pg < n_gt) out[pg] = i + e;
+        ++pg;
+      }
+      if ((fe >> e) & 1u) {
+        if (pe < need) out[n_gt + pe] = i + e;
+        ++pe;
+      }
     }
-    if (eq) {
-      const uint32_t slot = base_eq + __popcll(be & below);
-      if (slot < need) out[n_gt + slot] = i;
-    }
-    base_gt += __popcll(bg);
-    base_eq += __popcll(be);
+    base_gt += __shfl(sg, 63);
+    base_eq += __shfl(se, 63);
   }
 }
 
 __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkParams p) {
   extern __shared__ uint32_t dyn[];
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t whist[TOPK_WAVES * 256];
   __shared__ uint32_t wcnt[2 * TOPK_WAVES];
 
   const int tid = threadIdx.x;
@@ -193,8 +238,28 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkParams p) {
     for (int i = tid; i < n; i += TOPK_THREADS) out[i] = i;
     return;
   }
-  if (n <= LDS_KEYS && p.keys_in_lds) select_row<true>(row, n, m, K, out, dyn, hist, wcnt);
-  else select_row<false>(row, n, m, K, out, dyn, hist, wcnt);
+  if (n <= LDS_KEYS && p.keys_in_lds) {
+    // copy the row into LDS as keys, 4 per lane per access, UNROLL in flight
+    const int n4 = (n + 3) / 4 * 4;
+    const Keys<false> src{nullptr, row, n};
+    for (int i0 = 4 * tid; i0 < n4; i0 += 4 * TOPK_THREADS * UNROLL) {
+      u32x4 k[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int i = i0 + u * 4 * TOPK_THREADS;
+        if (i < n4) k[u] = src.get4(i);
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int i = i0 + u * 4 * TOPK_THREADS;
+        if (i < n4) *(u32x4*)(dyn + i) = k[u];
+      }
+    }
+    __syncthreads();
+    select_row<true>(Keys<true>{dyn, row, n}, n, m, out, hist, whist, wcnt);
+  } else {
+    select_row<false>(Keys<false>{nullptr, row, n}, n, m, out, hist, whist, wcnt);
+  }
 }
 
 }  // namespace
@@ -203,7 +268,8 @@ hipError_t launch_topk(const TopkParams& p0, hipStream_t stream) {
   TopkParams p = p0;
   // LDS key cache only when some row can use it (dynamic LDS is sized per launch)
   p.keys_in_lds = p.sv.max_ctx_len > p.top_k ? 1 : 0;
-  const size_t dyn = p.keys_in_lds ? (size_t)std::min(p.sv.max_ctx_len, LDS_KEYS) * sizeof(uint32_t) : 0;
+  const int cap = (std::min(p.sv.max_ctx_len, LDS_KEYS) + 3) / 4 * 4;
+  const size_t dyn = p.keys_in_lds ? (size_t)cap * sizeof(uint32_t) : 0;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
