@@ -44,7 +44,7 @@ constexpr int LAT_TILE_BYTES = TILE * LAT_STRIDE;
 constexpr int ROPE_TILE_BYTES = TILE * 128;     // 64 bf16 per row
 constexpr int BUF_BYTES = LAT_TILE_BYTES + ROPE_TILE_BYTES;
 constexpr float RESCALE_SLACK = 8.0f;           // log2 growth of the running max tolerated before rescaling
-constexpr int EAGER_TILES = 4;                  // tiles with exact running-max normalisation
+constexpr int EAGER_TILES = 1;                  // tiles with exact running-max normalisation
 constexpr float LN2 = 0.69314718055994530942f;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -146,8 +146,12 @@ __device__ __forceinline__ bf16x8 v_operand(const uint8_t* buf, const TileAddr& 
 // 16 (j / 4) + 4 g + j % 4 of the tile is a real selected row.  Returns the
 // P^T operand of the tile and rescales the O^T accumulator when the running
 // max moves.
+struct PSplit {
+  bf16x8 hi, lo;
+};
+
 template <int NQ, int NT>
-__device__ __forceinline__ bf16x8 softmax_tile(WaveAccT<NQ, NT>& a, const f32x4 (&sacc)[2], uint32_t valid8,
+__device__ __forceinline__ PSplit softmax_tile(WaveAccT<NQ, NT>& a, const f32x4 (&sacc)[2], uint32_t valid8,
                                                float scale_log2) {
   float x[8];
   float tmax = -INFINITY;
@@ -160,8 +164,8 @@ __device__ __forceinline__ bf16x8 softmax_tile(WaveAccT<NQ, NT>& a, const f32x4 
   tmax = fmaxf(tmax, shfl_xor(tmax, 32));
   // Lazy rescaling: after the first EAGER_TILES tiles keep the running max
   // unless the tile exceeds it by more than RESCALE_SLACK (p values then
-  // stay below 2^RESCALE_SLACK).  The early tiles, where the max moves most,
-  // normalise exactly so the dominant weights stay exact in bf16.
+  // stay below 2^RESCALE_SLACK; with P split into two bf16 parts their
+  // rounding does not depend on the reference).
   const bool first = a.m_run == -INFINITY;
   const float slack = a.tiles < EAGER_TILES ? 0.0f : RESCALE_SLACK;
   a.tiles++;
@@ -180,12 +184,19 @@ __device__ __forceinline__ bf16x8 softmax_tile(WaveAccT<NQ, NT>& a, const f32x4 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) a.o[nt] *= alpha;
   }
-  u32x4 pk;
-  pk[0] = pack_bf16x2(pv[0], pv[1]);
-  pk[1] = pack_bf16x2(pv[2], pv[3]);
-  pk[2] = pack_bf16x2(pv[4], pv[5]);
-  pk[3] = pack_bf16x2(pv[6], pv[7]);
-  return as_bf16x8(pk);
+  // P = P_hi + P_lo, both bf16: the PV product runs twice on the same V^T
+  // operand, so P carries ~16 mantissa bits instead of 8.
+  u32x4 hi, lo;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const __bf16 h0 = (__bf16)pv[2 * j], h1 = (__bf16)pv[2 * j + 1];
+    hi[j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    lo[j] = pack_bf16x2(pv[2 * j] - (float)h0, pv[2 * j + 1] - (float)h1);
+  }
+  PSplit r;
+  r.hi = as_bf16x8(hi);
+  r.lo = as_bf16x8(lo);
+  return r;
 }
 
 // S^T[32 keys x 16 heads] = C_tile . Q^T over k-steps [ks0, ks0 + NQ).  The
@@ -227,7 +238,7 @@ __device__ __forceinline__ void s_phase(const WaveAccT<NQ, NT>& a, const uint8_t
 // g is key 16 (j / 4) + 4 g + j % 4 (the S^T register layout), which the
 // V^T operand rows follow.  Operands of VB tiles are read one batch ahead.
 template <int NQ, int NT>
-__device__ __forceinline__ void v_phase(WaveAccT<NQ, NT>& a, const uint8_t* buf, const TileAddr& ad, bf16x8 pb,
+__device__ __forceinline__ void v_phase(WaveAccT<NQ, NT>& a, const uint8_t* buf, const TileAddr& ad, PSplit pb,
                                         int nt0 = 0) {
   constexpr int VB = 4;
   constexpr int NB = NT / VB;
@@ -241,7 +252,9 @@ __device__ __forceinline__ void v_phase(WaveAccT<NQ, NT>& a, const uint8_t* buf,
       for (int j = 0; j < VB; ++j) op[(bi + 1) & 1][j] = v_operand(buf, ad, nt0 + (bi + 1) * VB + j);
     }
 #pragma unroll
-    for (int j = 0; j < VB; ++j) a.o[bi * VB + j] = mfma16(op[bi & 1][j], pb, a.o[bi * VB + j]);
+    for (int j = 0; j < VB; ++j) a.o[bi * VB + j] = mfma16(op[bi & 1][j], pb.hi, a.o[bi * VB + j]);
+#pragma unroll
+    for (int j = 0; j < VB; ++j) a.o[bi * VB + j] = mfma16(op[bi & 1][j], pb.lo, a.o[bi * VB + j]);
   }
 }
 
@@ -250,7 +263,7 @@ __device__ __forceinline__ void compute_tile(WaveAcc& a, const uint8_t* buf, con
                                              float scale_log2) {
   f32x4 sacc[2];
   s_phase(a, buf, ad, sacc);
-  const bf16x8 pb = softmax_tile(a, sacc, valid8, scale_log2);
+  const PSplit pb = softmax_tile(a, sacc, valid8, scale_log2);
   v_phase(a, buf, ad, pb);
 }
 
