@@ -153,3 +153,13 @@ def test_workspace_sizes(L):
 def test_timer_arm_rejects_bad_kernel(L):
     assert L.idx_timer_arm(9, FAKE, FAKE) == -1
     assert L.idx_timer_arm(0, None, FAKE) == -1
+
+
+def test_empty_batch_is_a_no_op(L):
+    # T = 0: every entry point returns IDX_OK without launching anything
+    s = seqs(cu_q=FAKE, num_tokens=0)
+    assert score(L, s, ws=None, wsb=0) == 0
+    assert attn(L, s, ws=None, wsb=0) == 0
+    rc = L.idx_sparse_attn_prefill(ctypes.byref(s), FAKE, 1, FAKE, 1, None, FAKE, 64, 128, 2048,
+                                   FAKE, 128, FAKE, 1, 1 / 24, FAKE, None, None, None, 0, None)
+    assert rc == 0
