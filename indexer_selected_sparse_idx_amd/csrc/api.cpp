@@ -95,8 +95,12 @@ int check_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, int k
   return IDX_OK;
 }
 
-size_t score_ws_bytes(const idx_seqs* s) {
+// score workspace: fp32 score rows, then the per-row key histograms
+size_t score_rows_bytes(const idx_seqs* s) {
   return align_up((size_t)std::max(s->num_tokens, 0) * (size_t)score_stride(s) * sizeof(float));
+}
+size_t score_ws_bytes(const idx_seqs* s) {
+  return score_rows_bytes(s) + align_up((size_t)std::max(s->num_tokens, 0) * SCORE_HIST_BINS * sizeof(uint32_t));
 }
 
 size_t attn_ws_bytes(const idx_seqs* s, int H, int top_k) {
@@ -123,11 +127,13 @@ int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int 
   sp.d_I = d_I;
   sp.scores = static_cast<float*>(ws);
   sp.score_stride = score_stride(seqs);
+  sp.hist = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + score_rows_bytes(seqs));
   if (launch_score(sp, k_dtype == IDX_E4M3, stream) != hipSuccess) return IDX_ERR_HIP;
   TopkParams tp;
   tp.sv = sp.sv;
   tp.scores = sp.scores;
   tp.score_stride = sp.score_stride;
+  tp.hist = sp.hist;
   tp.top_k = top_k;
   tp.out_idx = out_idx;
   if (launch_topk(tp, stream) != hipSuccess) return IDX_ERR_HIP;

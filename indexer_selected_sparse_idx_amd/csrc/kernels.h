@@ -50,16 +50,22 @@ struct ScoreParams {
   int d_I;
   float* scores;           // [T, score_stride]
   int64_t score_stride;
+  uint32_t* hist;          // [T, SCORE_HIST_BINS] histogram of the top key bits (zeroed by the launcher)
 };
 
 struct TopkParams {
   SeqView sv;
   const float* scores;
   int64_t score_stride;
+  const uint32_t* hist;    // [T, SCORE_HIST_BINS] from the score kernel
   int top_k;
   int32_t* out_idx;        // [T, top_k]
-  int keys_in_lds;         // set by the launcher
 };
+
+// The score kernel histograms the top SCORE_HIST_BITS bits of every score's
+// order-preserving key per row; the selection kernel starts from it.
+constexpr int SCORE_HIST_BITS = 11;
+constexpr int SCORE_HIST_BINS = 1 << SCORE_HIST_BITS;
 
 struct AttnParams {
   SeqView sv;

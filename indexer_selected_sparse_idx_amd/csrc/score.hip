@@ -13,12 +13,19 @@
 // sum.  Per-head values never leave registers; only the fp32 score of each
 // key is written (to the workspace row that the selection kernel reads).
 //
+// The kernel also histograms the top 11 bits of each score's order-preserving
+// key per row (LDS per workgroup, merged into the row's global histogram with
+// one atomic per occupied bin), so the selection kernel knows the bucket that
+// holds the K-th largest score before it reads the row.
+//
 // Keys stream from HBM straight into the MFMA B-operand registers (16 bytes
 // per lane per load).  The contraction order over d_I is free, so the dims a
 // lane loads are chosen for wide loads: for bf16 keys lane group g = l/16
 // takes dims 32*ks + 8*g .. +8 at k-step ks; for e4m3 keys one 16-byte load
 // covers two k-steps (dims 64*j + 16*g .. +16).  The query operand uses the
 // same permutation.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -41,13 +48,19 @@ __device__ __forceinline__ int kdim(int ks, int g) {
 //          all scan the workgroup's key block (shared through L1/L2).
 template <int MT, int KS, bool FP8, bool DECODE>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_wg) {
+  // decode: one histogram shared by the 4 waves (one token);
+  // prefill: one histogram per wave (one token each)
+  __shared__ uint32_t lhist[DECODE ? 1 : SCORE_WAVES][SCORE_HIST_BINS];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;
   const int c = lane & 15;
   const SeqView& sv = p.sv;
 
+  for (int i = threadIdx.x; i < (DECODE ? 1 : SCORE_WAVES) * SCORE_HIST_BINS; i += 256) (&lhist[0][0])[i] = 0;
+
   int b, tok, t, key_lo, key_hi;  // wave's keys: [key_lo, key_hi]
+  bool active = true;
   if (DECODE) {
     b = blockIdx.y;
     tok = first_token(sv, b);
@@ -61,81 +74,109 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_
     b = blockIdx.y / nqb;
     const int i = (blockIdx.y % nqb) * SCORE_WAVES + wave;
     const int ql = q_len(sv, b);
-    if (i >= ql) return;
-    tok = first_token(sv, b) + i;
+    active = i < ql;
+    tok = first_token(sv, b) + (active ? i : 0);
     t = sv.ctx_len[b] - ql + i;
     key_lo = blockIdx.x * keys_per_wg;
     key_hi = min(t, key_lo + keys_per_wg - 1);
   }
-  if (key_lo > key_hi) return;
+  active = active && key_lo <= key_hi;
+  uint32_t* my_hist = lhist[DECODE ? 0 : wave];
+  __syncthreads();
 
-  // ---- query operand (A): Q[h = 16 mt + c][kdim(ks, g) .. +8] -------------
-  bf16x8 qa[MT][KS];
-  float w[MT][4];
-  const uint16_t* qrow = p.q_idx + (int64_t)tok * p.H_I * p.d_I;
+  if (active) {
+    // ---- query operand (A): Q[h = 16 mt + c][kdim(ks, g) .. +8] -------------
+    bf16x8 qa[MT][KS];
+    float w[MT][4];
+    const uint16_t* qrow = p.q_idx + (int64_t)tok * p.H_I * p.d_I;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int h = mt * 16 + c;
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = mt * 16 + c;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (h < p.H_I) v = *(const u32x4*)(qrow + (int64_t)h * p.d_I + kdim<FP8>(ks, g));
-      qa[mt][ks] = as_bf16x8(v);
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (h < p.H_I) v = *(const u32x4*)(qrow + (int64_t)h * p.d_I + kdim<FP8>(ks, g));
+        qa[mt][ks] = as_bf16x8(v);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hr = mt * 16 + g * 4 + r;
+        w[mt][r] = hr < p.H_I ? p.head_w[(int64_t)tok * p.H_I + hr] : 0.0f;
+      }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hr = mt * 16 + g * 4 + r;
-      w[mt][r] = hr < p.H_I ? p.head_w[(int64_t)tok * p.H_I + hr] : 0.0f;
-    }
-  }
 
-  const int row_bytes = FP8 ? p.d_I : p.d_I * 2;
-  float* srow = p.scores + (int64_t)tok * p.score_stride;
+    const int row_bytes = FP8 ? p.d_I : p.d_I * 2;
+    float* srow = p.scores + (int64_t)tok * p.score_stride;
 
-  for (int s0 = key_lo; s0 <= key_hi; s0 += 16 * NT) {
-    bf16x8 kb[NT][KS];
-    float ksc[NT];
+    for (int s0 = key_lo; s0 <= key_hi; s0 += 16 * NT) {
+      bf16x8 kb[NT][KS];
+      float ksc[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int s = min(s0 + nt * 16 + c, key_hi);  // clamp: rows past key_hi are masked below
-      const int64_t row = cache_row(sv, b, s);
-      const uint8_t* krow = p.k_idx + row * row_bytes;
-      ksc[nt] = p.k_scale ? p.k_scale[row] : 1.0f;
-      if (FP8) {
+      for (int nt = 0; nt < NT; ++nt) {
+        const int s = min(s0 + nt * 16 + c, key_hi);  // clamp: rows past key_hi are masked below
+        const int64_t row = cache_row(sv, b, s);
+        const uint8_t* krow = p.k_idx + row * row_bytes;
+        ksc[nt] = p.k_scale ? p.k_scale[row] : 1.0f;
+        if (FP8) {
 #pragma unroll
-        for (int j = 0; j < KS / 2; ++j) {
-          const u32x4 raw = *(const u32x4*)(krow + j * 64 + g * 16);
-          u32x4 lo, hi;
-          u32x2 a0 = e4m3x4_to_bf16(raw[0], 1.0f), a1 = e4m3x4_to_bf16(raw[1], 1.0f);
-          u32x2 a2 = e4m3x4_to_bf16(raw[2], 1.0f), a3 = e4m3x4_to_bf16(raw[3], 1.0f);
-          lo[0] = a0[0]; lo[1] = a0[1]; lo[2] = a1[0]; lo[3] = a1[1];
-          hi[0] = a2[0]; hi[1] = a2[1]; hi[2] = a3[0]; hi[3] = a3[1];
-          kb[nt][2 * j] = as_bf16x8(lo);
-          kb[nt][2 * j + 1] = as_bf16x8(hi);
+          for (int j = 0; j < KS / 2; ++j) {
+            const u32x4 raw = *(const u32x4*)(krow + j * 64 + g * 16);
+            u32x4 lo, hi;
+            u32x2 a0 = e4m3x4_to_bf16(raw[0], 1.0f), a1 = e4m3x4_to_bf16(raw[1], 1.0f);
+            u32x2 a2 = e4m3x4_to_bf16(raw[2], 1.0f), a3 = e4m3x4_to_bf16(raw[3], 1.0f);
+            lo[0] = a0[0]; lo[1] = a0[1]; lo[2] = a1[0]; lo[3] = a1[1];
+            hi[0] = a2[0]; hi[1] = a2[1]; hi[2] = a3[0]; hi[3] = a3[1];
+            kb[nt][2 * j] = as_bf16x8(lo);
+            kb[nt][2 * j + 1] = as_bf16x8(hi);
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            kb[nt][ks] = as_bf16x8(*(const u32x4*)(krow + kdim<false>(ks, g) * 2));
         }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kb[nt][ks] = as_bf16x8(*(const u32x4*)(krow + kdim<false>(ks, g) * 2));
       }
-    }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float v = 0.0f;
+      for (int nt = 0; nt < NT; ++nt) {
+        float v = 0.0f;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma16(qa[mt][ks], kb[nt][ks], acc);
+          for (int ks = 0; ks < KS; ++ks) acc = mfma16(qa[mt][ks], kb[nt][ks], acc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v += w[mt][r] * fmaxf(acc[r] * ksc[nt], 0.0f);
+          for (int r = 0; r < 4; ++r) v += w[mt][r] * fmaxf(acc[r] * ksc[nt], 0.0f);
+        }
+        v += shfl_xor(v, 16);
+        v += shfl_xor(v, 32);
+        const int s = s0 + nt * 16 + c;
+        if (g == 0 && s <= key_hi) {
+          srow[s] = v;
+          atomicAdd(&my_hist[score_key(v) >> (32 - SCORE_HIST_BITS)], 1u);
+        }
       }
-      v += shfl_xor(v, 16);
-      v += shfl_xor(v, 32);
-      const int s = s0 + nt * 16 + c;
-      if (g == 0 && s <= key_hi) srow[s] = v;
     }
   }
+
+  // ---- merge the workgroup's histogram(s) into the row histogram(s) ---------
+  __syncthreads();
+  if (DECODE) {
+    uint32_t* gh = p.hist + (int64_t)tok * SCORE_HIST_BINS;
+    for (int i = threadIdx.x; i < SCORE_HIST_BINS; i += 256) {
+      const uint32_t v = lhist[0][i];
+      if (v) atomicAdd(&gh[i], v);
+    }
+  } else if (active) {
+    uint32_t* gh = p.hist + (int64_t)tok * SCORE_HIST_BINS;
+    for (int i = lane; i < SCORE_HIST_BINS; i += WAVE) {
+      const uint32_t v = my_hist[i];
+      if (v) atomicAdd(&gh[i], v);
+    }
+  }
+}
+
+__global__ void zero_kernel(uint32_t* p, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
+    ((u32x4*)p)[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
 template <int MT, int KS, bool FP8>
@@ -176,6 +217,12 @@ hipError_t launch_dt(const ScoreParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream) {
+  // the row histograms are accumulated with atomics: clear them first (a
+  // kernel, not a memset, so the call stays safe to capture in a graph)
+  const int64_t n4 = (int64_t)p.sv.num_tokens * SCORE_HIST_BINS / 4;
+  const int64_t zblocks = std::min<int64_t>((n4 + 255) / 256, 2048);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream, p.hist, n4);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   timer_before(0, stream);
   hipError_t e = k_fp8 ? launch_dt<true>(p, stream) : launch_dt<false>(p, stream);
   timer_after(0, stream);

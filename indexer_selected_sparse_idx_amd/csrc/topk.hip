@@ -8,18 +8,27 @@
 // of its fused indexer sketch; the tie rule is this library's reading).
 //
 // One workgroup (16 waves) per row:
-// 1. Rows of up to 32768 candidates are converted to keys once and kept in
-//    LDS; longer rows are re-read from the (L2-resident) score row.  Every
-//    pass reads 4 consecutive keys per lane with one vector access and keeps
-//    several such accesses in flight.
-// 2. Up to four 8-bit digit passes, most significant first, histogram the
+// 1. The score kernel has already histogrammed the top 11 bits of every key
+//    of the row.  A block-wide suffix scan of that histogram gives the bucket
+//    d1 holding the m-th largest key, the count above it and its size.
+// 2. One ordered streaming pass over the fp32 score row (4 keys per lane per
+//    access): keys in buckets above d1 are emitted directly; keys in d1 are
+//    appended, with their positions, to an LDS candidate list, in position
+//    order (wavefront prefix sums over per-lane counts, one barrier per 4096
+//    keys).
+// 3. The candidates (a few thousand at most for smooth score distributions)
+//    go through the radix select below; when d1 holds more than the LDS
+//    capacity (massive ties) the whole row goes through it instead, read from
+//    the score row.
+// Radix select over a key list:
+// a. Up to four 8-bit digit passes, most significant first, histogram the
 //    keys that share the digits chosen so far.  Every wave owns a private
 //    LDS histogram (merged after the pass): integer-valued scores put most
 //    keys into a few bins, and same-address atomics from different waves
 //    would serialise.  A one-wave suffix scan picks the digit whose bucket
 //    holds the m-th largest key; when that bucket is taken whole the passes
 //    stop early.
-// 3. Ordered compaction: each wave owns a contiguous segment of the row,
+// b. Ordered compaction: each wave owns a contiguous segment of the list,
 //    counts its keys above / equal to the threshold, and after one exclusive
 //    scan over the waves emits them in position order (a wavefront prefix
 //    sum over the per-lane counts), so equal keys are taken lowest position
@@ -36,8 +45,8 @@ namespace {
 
 constexpr int TOPK_THREADS = 1024;
 constexpr int TOPK_WAVES = TOPK_THREADS / WAVE;
-constexpr int LDS_KEYS = 32768;
-constexpr int UNROLL = 4;  // 4-key vector accesses in flight per lane
+constexpr int CAP = 12288;   // LDS candidate capacity (keys + positions)
+constexpr int UNROLL = 4;   // 4-key vector accesses in flight per lane
 
 // Key source: the LDS copy of the row, or the fp32 score row itself.
 template <bool IN_LDS>
@@ -73,9 +82,11 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
   return v;
 }
 
+// Select the m largest of n keys (ties: lowest index first) and write their
+// positions (pos[i], or i when pos is null) to out[0 .. m).
 template <bool IN_LDS>
-__device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out, uint32_t* hist, uint32_t* whist,
-                           uint32_t* wcnt) {
+__device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out, const int32_t* pos, uint32_t* hist,
+                           uint32_t* whist, uint32_t* wcnt) {
   __shared__ uint32_t sh_digit, sh_above, sh_whole;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -202,11 +213,11 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if ((fg >> e) & 1u) {
-        if (pg < n_gt) out[pg] = i + e;
+        if (pg < n_gt) out[pg] = pos ? pos[i + e] : i + e;
         ++pg;
       }
       if ((fe >> e) & 1u) {
-        if (pe < need) out[n_gt + pe] = i + e;
+        if (pe < need) out[n_gt + pe] = pos ? pos[i + e] : i + e;
         ++pe;
       }
     }
@@ -216,12 +227,17 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
 }
 
 __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkParams p) {
-  extern __shared__ uint32_t dyn[];
+  __shared__ __attribute__((aligned(16))) uint32_t cand_key[CAP];
+  __shared__ __attribute__((aligned(16))) int32_t cand_pos[CAP];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t whist[TOPK_WAVES * 256];
   __shared__ uint32_t wcnt[2 * TOPK_WAVES];
+  __shared__ uint32_t wtot[2][TOPK_WAVES][2];
+  __shared__ uint32_t sh_d1, sh_above1, sh_cnt1;
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const SeqView& sv = p.sv;
   const int tok = blockIdx.x;
   const int b = seq_of_token(sv, tok);
@@ -238,46 +254,100 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkParams p) {
     for (int i = tid; i < n; i += TOPK_THREADS) out[i] = i;
     return;
   }
-  if (n <= LDS_KEYS && p.keys_in_lds) {
-    // copy the row into LDS as keys, 4 per lane per access, UNROLL in flight
-    const int n4 = (n + 3) / 4 * 4;
-    const Keys<false> src{nullptr, row, n};
-    for (int i0 = 4 * tid; i0 < n4; i0 += 4 * TOPK_THREADS * UNROLL) {
-      u32x4 k[UNROLL];
+
+  // ---- 1. the bucket of the m-th largest key, from the row histogram ----------
+  {
+    const uint32_t* gh = p.hist + (int64_t)tok * SCORE_HIST_BINS;
+    const uint32_t h0 = gh[2 * tid], h1 = gh[2 * tid + 1];
+    uint32_t suf = h0 + h1;  // suffix over this wave's lanes >= lane
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int i = i0 + u * 4 * TOPK_THREADS;
-        if (i < n4) k[u] = src.get4(i);
-      }
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int i = i0 + u * 4 * TOPK_THREADS;
-        if (i < n4) *(u32x4*)(dyn + i) = k[u];
-      }
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(suf, off);
+      if (lane + off < 64) suf += o;
     }
+    if (lane == 0) wcnt[wave] = suf;
     __syncthreads();
-    select_row<true>(Keys<true>{dyn, row, n}, n, m, out, hist, whist, wcnt);
-  } else {
-    select_row<false>(Keys<false>{nullptr, row, n}, n, m, out, hist, whist, wcnt);
+    uint32_t above_waves = 0;
+    for (int w = wave + 1; w < TOPK_WAVES; ++w) above_waves += wcnt[w];
+    const uint32_t s0 = suf + above_waves;  // keys in bins >= 2 tid
+    const uint32_t s1 = s0 - h0, s2 = s1 - h1;
+    const uint32_t um = (uint32_t)m;
+    if (s1 >= um && s2 < um) { sh_d1 = 2 * tid + 1; sh_above1 = s2; sh_cnt1 = h1; }
+    else if (s0 >= um && s1 < um) { sh_d1 = 2 * tid; sh_above1 = s1; sh_cnt1 = h0; }
+    __syncthreads();
   }
+  const uint32_t d1 = sh_d1, above1 = sh_above1, cnt1 = sh_cnt1;
+  if (cnt1 > (uint32_t)CAP) {  // massive ties: select over the whole row
+    select_row<false>(Keys<false>{nullptr, row, n}, n, m, out, nullptr, hist, whist, wcnt);
+    return;
+  }
+
+  // ---- 2. ordered extraction: above d1 -> output, in d1 -> candidates ------------
+  const Keys<false> src{nullptr, row, n};
+  const int n4 = (n + 3) / 4 * 4;
+  uint32_t base_g = 0, base_c = 0;
+  int par = 0;
+  constexpr int CHUNK = 4 * TOPK_THREADS;
+  for (int s0 = 0; s0 < n4; s0 += CHUNK * UNROLL) {
+    u32x4 kk[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int i = s0 + u * CHUNK + 4 * tid;
+      kk[u] = i < n4 ? src.get4(i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int c0 = s0 + u * CHUNK;
+      if (c0 >= n4) break;  // uniform
+      const int i = c0 + 4 * tid;
+      uint32_t fg = 0, fc = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t top = kk[u][e] >> (32 - SCORE_HIST_BITS);
+        const bool valid = i + e < n;
+        fg |= (uint32_t)(valid && top > d1) << e;
+        fc |= (uint32_t)(valid && top == d1) << e;
+      }
+      const uint32_t ng = __popc(fg), nc = __popc(fc);
+      const uint32_t sg = wave_incl_scan(ng, lane), sc = wave_incl_scan(nc, lane);
+      if (lane == 63) { wtot[par][wave][0] = sg; wtot[par][wave][1] = sc; }
+      __syncthreads();
+      uint32_t og = base_g + sg - ng, oc = base_c + sc - nc, tg = 0, tc = 0;
+#pragma unroll
+      for (int w = 0; w < TOPK_WAVES; ++w) {
+        const uint32_t a = wtot[par][w][0], c = wtot[par][w][1];
+        if (w < wave) { og += a; oc += c; }
+        tg += a;
+        tc += c;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((fg >> e) & 1u) {
+          if (og < above1) out[og] = i + e;
+          ++og;
+        }
+        if ((fc >> e) & 1u) {
+          if (oc < (uint32_t)CAP) { cand_key[oc] = kk[u][e]; cand_pos[oc] = i + e; }
+          ++oc;
+        }
+      }
+      base_g += tg;
+      base_c += tc;
+      par ^= 1;
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. the remaining m - above1 positions come from the candidates -------------
+  select_row<true>(Keys<true>{cand_key, nullptr, (int)cnt1}, (int)cnt1, m - (int)above1, out + above1, cand_pos, hist,
+                   whist, wcnt);
 }
 
 }  // namespace
 
-hipError_t launch_topk(const TopkParams& p0, hipStream_t stream) {
-  TopkParams p = p0;
-  // LDS key cache only when some row can use it (dynamic LDS is sized per launch)
-  p.keys_in_lds = p.sv.max_ctx_len > p.top_k ? 1 : 0;
-  const int cap = (std::min(p.sv.max_ctx_len, LDS_KEYS) + 3) / 4 * 4;
-  const size_t dyn = p.keys_in_lds ? (size_t)cap * sizeof(uint32_t) : 0;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              LDS_KEYS * (int)sizeof(uint32_t));
-    attr_set = true;
-  }
+hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
   timer_before(1, stream);
-  hipLaunchKernelGGL(topk_kernel, dim3(p.sv.num_tokens), dim3(TOPK_THREADS), dyn, stream, p);
+  hipLaunchKernelGGL(topk_kernel, dim3(p.sv.num_tokens), dim3(TOPK_THREADS), 0, stream, p);
   hipError_t e = hipGetLastError();
   timer_after(1, stream);
   return e;

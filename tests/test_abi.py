@@ -141,8 +141,9 @@ def test_fused_workspace_check(L):
 
 def test_workspace_sizes(L):
     s = seqs(num_seqs=3, num_tokens=3, max_ctx_len=1000, seq_stride=1000)
-    # one fp32 score row per token, padded to 64 columns, rounded to 256 bytes
-    want = -(-3 * 1024 * 4 // 256) * 256
+    # one fp32 score row per token padded to 64 columns, then one 2048-bin
+    # key histogram per token, each part rounded to 256 bytes
+    want = -(-3 * 1024 * 4 // 256) * 256 + -(-3 * 2048 * 4 // 256) * 256
     assert L.idx_score_topk_workspace(ctypes.byref(s), 64, 128, 2048) == want
     assert L.sparse_mla_attn_workspace(ctypes.byref(s), 128, 2048) > 0     # decode splits
     big = seqs(num_seqs=1, num_tokens=4096, cu_q=FAKE, max_q_len=4096, max_ctx_len=8192,
