@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run this many steps with no timing or oracle (for rocprofv3)")
+    ap.add_argument("--workload", type=int, default=0,
+                    help="1..5: time another workload (all of its calls per step) and print per-kernel "
+                         "figures instead of the headline JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -126,6 +129,90 @@ def cpu_baseline(inp, call, n_tokens, min_seconds=10.0):
                           inp.wl.H, dt))
 
 
+def measure_workload(n, steps, warmup):
+    """Per-call and per-kernel times of workload n (a step = every call)."""
+    import numpy as np
+    import torch
+    import indexer_selected_sparse_idx_amd as lib
+    from workloads import config, generate
+
+    dev = torch.device("cuda:0")
+    wl = config(n)
+    inp = generate(wl, dev)
+    scale = 1.0 / math.sqrt(576.0)
+    calls = []
+    ws_bytes = 0
+    for call in inp.calls:
+        ctx = torch.from_numpy(call.ctx_len.astype(np.int32)).to(dev)
+        cu = None if call.cu_q is None else torch.from_numpy(call.cu_q.astype(np.int32)).to(dev)
+        bt_np = inp.call_block_table(call)
+        bt = None if bt_np is None else torch.from_numpy(bt_np.astype(np.int32)).to(dev)
+        s = lib.Seqs(ctx, cu, max_q_len=call.max_q_len, max_ctx_len=int(call.ctx_len.max()),
+                     num_tokens=call.num_tokens, block_table=bt, page_size=wl.page_size,
+                     seq_stride=inp.seq_stride if not wl.paged else 0)
+        s._keep = (ctx, cu, bt)
+        ws_bytes = max(ws_bytes, lib.idx_sparse_attn_workspace(s, wl.H_I, wl.d_I, wl.H, wl.top_k))
+        calls.append((call, s))
+    T_max = max(c.num_tokens for c, _ in calls)
+    out = torch.empty((T_max, wl.H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((T_max, wl.H), dtype=torch.float32, device=dev)
+    idx = torch.empty((T_max, wl.top_k), dtype=torch.int32, device=dev)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def run(call, s):
+        sl = slice(call.tok_lo, call.tok_hi)
+        fn = lib.idx_sparse_attn_decode if call.is_decode else lib.idx_sparse_attn_prefill
+        fn(s, inp.q_idx[sl], inp.k_idx, inp.head_w[sl], wl.top_k, inp.q[sl], inp.kv, scale, k_scale=inp.k_scale,
+           out=out[:call.num_tokens], lse=lse[:call.num_tokens], out_idx=idx[:call.num_tokens], ws=ws)
+
+    for _ in range(warmup):
+        for c, s in calls:
+            run(c, s)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        for c, s in calls:
+            run(c, s)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    names = {lib.IDX_KERNEL_SCORE: "score", lib.IDX_KERNEL_TOPK: "topk", lib.IDX_KERNEL_ATTN: "attn",
+             lib.IDX_KERNEL_COMBINE: "combine"}
+    per_call = []
+    tot = {v: 0.0 for v in names.values()}
+    for c, s in calls:
+        ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in names}
+        for e0, e1 in ev.values():
+            e0.record()
+            e1.record()
+        torch.cuda.synchronize()
+        for k, (e0, e1) in ev.items():
+            lib.idx_timer_arm(k, e0, e1)
+        run(c, s)
+        torch.cuda.synchronize()
+        kt = {}
+        for k, (e0, e1) in ev.items():
+            kt[names[k]] = e0.elapsed_time(e1) * 1e3 if (k != lib.IDX_KERNEL_COMBINE or e1.query()) else 0.0
+        per_call.append({"tokens": c.num_tokens, "max_ctx": int(c.ctx_len.max()), "kernels_us": kt})
+        for k in tot:
+            tot[k] += kt[k]
+    # algorithmic flops of the whole step (causal pairs for the indexer, selected rows for attention)
+    idx_flops = attn_flops = 0.0
+    for c, _ in calls:
+        qlen = [1] * len(c.ctx_len) if c.cu_q is None else list(np.diff(c.cu_q))
+        for ctx, ql in zip(c.ctx_len, qlen):
+            ts = np.arange(int(ctx) - ql, int(ctx))
+            idx_flops += 2.0 * wl.H_I * wl.d_I * float((ts + 1).sum())
+            attn_flops += 2176.0 * wl.H * float(np.minimum(wl.top_k, ts + 1).sum())
+    tokens = sum(c.num_tokens for c, _ in calls)
+    print(json.dumps({"workload": wl.name, "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+                      "kernels_us_total": tot,
+                      "indexer_tflops": idx_flops / (tot["score"] * 1e-6) / 1e12 if tot["score"] else None,
+                      "attn_tflops": attn_flops / ((tot["attn"] + tot["combine"]) * 1e-6) / 1e12,
+                      "per_call": per_call}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -154,6 +241,9 @@ def main():
         return
     lib.lib()
     dev = torch.device("cuda:0")
+    if args.workload:
+        measure_workload(args.workload, args.steps, args.warmup)
+        return
     wl = config(2)
     inp = generate(wl, dev)
     call = inp.calls[0]
