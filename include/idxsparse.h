@@ -202,7 +202,8 @@ typedef enum {
   IDX_KERNEL_SCORE = 0,     /* indexer score                                  */
   IDX_KERNEL_TOPK = 1,      /* per-row radix select                           */
   IDX_KERNEL_ATTN = 2,      /* sparse latent attention                        */
-  IDX_KERNEL_COMBINE = 3,   /* split merge of the attention partials          */
+  IDX_KERNEL_COMBINE = 3,   /* split merge of the attention partials (only
+                               launched when a call splits the index lists) */
   IDX_KERNEL_COUNT = 4
 } idx_kernel;
 int idx_timer_arm(int kernel, void *start_event, void *stop_event);

@@ -35,9 +35,14 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
+# per-source extra flags: the attention kernels keep the O^T accumulator in
+# AGPRs through inline asm and want every builtin MFMA in VGPR form
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + CFLAGS
+    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + CFLAGS + EXTRA.get(src, [])
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s\n%s" % (" ".join(cmd), res.stdout, res.stderr))

@@ -9,24 +9,31 @@
 // head, MLA: section 1 of Day 0 Inference Adaptation and Performance
 // Optimization for New Models).
 //
-// Work item: (token, group of 16*NW heads, split of the index list).  The
-// cache row of every index of the split is resolved once (block table
-// included) into LDS.  Selected latent rows are then gathered 32 per tile
-// into LDS, and each wave owns 16 heads:
-//   S^T[32 keys x 16 heads] = C_tile . Q^T   (MFMA 16x16x32, keys on M)
-//   online softmax in fp32 registers (each lane holds 8 keys of one head)
-//   O^T[512 x 16 heads]   += V^T . P^T       (MFMA, dv on M)
-// The fp32 S^T tile is already laid out as the B operand of the second
-// product once the key order inside the contraction is permuted to match;
-// the V^T operand comes from the key-major LDS tile through the gfx950
-// transposing LDS read (ds_read_b64_tr_b16), so V is stored only once.
+// Work item: (token, split of the index list), every head of the token.  The
+// workgroup has one wave per 32 heads.  The valid entries of the split are
+// resolved to cache rows (block table included) and compacted into LDS, so
+// entries that select nothing (-1, or past the context) cost no tile.  The
+// selected latent rows are gathered 32 per tile into LDS, shared by all the
+// waves, and each wave runs with its 32 heads on the MFMA N dimension
+// (v_mfma_f32_32x32x16_bf16):
+//   S^T[32 keys x 32 heads] = C_tile . Q^T   (keys on M, 36 k-steps over 576)
+//   online softmax in fp32 registers (a lane holds 16 keys of one head; the
+//   other 16 sit in lane ^ 32)
+//   O^T[512 x 32 heads]   += V^T . P^T       (dv on M, 16 tiles of 32)
+// The S^T accumulator is already the B operand of the second product once
+// the key order inside its contraction is permuted to match (k-step kk takes
+// accumulator registers 8 kk .. 8 kk + 7); the V^T operand is read from the
+// key-major tile with the gfx950 transposing LDS read (ds_read_b64_tr_b16),
+// so each row is stored once.  Q^T stays in registers for the whole split and
+// O^T in the accumulation registers.
 //
-// bf16 rows go from HBM straight into LDS (global_load_lds_dwordx4, one
-// wave instruction per 1 KiB latent row, chunks XOR-swizzled by row so the
-// MFMA operand reads are bank-conflict free) through an NBUF-deep ring, so
-// NBUF-1 tiles are in flight while one is computed.  FP8 rows (656 bytes)
-// are staged through registers and dequantised to bf16 on their way into
-// LDS.  Splits (for decode occupancy) are merged by combine_kernel.
+// bf16 rows go from HBM straight into LDS (global_load_lds_dwordx4, one wave
+// instruction per 1 KiB latent row) through an NBUF-deep ring, and the loop is
+// software-pipelined: after one barrier per tile, the MFMAs of S for tile k+1
+// are issued together with the softmax of tile k, then P.V of tile k.  FP8
+// rows (656 bytes) go into a raw LDS ring the same way and are dequantised to
+// the bf16 tile layout by the workgroup.  Splits (decode occupancy) are
+// merged by combine_kernel.
 #include <math.h>
 
 #include <algorithm>
@@ -39,15 +46,51 @@ namespace idxs {
 namespace {
 
 constexpr int TILE = ATTN_TILE;                 // selected rows per tile
-constexpr int LAT_STRIDE = 1024 + 32;           // 512 bf16 per row, padded by two 16-byte chunks
+constexpr int HPW = 32;                         // heads per wave
+constexpr int LAT_STRIDE = 1024 + 64;           // 512 bf16 per row, padded by four 16-byte chunks
 constexpr int LAT_TILE_BYTES = TILE * LAT_STRIDE;
 constexpr int ROPE_TILE_BYTES = TILE * 128;     // 64 bf16 per row
 constexpr int BUF_BYTES = LAT_TILE_BYTES + ROPE_TILE_BYTES;
-constexpr float RESCALE_SLACK = 8.0f;           // log2 growth of the running max tolerated before rescaling
-constexpr int EAGER_TILES = 1;                  // tiles with exact running-max normalisation
+constexpr int RAW_TILE_BYTES = TILE * FP8_ROW_BYTES;
+constexpr int RAW_CHUNKS = RAW_TILE_BYTES / 16;  // 16-byte chunks of a raw FP8 tile
+constexpr int KSTEPS = ROW / 16;                // 36 k-steps of the S product
+constexpr int DV_TILES = LATENT / 32;           // 16 dv tiles of the P.V product
+constexpr float MAX_GROWTH = 64.0f;             // log2 growth of the max over the softmax reference tolerated
 constexpr float LN2 = 0.69314718055994530942f;
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
+
+// D += A * B on a 32x32 fp32 tile, K = 16 (bf16 operands).
+//   a: lane l holds A[l % 32][8 * (l / 32) + 0..7]
+//   b: lane l holds B[8 * (l / 32) + 0..7][l % 32]
+//   d: register 4 i + j of lane l holds D[8 i + 4 * (l / 32) + j][l % 32]
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// O^T accumulation: the same MFMA written as inline asm with the accumulator
+// tied to AGPRs ("+a"), so the 256 registers of O^T stay in the accumulation
+// file while the builtin MFMAs (this file is built with VGPR-form MFMAs) keep
+// S^T in VGPRs.  The compiler does not see these as MFMAs, so the hazards it
+// would otherwise pad are handled here: NOP_B adds the wait state needed when
+// b was just written by a VALU instruction; back-to-back MFMAs accumulating
+// into the same registers need none; o_fence() must separate the last of them
+// from any other access to the accumulators.
+template <bool NOP_B>
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+  if (NOP_B)
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// max / sum of v over lanes l and l ^ 32 (both lanes get the result).
+// (v_permlane32_swap would do the exchange without the LDS crossbar, but the
+// compiler folds the builtin's two results into one when both inputs are
+// the same value.)
+__device__ __forceinline__ float pair_max(float v) { return fmaxf(v, shfl_xor(v, 32)); }
+__device__ __forceinline__ float pair_sum(float v) { return v + shfl_xor(v, 32); }
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding; the
 // 6-bit vmcnt saturates at 63, and waiting for fewer is always safe).
@@ -58,7 +101,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // 16 bytes per lane from global memory straight into LDS at lds_addr + 16 *
-// lane (lds_addr is wave-uniform).  Written as inline asm so that the
+// lane (lds_addr is wave-uniform).  dma16_s takes a wave-uniform base address
+// (SGPRs) and a 32-bit per-lane byte offset.  Written as inline asm so that the
 // compiler does not turn later LDS reads of other ring slots into waits for
 // every outstanding gather: completion is tracked with wait_vmcnt().
 __device__ __forceinline__ void dma16(const uint8_t* gptr, uint32_t lds_addr) {
@@ -67,446 +111,542 @@ __device__ __forceinline__ void dma16(const uint8_t* gptr, uint32_t lds_addr) {
                : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory", "m0");
 }
+__device__ __forceinline__ void dma16_s(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory", "m0");
+}
 
-// LDS addresses of 16-byte chunk `ch` of tile row r.  Latent rows are padded
-// to 66 chunks (rows 4 apart then share a bank window) and bit 0 of the
-// chunk index is flipped on rows with bit 2 set.  Then 8 consecutive rows at
-// one chunk (a 128-bit read of 8 lanes) cover all 32 banks, the 4 rows x 2
-// chunks of a transposing read of 16 lanes cover all 32 banks, and every
-// per-lane address stays affine in the chunk index (immediate offsets),
-// because the flip only touches the lane-dependent bit.  The rope part is
-// XOR-swizzled.
-__device__ __forceinline__ int lat_flip(int r) { return (r >> 2) & 1; }
-__device__ __forceinline__ int lat_off(int r, int ch) { return r * LAT_STRIDE + ((ch ^ lat_flip(r)) << 4); }
-__device__ __forceinline__ int rope_off(int r, int ch) { return LAT_TILE_BYTES + r * 128 + ((ch ^ (r & 7)) << 4); }
+// LDS addresses of 16-byte chunk `ch` of tile row r.  The LDS has 64 banks
+// of 4 bytes; a 128-bit read serves 16 lanes per cycle, a 64-bit transposing
+// read 32.  Latent rows are padded to 68 chunks, so row r starts 4 r chunks
+// into the 16-chunk bank window, and the two low bits of the chunk index are
+// XOR-ed with bits 2-3 of the row.  Then
+//   - 16 consecutive rows at one chunk (the S operand read) and
+//   - 4 rows (4 m .. 4 m + 3) x 4 consecutive aligned chunks (the V^T
+//     operand read of 32 lanes)
+// each cover all 64 banks, and every per-lane address stays affine in the
+// chunk index above bit 1 and in the row above bit 3 (immediate offsets).
+// Rope rows (8 chunks) are XOR-swizzled with bits 1-3 of the row, so 16
+// consecutive rows at one chunk cover the banks too.
+__device__ __forceinline__ int lat_swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int lat_off(int r, int ch) { return r * LAT_STRIDE + ((ch ^ lat_swz(r)) << 4); }
+__device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int rope_off(int r, int ch) { return LAT_TILE_BYTES + r * 128 + ((ch ^ rope_swz(r)) << 4); }
 
-// Per-wave state of the online softmax and the O^T accumulator: the wave
-// holds NQ of the 18 k-steps of its Q^T operand (lane: Q[h][32 ks + 8 g .. +8])
-// and NT of the 32 dv tiles of O^T (lane: O^T[dv = 16 nt + 4 g + r][head c]).
-template <int NQ, int NT>
-struct WaveAccT {
-  bf16x8 qb[NQ];
-  f32x4 o[NT];
-  float m_run, l_run;
-  int tiles;       // tiles processed so far
+// Per-wave state: Q^T operand (k-step ks: lane holds Q[head][16 ks + 8 h .. +8],
+// h = lane / 32), the O^T accumulator (register 4 i + j of tile nt holds
+// O^T[32 nt + 8 i + 4 h + j][head]) and the softmax state of the lane's head.
+//
+// The softmax runs against a fixed reference m_ref per head (the maximum of
+// the first tile, base 2), so O^T never needs rescaling: p = 2^(x - m_ref)
+// and O = sum p v / sum p is exact for any reference as long as nothing
+// overflows.  m_max tracks the true maximum; if it outgrows the reference by
+// more than MAX_GROWTH (p could then overflow), the workgroup recomputes the
+// split with m_ref = m_max.
+struct WaveAcc {
+  bf16x8 qb[KSTEPS];
+  f32x16 o[DV_TILES];
+  float m_ref, m_max, l_run;
 };
-typedef WaveAccT<18, 32> WaveAcc;
 
-template <int NQ, int NT>
-__device__ __forceinline__ void load_q(WaveAccT<NQ, NT>& a, const AttnParams& p, int tok, int h, bool head_ok, int g,
-                                       int ks0 = 0) {
-  const uint16_t* qrow = p.q + ((int64_t)tok * p.H + (head_ok ? h : 0)) * ROW;
+__device__ __forceinline__ void load_q(WaveAcc& a, const AttnParams& p, int tok, int head, bool head_ok, int h) {
+  const uint16_t* qrow = p.q + ((int64_t)tok * p.H + (head_ok ? head : 0)) * ROW + h * 8;
 #pragma unroll
-  for (int kk = 0; kk < NQ; ++kk) {
+  for (int ks = 0; ks < KSTEPS; ++ks) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (head_ok) v = *(const u32x4*)(qrow + (ks0 + kk) * 32 + g * 8);
-    a.qb[kk] = as_bf16x8(v);
+    if (head_ok) v = *(const u32x4*)(qrow + ks * 16);
+    a.qb[ks] = as_bf16x8(v);
   }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) a.o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  a.m_run = -INFINITY;
-  a.l_run = 0.0f;
-  a.tiles = 0;
 }
 
-// Per-lane addresses inside a tile buffer.
-struct TileAddr {
-  int s_lat[2];   // S-phase latent operand of key tiles mt = 0, 1 (chunk 4 ks + g added as offset)
-  int s_rope[2][2];
-  int v_lo, v_hi; // V^T operand rows 4 g + c / 4 and 16 + 4 g + c / 4
-  __device__ __forceinline__ void init(int g, int c) {
+// Start (or restart) the accumulation; m_ref < -FLT_MAX means "take the
+// reference from the first tile".
+// Wait states after the last accumulating MFMA before the accumulators are
+// read or overwritten (the 32x32x16 result latency, with margin).
+__device__ __forceinline__ void o_fence(WaveAcc& a) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7"
+               : "+a"(a.o[0]), "+a"(a.o[1]), "+a"(a.o[2]), "+a"(a.o[3]), "+a"(a.o[4]), "+a"(a.o[5]),
+                 "+a"(a.o[6]), "+a"(a.o[7]), "+a"(a.o[8]), "+a"(a.o[9]), "+a"(a.o[10]), "+a"(a.o[11]),
+                 "+a"(a.o[12]), "+a"(a.o[13]), "+a"(a.o[14]), "+a"(a.o[15]));
+}
+
+__device__ __forceinline__ void reset_acc(WaveAcc& a, float m_ref) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int r = mt * 16 + c;
-      s_lat[mt] = lat_off(r, g);
-      s_rope[mt][0] = rope_off(r, g);
-      s_rope[mt][1] = rope_off(r, 4 + g);
-    }
-    const int ra = 4 * g + (c >> 2);
-    const int half = (c & 1) * 8;
-    v_lo = lat_off(ra, (c & 3) >> 1) + half;
-    v_hi = lat_off(ra + 16, (c & 3) >> 1) + half;
-  }
-  __device__ __forceinline__ int s_off(int ks, int mt) const {
-    return ks < 16 ? s_lat[mt] + ks * 64 : s_rope[mt][ks - 16];
+  for (int nt = 0; nt < DV_TILES; ++nt) a.o[nt] = f32x16{};
+  a.m_ref = m_ref;
+  a.m_max = -INFINITY;
+  a.l_run = 0.0f;
+}
+
+// Per-lane LDS byte offsets inside a tile buffer.
+struct TileAddr {
+  int s_lat[2];   // S operand, latent k-step ks: s_lat[ks & 1] + 64 (ks >> 1)
+  int s_rope[4];  // S operand, rope k-steps 32 .. 35
+  int v[2];       // V^T operand, read r of k-step kk, dv tile nt: v[r] + 16 kk LAT_STRIDE + 64 nt
+  __device__ __forceinline__ void init(int lane) {
+    const int h = lane >> 5, col = lane & 31;
+    // k-step ks reads chunk 2 ks + h of row col; the swizzle only touches
+    // the two low chunk bits (h and the parity of ks)
+    s_lat[0] = lat_off(col, h);
+    s_lat[1] = lat_off(col, 2 + h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_rope[j] = rope_off(col, 2 * j + h);
+    // transposing read: 16-lane group G = lane / 16 reads keys 16 kk + 8 r +
+    // 4 h + 0..3 (h = G / 2) at dv 32 nt + 16 (G % 2) + 0..15; lane k of the
+    // group addresses key + k / 4, dv + 4 (k % 4)
+    const int G = lane >> 4, k = lane & 15;
+    const int hh = G >> 1, dvhalf = G & 1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) v[r] = lat_off(8 * r + 4 * hh + (k >> 2), 2 * dvhalf + ((k & 3) >> 1)) + 8 * (k & 1);
   }
 };
 
-__device__ __forceinline__ bf16x8 s_operand(const uint8_t* buf, const TileAddr& ad, int ks, int mt) {
-  return *(const bf16x8*)(buf + ad.s_off(ks, mt));
+__device__ __forceinline__ bf16x8 s_operand(const uint8_t* buf, const TileAddr& ad, int ks) {
+  return *(const bf16x8*)(buf + (ks < 32 ? ad.s_lat[ks & 1] + (ks >> 1) * 64 : ad.s_rope[ks - 32]));
 }
 
-__device__ __forceinline__ bf16x8 v_operand(const uint8_t* buf, const TileAddr& ad, int nt) {
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + ad.v_lo + nt * 32));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + ad.v_hi + nt * 32));
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* buf, const TileAddr& ad, int nt, int kk) {
+  const int off = kk * 16 * LAT_STRIDE + nt * 64;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + ad.v[0] + off));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + ad.v[1] + off));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Online softmax of one S^T tile (base 2).  valid8 bit j says whether key
-// 16 (j / 4) + 4 g + j % 4 of the tile is a real selected row.  Returns the
-// P^T operand of the tile and rescales the O^T accumulator when the running
-// max moves.
-struct PSplit {
-  bf16x8 hi, lo;
-};
+// S^T[32 keys x 32 heads] of one tile.  The operand of k-step ks + SPRE is
+// read from LDS while the MFMA of k-step ks runs; the scheduling fences keep
+// that order (left alone, the scheduler serialises read -> wait -> MFMA).
+constexpr int SPRE = 4;
 
-template <int NQ, int NT>
-__device__ __forceinline__ PSplit softmax_tile(WaveAccT<NQ, NT>& a, const f32x4 (&sacc)[2], uint32_t valid8,
-                                               float scale_log2) {
-  float x[8];
+__device__ __forceinline__ f32x16 s_phase(const WaveAcc& a, const uint8_t* buf, const TileAddr& ad) {
+  f32x16 acc = {};
+  bf16x8 op[SPRE];
+#pragma unroll
+  for (int j = 0; j < SPRE; ++j) op[j] = s_operand(buf, ad, j);
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    acc = mfma32(op[ks % SPRE], a.qb[ks], acc);
+    if (ks + SPRE < KSTEPS) op[ks % SPRE] = s_operand(buf, ad, ks + SPRE);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return acc;
+}
+
+// Softmax numerators of one S^T tile (base 2) against the reference; the
+// first nv keys of the tile are valid.
+__device__ __forceinline__ void softmax_tile(WaveAcc& a, const f32x16& s, int nv, float scale_log2, int h,
+                                             float (&p)[16]) {
   float tmax = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    x[j] = ((valid8 >> j) & 1u) ? sacc[j >> 2][j & 3] * scale_log2 : -INFINITY;
-    tmax = fmaxf(tmax, x[j]);
+  for (int j = 0; j < 16; ++j) {
+    const int key = 8 * (j >> 2) + 4 * h + (j & 3);
+    p[j] = key < nv ? s[j] * scale_log2 : -INFINITY;
+    tmax = fmaxf(tmax, p[j]);
   }
-  tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-  // Lazy rescaling: after the first EAGER_TILES tiles keep the running max
-  // unless the tile exceeds it by more than RESCALE_SLACK (p values then
-  // stay below 2^RESCALE_SLACK; with P split into two bf16 parts their
-  // rounding does not depend on the reference).
-  const bool first = a.m_run == -INFINITY;
-  const float slack = a.tiles < EAGER_TILES ? 0.0f : RESCALE_SLACK;
-  a.tiles++;
-  const bool grow = tmax > a.m_run + slack;
-  const float m_new = grow ? tmax : a.m_run;
-  const float alpha = (grow && !first) ? exp2f(a.m_run - m_new) : 1.0f;
-  float pv[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) pv[j] = m_new == -INFINITY ? 0.0f : exp2f(x[j] - m_new);
+  tmax = pair_max(tmax);
+  if (a.m_ref == -INFINITY) a.m_ref = tmax == -INFINITY ? 0.0f : tmax;
+  a.m_max = fmaxf(a.m_max, tmax);
   float psum = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) psum += pv[j];
-  a.l_run = a.l_run * alpha + psum;
-  a.m_run = m_new;
-  if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) a.o[nt] *= alpha;
+  for (int j = 0; j < 16; ++j) {
+    p[j] = __builtin_amdgcn_exp2f(p[j] - a.m_ref);
+    psum += p[j];
   }
-  // P = P_hi + P_lo, both bf16: the PV product runs twice on the same V^T
-  // operand, so P carries ~16 mantissa bits instead of 8.
-  u32x4 hi, lo;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const __bf16 h0 = (__bf16)pv[2 * j], h1 = (__bf16)pv[2 * j + 1];
-    hi[j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    lo[j] = pack_bf16x2(pv[2 * j] - (float)h0, pv[2 * j + 1] - (float)h1);
-  }
-  PSplit r;
-  r.hi = as_bf16x8(hi);
-  r.lo = as_bf16x8(lo);
-  return r;
+  a.l_run += psum;
 }
 
-// S^T[32 keys x 16 heads] = C_tile . Q^T over k-steps [ks0, ks0 + NQ).  The
-// operands of SB k-steps are read from LDS one batch ahead of the MFMAs
-// that use them, and even / odd k-steps accumulate into separate chains, so
-// neither LDS latency nor the MFMA dependency latency is exposed per step.
-template <int NQ, int NT>
-__device__ __forceinline__ void s_phase(const WaveAccT<NQ, NT>& a, const uint8_t* buf, const TileAddr& ad,
-                                        f32x4 (&sacc)[2], int ks0 = 0) {
-  constexpr int SB = NQ % 6 == 0 ? 6 : (NQ % 3 == 0 ? 3 : 1);
-  constexpr int NB = NQ / SB;
-  f32x4 acc[2][2];
+// true when some head of the workgroup outgrew its reference.  `flags` is
+// one int per wave in LDS that no wave reads or writes at this point.
+template <int NW>
+__device__ __forceinline__ bool needs_redo(const WaveAcc& a, int* flags, int wave, int lane) {
+  const bool mine = __builtin_amdgcn_ballot_w64(a.m_max > a.m_ref + MAX_GROWTH) != 0;
+  __syncthreads();
+  if (lane == 0) flags[wave] = mine ? 1 : 0;
+  __syncthreads();
+  int any = 0;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  bf16x8 op[2][SB][2];
+  for (int j = 0; j < NW; ++j) any |= flags[j];
+  return any != 0;
+}
+
+// S of the next tile with the softmax of the current one interleaved.
+__device__ __forceinline__ f32x16 s_phase_softmax(WaveAcc& a, const uint8_t* buf, const TileAddr& ad,
+                                                  const f32x16& s_cur, int nv, float scale_log2, int h,
+                                                  float (&p)[16]) {
+  const f32x16 s_next = s_phase(a, buf, ad);
+  softmax_tile(a, s_cur, nv, scale_log2, h, p);
+  return s_next;
+}
+
+// O^T += V^T . P^T over the 16 dv tiles.  With SPLITP, P = P_hi + P_lo, both
+// bf16: the product runs twice on the same V^T operand, so P carries ~16
+// mantissa bits instead of 8.
+// P^T operand of a tile (k-step kk takes p values 8 kk .. 8 kk + 7); with
+// SPLITP, P = P_hi + P_lo, both bf16: the product then runs twice on the same
+// V^T operand, so P carries ~16 mantissa bits instead of 8.
+struct POp {
+  bf16x8 hi[2], lo[2];
+};
+
+template <bool SPLITP>
+__device__ __forceinline__ POp pack_p(const float (&pv)[16]) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  POp op;
 #pragma unroll
-  for (int kk = 0; kk < SB; ++kk)
+  for (int kk = 0; kk < 2; ++kk) {
+    u32x4 hi, lo;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) op[0][kk][mt] = s_operand(buf, ad, ks0 + kk, mt);
-#pragma unroll
-  for (int bi = 0; bi < NB; ++bi) {
-    if (bi + 1 < NB) {
-#pragma unroll
-      for (int kk = 0; kk < SB; ++kk)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) op[(bi + 1) & 1][kk][mt] = s_operand(buf, ad, ks0 + (bi + 1) * SB + kk, mt);
+    for (int j = 0; j < 4; ++j) {
+      const float p0 = pv[8 * kk + 2 * j], p1 = pv[8 * kk + 2 * j + 1];
+      const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+      hi[j] = hw;
+      if (SPLITP) {
+        const float h0 = __builtin_bit_cast(float, hw << 16), h1 = __builtin_bit_cast(float, hw & 0xffff0000u);
+        lo[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0 - h0, p1 - h1}, bf16x2));
+      } else {
+        lo[j] = 0u;
+      }
     }
-#pragma unroll
-    for (int kk = 0; kk < SB; ++kk)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        acc[mt][kk & 1] = mfma16(op[bi & 1][kk][mt], a.qb[bi * SB + kk], acc[mt][kk & 1]);
+    op.hi[kk] = as_bf16x8(hi);
+    op.lo[kk] = as_bf16x8(lo);
   }
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) sacc[mt] = acc[mt][0] + acc[mt][1];
+  return op;
 }
 
-// O^T += V^T . P^T over dv tiles [nt0, nt0 + NT); the k-slot j of lane group
-// g is key 16 (j / 4) + 4 g + j % 4 (the S^T register layout), which the
-// V^T operand rows follow.  Operands of VB tiles are read one batch ahead.
-template <int NQ, int NT>
-__device__ __forceinline__ void v_phase(WaveAccT<NQ, NT>& a, const uint8_t* buf, const TileAddr& ad, PSplit pb,
-                                        int nt0 = 0) {
-  constexpr int VB = 4;
-  constexpr int NB = NT / VB;
-  bf16x8 op[2][VB];
+// O^T += V^T . P^T over dv tiles [NT0, NT1).  The operands of dv tile nt + 1
+// are read while the MFMAs of tile nt run.  FIRST: P was just written by VALU
+// instructions (the first MFMAs then wait one state).
+template <bool SPLITP, int NT0, int NT1, bool FIRST>
+__device__ __forceinline__ void v_phase(WaveAcc& a, const uint8_t* buf, const TileAddr& ad, const POp& op) {
+  bf16x8 v0 = v_operand(buf, ad, NT0, 0), v1 = v_operand(buf, ad, NT0, 1);
 #pragma unroll
-  for (int j = 0; j < VB; ++j) op[0][j] = v_operand(buf, ad, nt0 + j);
-#pragma unroll
-  for (int bi = 0; bi < NB; ++bi) {
-    if (bi + 1 < NB) {
-#pragma unroll
-      for (int j = 0; j < VB; ++j) op[(bi + 1) & 1][j] = v_operand(buf, ad, nt0 + (bi + 1) * VB + j);
+  for (int nt = NT0; nt < NT1; ++nt) {
+    bf16x8 n0 = v0, n1 = v1;
+    if (nt + 1 < NT1) {
+      n0 = v_operand(buf, ad, nt + 1, 0);
+      n1 = v_operand(buf, ad, nt + 1, 1);
     }
-#pragma unroll
-    for (int j = 0; j < VB; ++j) a.o[bi * VB + j] = mfma16(op[bi & 1][j], pb.hi, a.o[bi * VB + j]);
-#pragma unroll
-    for (int j = 0; j < VB; ++j) a.o[bi * VB + j] = mfma16(op[bi & 1][j], pb.lo, a.o[bi * VB + j]);
+    if (FIRST && nt == NT0) {
+      mfma32_acc<true>(a.o[nt], v0, op.hi[0]);
+      mfma32_acc<true>(a.o[nt], v1, op.hi[1]);
+      if (SPLITP) {
+        mfma32_acc<true>(a.o[nt], v0, op.lo[0]);
+        mfma32_acc<true>(a.o[nt], v1, op.lo[1]);
+      }
+    } else {
+      mfma32_acc<false>(a.o[nt], v0, op.hi[0]);
+      mfma32_acc<false>(a.o[nt], v1, op.hi[1]);
+      if (SPLITP) {
+        mfma32_acc<false>(a.o[nt], v0, op.lo[0]);
+        mfma32_acc<false>(a.o[nt], v1, op.lo[1]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    v0 = n0;
+    v1 = n1;
   }
 }
 
-// One tile, start to finish (used by the FP8 path).
-__device__ __forceinline__ void compute_tile(WaveAcc& a, const uint8_t* buf, const TileAddr& ad, uint32_t valid8,
-                                             float scale_log2) {
-  f32x4 sacc[2];
-  s_phase(a, buf, ad, sacc);
-  const PSplit pb = softmax_tile(a, sacc, valid8, scale_log2);
-  v_phase(a, buf, ad, pb);
-}
-
-// Normalise and store the wave's O^T tiles (dv tiles nt0 .. nt0 + NT) and, if
-// write_lse, its lse.
-template <int NQ, int NT>
-__device__ __forceinline__ void write_result(const WaveAccT<NQ, NT>& a, const AttnParams& p, int tok, int split,
-                                             int h, bool head_ok, int g, int nt0 = 0, bool write_lse = true) {
-  float l_tot = a.l_run;
-  l_tot += shfl_xor(l_tot, 16);
-  l_tot += shfl_xor(l_tot, 32);
+// Normalise and store the wave's O^T (and lse) for its 32 heads.
+__device__ __forceinline__ void write_result(const WaveAcc& a, const AttnParams& p, int tok, int split, int head,
+                                             bool head_ok, int h) {
+  const float l_tot = pair_sum(a.l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float lse_v = l_tot > 0.0f ? (a.m_run + log2f(l_tot)) * LN2 : -INFINITY;
+  const float lse_v = l_tot > 0.0f ? (a.m_ref + __builtin_amdgcn_logf(l_tot)) * LN2 : -INFINITY;
   if (!head_ok) return;
   float* orow;
   float* lrow;
   if (p.num_splits == 1) {
-    orow = p.out + ((int64_t)tok * p.H + h) * LATENT;
-    lrow = p.lse ? p.lse + (int64_t)tok * p.H + h : nullptr;
+    orow = p.out + ((int64_t)tok * p.H + head) * LATENT;
+    lrow = p.lse ? p.lse + (int64_t)tok * p.H + head : nullptr;
   } else {
-    const int64_t pi = ((int64_t)tok * p.num_splits + split) * p.H + h;
+    const int64_t pi = ((int64_t)tok * p.num_splits + split) * p.H + head;
     orow = p.part_o + pi * LATENT;
     lrow = p.part_lse + pi;
   }
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) *(f32x4*)(orow + (nt0 + nt) * 16 + g * 4) = a.o[nt] * inv;
-  if (write_lse && g == 0 && lrow) *lrow = lse_v;
+  for (int nt = 0; nt < DV_TILES; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = {a.o[nt][4 * i], a.o[nt][4 * i + 1], a.o[nt][4 * i + 2], a.o[nt][4 * i + 3]};
+      *(f32x4*)(orow + nt * 32 + i * 8 + h * 4) = v * inv;
+    }
+  if (h == 0 && lrow) *lrow = lse_v;
 }
 
-// Work mapping shared by both kernels.  Workgroups are dispatched
-// round-robin over the 8 XCDs, so the head groups of one (token, split) pair
-// are placed 8 blocks apart and share an XCD (and its L2) for the gathered
-// rows.
+// Work item of a workgroup.  Workgroups are dispatched round-robin over the
+// 8 XCDs; the splits of one token are placed 8 blocks apart so that they
+// share an XCD (the token's queries are then read into one L2).
 struct Work {
-  int tok, split, hg, b, ctx, e_lo, e_hi, ntiles;
+  int tok, split, b, ctx, e_lo, e_hi;
 };
 
-template <int NW>
 __device__ __forceinline__ bool map_work(const AttnParams& p, Work& w) {
-  const int nhg = cdiv(p.H, 16 * NW);
+  const int S = p.num_splits;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, slot = bid >> 3;
-  w.hg = slot % nhg;
-  const int pair = (slot / nhg) * 8 + xcd;
-  if (pair >= p.sv.num_tokens * p.num_splits) return false;
-  w.tok = pair / p.num_splits;
-  w.split = pair % p.num_splits;
+  w.tok = xcd + 8 * (slot / S);
+  w.split = slot % S;
+  if (w.tok >= p.sv.num_tokens) return false;
   w.b = seq_of_token(p.sv, w.tok);
   w.ctx = p.sv.ctx_len[w.b];
   w.e_lo = w.split * p.split_len;
   w.e_hi = min(p.top_k, w.e_lo + p.split_len);
-  w.ntiles = w.e_hi > w.e_lo ? cdiv(w.e_hi - w.e_lo, TILE) : 0;
   return true;
 }
 
-// Resolve the cache row of every index entry of the split into LDS:
-// rows[i] = row of entry e_lo + i, or ~row0 (negative) when the entry is not
-// a valid position (the dummy row0 keeps every gather in bounds).
-template <int THREADS>
-__device__ __forceinline__ void resolve_rows(const AttnParams& p, const Work& w, int* rows, int tid) {
-  const int32_t* idx_row = p.idx + (int64_t)w.tok * p.top_k;
-  const int row0 = (int)cache_row(p.sv, w.b, 0);
-  const int n = w.ntiles * TILE;
-  for (int i = tid; i < n; i += THREADS) {
-    const int e = w.e_lo + i;
-    const int s = e < w.e_hi ? idx_row[e] : -1;
-    rows[i] = (s >= 0 && s < w.ctx) ? (int)cache_row(p.sv, w.b, s) : ~row0;
-  }
-}
-
-__device__ __forceinline__ uint32_t tile_valid8(const int* rows, int g) {
-  uint32_t v = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v |= (rows[(j >> 2) * 16 + g * 4 + (j & 3)] >= 0 ? 1u : 0u) << j;
-  return v;
-}
-
-// ---------------------------------------------------------------------------
-// bf16 rows: direct HBM -> LDS gathers through an NBUF-deep ring.
-// ---------------------------------------------------------------------------
-template <int NW, int NBUF, int MAXE>
-__global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF_BYTES];
-  __shared__ int rows_sh[MAXE];
+// Resolve the valid index entries of the split (0 <= s < ctx) to cache rows,
+// compacted in entry order into rows[0 .. n); the tail of the last tile
+// repeats rows[0] so every gather stays in bounds.  Returns n.  All index
+// loads of the split are issued before the first is used (one memory
+// latency, not one per round).
+template <int NW, int MAXE>
+__device__ __forceinline__ int resolve_rows(const AttnParams& p, const Work& w, int* rows, int* wsum, int tid) {
   constexpr int THREADS = NW * WAVE;
-  constexpr int LAT_PER_WAVE = TILE / NW;        // latent rows issued per wave per tile
-  constexpr int ROPE_INSTR = ROPE_TILE_BYTES / 1024;
-  constexpr int LOADS_PER_WAVE = LAT_PER_WAVE + (ROPE_INSTR + NW - 1) / NW;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g = lane >> 4;
-  const int c = lane & 15;
-  Work w;
-  if (!map_work<NW>(p, w)) return;
-  const int h = w.hg * 16 * NW + wave * 16 + c;
-  const bool head_ok = h < p.H;
-
-  resolve_rows<THREADS>(p, w, rows_sh, tid);
-  WaveAcc a;
-  load_q(a, p, w.tok, h, head_ok, g);
-  wait_vmcnt<0>();  // Q and index loads done: no compiler-inserted waits in the loop
-  __syncthreads();
-
-  // issue the gathers of tile k into ring slot k % NBUF
-  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
-  auto issue = [&](int k) {
-    const uint32_t buf = smem_base + (k % NBUF) * BUF_BYTES;
-    const int* rows = rows_sh + k * TILE;
+  constexpr int ROUNDS = (MAXE + THREADS - 1) / THREADS;
+  const int32_t* idx_row = p.idx + (int64_t)w.tok * p.top_k;
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int sv[ROUNDS];
 #pragma unroll
-    for (int j = 0; j < LAT_PER_WAVE; ++j) {
-      const int r = wave * LAT_PER_WAVE + j;
-      int row = rows[r];
-      row = row < 0 ? ~row : row;
-      dma16(p.kv + (int64_t)row * (ROW * 2) + ((lane ^ lat_flip(r)) << 4), buf + r * LAT_STRIDE);
-    }
-#pragma unroll
-    for (int i = wave; i < ROPE_INSTR; i += NW) {
-      const int r = i * 8 + (lane >> 3);
-      int row = rows[r];
-      row = row < 0 ? ~row : row;
-      dma16(p.kv + (int64_t)row * (ROW * 2) + LATENT * 2 + (((lane & 7) ^ (r & 7)) << 4),
-            buf + LAT_TILE_BYTES + i * 1024);
-    }
-  };
-
-  TileAddr ad;
-  ad.init(g, c);
-#pragma unroll
-  for (int k = 0; k < NBUF - 1; ++k)
-    if (k < w.ntiles) issue(k);
-
-  // Iteration k: wait for this wave's gathers of tile k (later tiles stay in
-  // flight), one barrier (tile k visible to every wave; ring slot
-  // (k - 1) % NBUF is free again), issue tile k + NBUF - 1, compute tile k.
-  for (int k = 0; k < w.ntiles; ++k) {
-    const int later = min(NBUF - 2, w.ntiles - 1 - k);
-    if (later >= 2) wait_vmcnt<2 * LOADS_PER_WAVE>();
-    else if (later == 1) wait_vmcnt<LOADS_PER_WAVE>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (k + NBUF - 1 < w.ntiles) issue(k + NBUF - 1);
-    compute_tile(a, smem + (k % NBUF) * BUF_BYTES, ad, tile_valid8(rows_sh + k * TILE, g), p.scale_log2);
+  for (int j = 0; j < ROUNDS; ++j) {
+    const int e = w.e_lo + j * THREADS + tid;
+    sv[j] = e < w.e_hi ? idx_row[e] : -1;
   }
-  write_result(a, p, w.tok, w.split, h, head_ok, g);
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < ROUNDS; ++j) {
+    if (w.e_lo + j * THREADS >= w.e_hi) break;  // uniform
+    const int s = sv[j];
+    const bool valid = s >= 0 && s < w.ctx;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(valid);
+    if (lane == 0) wsum[(j & 1) * NW + wave] = __builtin_popcountll(m);
+    __syncthreads();
+    int off = n, tot = 0;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      const int c = wsum[(j & 1) * NW + q];
+      off += q < wave ? c : 0;
+      tot += c;
+    }
+    if (valid) rows[off + __builtin_popcountll(m & below)] = (int)cache_row(p.sv, w.b, s);
+    n += tot;
+  }
+  __syncthreads();
+  const int padded = cdiv(n, TILE) * TILE;
+  if (n > 0)
+    for (int i = n + tid; i < padded; i += THREADS) rows[i] = rows[0];
+  __syncthreads();
+  return n;
 }
 
 // ---------------------------------------------------------------------------
-// FP8 rows: register staging with dequantisation, double-buffered LDS.
+// Tile producers.  issue(k, slot) starts the gathers of tile k; for bf16 rows
+// they land in the compute buffer, for FP8 rows in a raw staging buffer that
+// convert() then dequantises.  LOADS is the per-wave count of gather
+// instructions per tile that every wave has at least (for wait_vmcnt).
 // ---------------------------------------------------------------------------
 template <int NW>
-struct Fp8Stage {
-  static constexpr int THREADS = NW * WAVE;
-  // per row: 32 latent code chunks (16 codes each) + 8 rope chunks
-  static constexpr int CHUNKS = 40;
-  static constexpr int JOBS = (TILE * CHUNKS + THREADS - 1) / THREADS;
-  u32x4 raw[JOBS];
-  float scale[JOBS];
+struct Bf16Rows {
+  static constexpr int INSTR = TILE + ROPE_TILE_BYTES / 1024;  // 32 latent rows + 4 rope KiB
+  static constexpr int LOADS = INSTR / NW;
+  static_assert(INSTR % NW == 0, "gathers must split evenly over the waves");
 
-  __device__ __forceinline__ void load(const AttnParams& p, const int* rows, int tid) {
+  // The wave's rows are wave-uniform: each gather takes its row from LDS
+  // into a scalar register and addresses the row with an SGPR base, so only
+  // the lane's chunk offset lives in a VGPR.
+  __device__ __forceinline__ static void issue(const AttnParams& p, const int* rows, uint32_t buf, int wave,
+                                               int lane) {
+    int rv[LOADS];
 #pragma unroll
-    for (int k = 0; k < JOBS; ++k) {
-      const int j = tid + k * THREADS;
-      raw[k] = u32x4{0u, 0u, 0u, 0u};
-      scale[k] = 0.0f;
-      if (j < TILE * CHUNKS) {
-        const int r = j / CHUNKS, ch = j % CHUNKS;
-        const int row = rows[r];
-        if (row >= 0) {
-          const uint8_t* base = p.kv + (int64_t)row * FP8_ROW_BYTES;
-          if (ch < 32) {
-            raw[k] = *(const u32x4*)(base + ch * 16);
-            scale[k] = *(const float*)(base + LATENT + (ch >> 3) * 4);
-          } else {
-            raw[k] = *(const u32x4*)(base + LATENT + 16 + (ch - 32) * 16);
-          }
-        }
-      }
+    for (int j = 0; j < LOADS; ++j) {
+      const int i = wave * LOADS + j;
+      rv[j] = rows[i < TILE ? i : (i - TILE) * 8];  // rope: first row of the instruction (unused)
     }
-  }
-
-  __device__ __forceinline__ void store(uint8_t* buf, int tid) {
 #pragma unroll
-    for (int k = 0; k < JOBS; ++k) {
-      const int j = tid + k * THREADS;
-      if (j < TILE * CHUNKS) {
-        const int r = j / CHUNKS, ch = j % CHUNKS;
-        if (ch < 32) {
-          const float sc = scale[k];
-          u32x2 a0 = e4m3x4_to_bf16(raw[k][0], sc), a1 = e4m3x4_to_bf16(raw[k][1], sc);
-          u32x2 a2 = e4m3x4_to_bf16(raw[k][2], sc), a3 = e4m3x4_to_bf16(raw[k][3], sc);
-          *(u32x4*)(buf + lat_off(r, 2 * ch)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
-          *(u32x4*)(buf + lat_off(r, 2 * ch + 1)) = u32x4{a2[0], a2[1], a3[0], a3[1]};
-        } else {
-          *(u32x4*)(buf + rope_off(r, ch - 32)) = raw[k];
-        }
+    for (int j = 0; j < LOADS; ++j) {
+      const int i = wave * LOADS + j;  // wave-uniform
+      if (i < TILE) {
+        const int r = i;
+        const int row = __builtin_amdgcn_readfirstlane(rv[j]);
+        dma16_s(p.kv + (int64_t)row * (ROW * 2), (uint32_t)((lane ^ lat_swz(r)) << 4), buf + r * LAT_STRIDE);
+      } else {
+        const int r = (i - TILE) * 8 + (lane >> 3);
+        const int row = rows[r];
+        dma16(p.kv + (int64_t)row * (ROW * 2) + LATENT * 2 + (((lane & 7) ^ rope_swz(r)) << 4),
+              buf + LAT_TILE_BYTES + (i - TILE) * 1024);
       }
     }
   }
 };
 
-template <int NW, int MAXE>
-__global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF_BYTES];
+template <int NW>
+struct Fp8Rows {
+  static constexpr int INSTR = (RAW_CHUNKS + 63) / 64;  // 21 (the last one half full)
+  static constexpr int LOADS = INSTR / NW;
+
+  __device__ __forceinline__ static void issue(const AttnParams& p, const int* rows, uint32_t raw, int wave,
+                                               int lane) {
+#pragma unroll
+    for (int i = wave; i < INSTR; i += NW) {
+      const int q = i * 64 + lane;
+      if (q < RAW_CHUNKS) {
+        const int r = q / (FP8_ROW_BYTES / 16), ch = q % (FP8_ROW_BYTES / 16);
+        dma16(p.kv + (int64_t)rows[r] * FP8_ROW_BYTES + ch * 16, raw + i * 1024);
+      }
+    }
+  }
+
+  // raw packed rows (512 e4m3, 4 fp32 tile scales, 64 bf16 rope) -> bf16 tile
+  __device__ __forceinline__ static void convert(const uint8_t* raw, uint8_t* buf, int tid) {
+    constexpr int THREADS = NW * WAVE;
+    for (int j = tid; j < TILE * 32; j += THREADS) {
+      const int r = j >> 5, ch = j & 31;
+      const uint8_t* src = raw + r * FP8_ROW_BYTES;
+      const u32x4 codes = *(const u32x4*)(src + ch * 16);
+      const float sc = *(const float*)(src + LATENT + (ch >> 3) * 4);
+      const u32x2 a0 = e4m3x4_to_bf16(codes[0], sc), a1 = e4m3x4_to_bf16(codes[1], sc);
+      const u32x2 a2 = e4m3x4_to_bf16(codes[2], sc), a3 = e4m3x4_to_bf16(codes[3], sc);
+      *(u32x4*)(buf + lat_off(r, 2 * ch)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+      *(u32x4*)(buf + lat_off(r, 2 * ch + 1)) = u32x4{a2[0], a2[1], a3[0], a3[1]};
+    }
+    for (int j = tid; j < TILE * 8; j += THREADS) {
+      const int r = j >> 3, ch = j & 7;
+      *(u32x4*)(buf + rope_off(r, ch)) = *(const u32x4*)(raw + r * FP8_ROW_BYTES + LATENT + 16 + ch * 16);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// bf16 rows: direct HBM -> LDS gathers through an NBUF-deep ring.
+// ---------------------------------------------------------------------------
+template <int NW, int NBUF, int MAXE, bool SPLITP>
+__global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF_BYTES];
   __shared__ int rows_sh[MAXE];
-  constexpr int THREADS = NW * WAVE;
+  // per-wave scratch ints in the last ring slot: it is first filled by the
+  // gather issued in iteration 0, after every use of the scratch
+  int* wsum = (int*)(smem + (NBUF - 1) * BUF_BYTES);
+  typedef Bf16Rows<NW> R;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g = lane >> 4;
-  const int c = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar branches)
+  const int h = lane >> 5;
   Work w;
-  if (!map_work<NW>(p, w)) return;
-  const int h = w.hg * 16 * NW + wave * 16 + c;
-  const bool head_ok = h < p.H;
+  if (!map_work(p, w)) return;
+  const int head = wave * HPW + (lane & 31);
+  const bool head_ok = head < p.H;
 
-  resolve_rows<THREADS>(p, w, rows_sh, tid);
+  // index entries first (they gate the gathers), then the queries and the
+  // first gathers in flight together
+  const int n = resolve_rows<NW, MAXE>(p, w, rows_sh, wsum, tid);
+  const int ntiles = cdiv(n, TILE);
   WaveAcc a;
-  load_q(a, p, w.tok, h, head_ok, g);
-  __syncthreads();
+  load_q(a, p, w.tok, head, head_ok, h);
 
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
   TileAddr ad;
-  ad.init(g, c);
-  Fp8Stage<NW> st;
-  if (w.ntiles > 0) {
-    st.load(p, rows_sh, tid);
-    st.store(smem, tid);
+  ad.init(lane);
+  float m_ref = -INFINITY;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    reset_acc(a, m_ref);
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (k < ntiles) R::issue(p, rows_sh + k * TILE, smem_base + k * BUF_BYTES, wave, lane);
+    // queries and the first tiles landed: no compiler-inserted waits in the loop
+    wait_vmcnt<0>();
+    // Iteration k: wait for this wave's gathers of tile k (later tiles stay
+    // in flight), one barrier (tile k visible to every wave; ring slot
+    // (k - 1) % NBUF free again), issue tile k + NBUF - 1, compute tile k.
+    for (int k = 0; k < ntiles; ++k) {
+      const int later = min(NBUF - 2, ntiles - 1 - k);
+      if (later >= 2) wait_vmcnt<2 * R::LOADS>();
+      else if (later == 1) wait_vmcnt<R::LOADS>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (k + NBUF - 1 < ntiles)
+        R::issue(p, rows_sh + (k + NBUF - 1) * TILE, smem_base + ((k + NBUF - 1) % NBUF) * BUF_BYTES, wave, lane);
+      const uint8_t* buf = smem + (k % NBUF) * BUF_BYTES;
+      const f32x16 s = s_phase(a, buf, ad);
+      float pv[16];
+      softmax_tile(a, s, min(TILE, n - k * TILE), p.scale_log2, h, pv);
+      v_phase<SPLITP, 0, DV_TILES, true>(a, buf, ad, pack_p<SPLITP>(pv));
+    }
+    o_fence(a);
+    if (!needs_redo<NW>(a, wsum, wave, lane)) break;
+    m_ref = a.m_max;
   }
-  __syncthreads();
-  for (int k = 0; k < w.ntiles; ++k) {
-    const bool more = k + 1 < w.ntiles;
-    if (more) st.load(p, rows_sh + (k + 1) * TILE, tid);
-    compute_tile(a, smem + (k & 1) * BUF_BYTES, ad, tile_valid8(rows_sh + k * TILE, g), p.scale_log2);
-    if (more) st.store(smem + ((k + 1) & 1) * BUF_BYTES, tid);
-    __syncthreads();
+  write_result(a, p, w.tok, w.split, head, head_ok, h);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 rows: gathers into a raw NRAW-deep ring, dequantised by the workgroup
+// into a double-buffered bf16 tile.
+// ---------------------------------------------------------------------------
+template <int NW, int NRAW, int MAXE>
+__global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF_BYTES + NRAW * RAW_TILE_BYTES];
+  __shared__ int rows_sh[MAXE];
+  // per-wave scratch ints in the last raw ring slot: it is first filled by
+  // the gather issued in iteration 0, after every use of the scratch
+  int* wsum = (int*)(smem + 2 * BUF_BYTES + (NRAW - 1) * RAW_TILE_BYTES);
+  typedef Fp8Rows<NW> R;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar branches)
+  const int h = lane >> 5;
+  Work w;
+  if (!map_work(p, w)) return;
+  const int head = wave * HPW + (lane & 31);
+  const bool head_ok = head < p.H;
+
+  WaveAcc a;
+  load_q(a, p, w.tok, head, head_ok, h);
+  const int n = resolve_rows<NW, MAXE>(p, w, rows_sh, wsum, tid);
+  const int ntiles = cdiv(n, TILE);
+  wait_vmcnt<0>();
+
+  uint8_t* raw = smem + 2 * BUF_BYTES;
+  const uint32_t raw_base = (uint32_t)(uintptr_t)(lds_void*)raw;
+  TileAddr ad;
+  ad.init(lane);
+  float m_ref = -INFINITY;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    reset_acc(a, m_ref);
+#pragma unroll
+    for (int k = 0; k < NRAW - 1; ++k)
+      if (k < ntiles) R::issue(p, rows_sh + k * TILE, raw_base + k * RAW_TILE_BYTES, wave, lane);
+    // Iteration k: raw tile k ready (barrier: visible; raw slot (k - 1) % NRAW
+    // and bf16 slot k % 2 free), issue raw tile k + NRAW - 1, dequantise tile
+    // k, barrier, compute tile k.
+    for (int k = 0; k < ntiles; ++k) {
+      const int later = min(NRAW - 2, ntiles - 1 - k);
+      if (later >= 2) wait_vmcnt<2 * R::LOADS>();
+      else if (later == 1) wait_vmcnt<R::LOADS>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (k + NRAW - 1 < ntiles)
+        R::issue(p, rows_sh + (k + NRAW - 1) * TILE, raw_base + ((k + NRAW - 1) % NRAW) * RAW_TILE_BYTES, wave,
+                 lane);
+      uint8_t* buf = smem + (k & 1) * BUF_BYTES;
+      R::convert(raw + (k % NRAW) * RAW_TILE_BYTES, buf, tid);
+      __syncthreads();
+      const f32x16 s = s_phase(a, buf, ad);
+      float pv[16];
+      softmax_tile(a, s, min(TILE, n - k * TILE), p.scale_log2, h, pv);
+      v_phase<false, 0, DV_TILES, true>(a, buf, ad, pack_p<false>(pv));
+    }
+    o_fence(a);
+    if (!needs_redo<NW>(a, wsum, wave, lane)) break;
+    m_ref = a.m_max;
   }
-  write_result(a, p, w.tok, w.split, h, head_ok, g);
+  write_result(a, p, w.tok, w.split, head, head_ok, h);
 }
 
 // Merge split partials: lse = log sum_s exp(lse_s); O = sum_s exp(lse_s - lse) O_s.
 __global__ __launch_bounds__(128) void combine_kernel(AttnParams p) {
-  const int th = blockIdx.x;  // (token, head)
+  const int th = blockIdx.x;
   const int tok = th / p.H, h = th % p.H;
   const int S = p.num_splits;
   const int64_t base = (int64_t)tok * S * p.H + h;
@@ -530,40 +670,37 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnParams p) {
     p.lse[(int64_t)tok * p.H + h] = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
 }
 
-// nhg16: 16-head groups per block; waves: waves per block
 template <typename K>
-hipError_t launch_grid(K kernel, const AttnParams& p, int nhg16, int waves, hipStream_t stream) {
-  const int nhg = cdiv(p.H, 16 * nhg16);
-  const int pairs = p.sv.num_tokens * p.num_splits;
-  const int blocks = cdiv(pairs, 8) * 8 * nhg;
+hipError_t launch_grid(K kernel, const AttnParams& p, int waves, hipStream_t stream) {
+  const int blocks = cdiv(p.sv.num_tokens, 8) * 8 * p.num_splits;
   hipLaunchKernelGGL(kernel, dim3(blocks), dim3(waves * WAVE), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int NW>
 hipError_t launch_nw(const AttnParams& p, bool fp8, hipStream_t stream) {
-  const int tiles_per_split = cdiv(p.split_len, TILE);
-  if (fp8) return launch_grid(attn_fp8_kernel<NW, 2048>, p, NW, NW, stream);
-  if (tiles_per_split * TILE <= 1024) return launch_grid(attn_bf16_kernel<NW, 4, 1024>, p, NW, NW, stream);
-  return launch_grid(attn_bf16_kernel<NW, 3, 2048>, p, NW, NW, stream);
+  if (fp8) return launch_grid(attn_fp8_kernel<NW, 3, 2048>, p, NW, stream);
+  if (p.split_len <= 1024) return launch_grid(attn_bf16_kernel<NW, 4, 1024, true>, p, NW, stream);
+  return launch_grid(attn_bf16_kernel<NW, 4, 2048, true>, p, NW, stream);
 }
 
 }  // namespace
 
 int attn_num_splits(int num_tokens, int H, int top_k) {
-  const int nw = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
-  const int nhg = cdiv(H, 16 * nw);
-  const int items = num_tokens * nhg;
+  (void)H;
+  // one workgroup per (token, split); aim for one per CU (256), splits of at
+  // least four tiles
   const int max_splits = std::max(1, cdiv(top_k, 4 * TILE));
-  const int s = cdiv(256, std::max(1, items));
+  const int s = cdiv(256, std::max(1, num_tokens));
   return std::min(std::max(s, 1), max_splits);
 }
 
 hipError_t launch_attn(const AttnParams& p, bool kv_fp8, hipStream_t stream) {
   timer_before(2, stream);
   hipError_t e;
-  if (p.H <= 16) e = launch_nw<1>(p, kv_fp8, stream);
-  else if (p.H <= 32) e = launch_nw<2>(p, kv_fp8, stream);
+  if (p.H <= 32) e = launch_nw<1>(p, kv_fp8, stream);
+  else if (p.H <= 64) e = launch_nw<2>(p, kv_fp8, stream);
+  else if (p.H <= 96) e = launch_nw<3>(p, kv_fp8, stream);
   else e = launch_nw<4>(p, kv_fp8, stream);
   timer_after(2, stream);
   if (e != hipSuccess || p.num_splits == 1) return e;
