@@ -59,7 +59,6 @@ constexpr float MAX_GROWTH = 64.0f;             // log2 growth of the max over t
 constexpr float LN2 = 0.69314718055994530942f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 // D += A * B on a 32x32 fp32 tile, K = 16 (bf16 operands).
 //   a: lane l holds A[l % 32][8 * (l / 32) + 0..7]
@@ -91,32 +90,6 @@ __device__ __forceinline__ void mfma32_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
 // the same value.)
 __device__ __forceinline__ float pair_max(float v) { return fmaxf(v, shfl_xor(v, 32)); }
 __device__ __forceinline__ float pair_sum(float v) { return v + shfl_xor(v, 32); }
-
-// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding; the
-// 6-bit vmcnt saturates at 63, and waiting for fewer is always safe).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  constexpr int n = N > 63 ? 63 : N;
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
-
-// 16 bytes per lane from global memory straight into LDS at lds_addr + 16 *
-// lane (lds_addr is wave-uniform).  dma16_s takes a wave-uniform base address
-// (SGPRs) and a 32-bit per-lane byte offset.  Written as inline asm so that the
-// compiler does not turn later LDS reads of other ring slots into waits for
-// every outstanding gather: completion is tracked with wait_vmcnt().
-__device__ __forceinline__ void dma16(const uint8_t* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma16_s(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-               : "memory", "m0");
-}
 
 // LDS addresses of 16-byte chunk `ch` of tile row r.  The LDS has 64 banks
 // of 4 bytes; a 128-bit read serves 16 lanes per cycle, a 64-bit transposing

@@ -179,11 +179,205 @@ __global__ void zero_kernel(uint32_t* p, int64_t n4) {
     ((u32x4*)p)[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
+// ---------------------------------------------------------------------------
+// Prefill: a workgroup takes PF_TOKS consecutive query tokens of one sequence
+// (one per wave, two waves per SIMD) and walks their whole causal key range
+// [0, t_last] in tiles of PF_KT keys that every wave reads from LDS.  The
+// tiles come from HBM / L2 straight into an LDS ring (global_load_lds), so
+// each key row is read once per workgroup instead of once per token.
+//
+// Per wave and tile: for each 16-key sub-tile, MT x KS MFMAs (16 heads x 16
+// keys x 32 dims) with the query operand in registers and the key operand
+// read from LDS; ReLU and the head weights fold into registers; the 4 lane
+// groups (4 heads each per M-tile) are summed across lanes.  Lane (g, c)
+// keeps sub-tile g, so one 256-byte store per tile writes the token's 64
+// scores.  Because the workgroup covers the whole row of each of its
+// tokens, it builds the rows' key histograms in LDS and writes them out
+// whole: no global atomics and no clearing pass.
+//
+// Key rows in LDS: the 16-byte chunk ch of key row r sits at chunk
+// ch ^ swz(r) of the row, so the 16 keys of a sub-tile read at one logical
+// chunk (16 lanes of a 128-bit read) hit 16 different bank windows.
+// ---------------------------------------------------------------------------
+constexpr int PF_TOKS = 8;        // tokens (= waves) per workgroup
+constexpr int PF_KT = 64;         // keys per tile
+constexpr int PF_NBUF = 3;        // tile ring depth
+constexpr int PF_MAX_PAGES = 8192;  // block-table entries a workgroup can stage
+
+template <int CPR>
+__device__ __forceinline__ int pf_swz(int r) {
+  return (r / (16 / CPR)) & (CPR - 1);
+}
+
+// lane-group sums across lanes l ^ 16 and l ^ 32 (all four groups end with the total)
+__device__ __forceinline__ float sum_groups(float v) {
+  v += shfl_xor(v, 16);
+  v += shfl_xor(v, 32);
+  return v;
+}
+
+template <int MT, int KS, bool FP8>
+__global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreParams p) {
+  constexpr int ROWB = FP8 ? KS * 32 : KS * 64;  // key row bytes
+  constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
+  constexpr int TILEB = PF_KT * ROWB;
+  constexpr int INSTR = TILEB / 1024;            // 1 KiB gathers per tile
+  constexpr int RPI = 1024 / ROWB;               // key rows per gather
+  constexpr int LOADS = INSTR / PF_TOKS;         // gathers per tile every wave has at least
+  __shared__ uint32_t hist[PF_TOKS][SCORE_HIST_BINS];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[PF_NBUF * TILEB];
+  __shared__ float ksc[PF_NBUF][PF_KT];
+  __shared__ int pages[PF_MAX_PAGES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const SeqView& sv = p.sv;
+
+  // ---- work: heaviest token blocks first -------------------------------------
+  const int b = blockIdx.y;
+  const int ql = q_len(sv, b);
+  const int nqb = cdiv(ql, PF_TOKS);
+  const int qb = nqb - 1 - (int)blockIdx.x;
+  if (qb < 0) return;
+  const int ctx = sv.ctx_len[b];
+  const int i_tok = qb * PF_TOKS + wave;           // query index inside the sequence
+  const bool active = i_tok < ql;
+  const int tok = first_token(sv, b) + (active ? i_tok : 0);
+  const int t = ctx - ql + i_tok;                  // this wave's query position
+  const int t_last = ctx - ql + min(ql, (qb + 1) * PF_TOKS) - 1;
+  const int ntiles = cdiv(t_last + 1, PF_KT);
+  const bool paged = sv.block_table != nullptr;
+
+  for (int i = tid; i < PF_TOKS * SCORE_HIST_BINS; i += PF_TOKS * WAVE) (&hist[0][0])[i] = 0u;
+  if (paged) {
+    const int np = (t_last >> sv.page_shift) + 1;
+    for (int i = tid; i < np; i += PF_TOKS * WAVE) pages[i] = sv.block_table[(int64_t)b * sv.bt_stride + i];
+  }
+
+  // ---- query operand: Q[h = 16 mt + c][kdim(ks, g) .. +8], head weights ------
+  bf16x8 qa[MT][KS];
+  float w[MT][4];
+  const uint16_t* qrow = p.q_idx + (int64_t)tok * p.H_I * p.d_I;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int hq = mt * 16 + c;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hq < p.H_I) v = *(const u32x4*)(qrow + (int64_t)hq * p.d_I + kdim<FP8>(ks, g));
+      qa[mt][ks] = as_bf16x8(v);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hr = mt * 16 + g * 4 + r;
+      w[mt][r] = hr < p.H_I ? p.head_w[(int64_t)tok * p.H_I + hr] : 0.0f;
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // histograms cleared, block-table entries staged
+
+  // ---- gathers of tile k into ring slot k % PF_NBUF --------------------------
+  const uint32_t ring_base = lds_addr(ring);
+  auto cache_row_of = [&](int s) -> int64_t {
+    s = min(s, t_last);  // keys past the last token are masked later; stay in bounds
+    if (!paged) return (int64_t)b * sv.seq_stride + s;
+    return ((int64_t)pages[s >> sv.page_shift] << sv.page_shift) + (s & ((1 << sv.page_shift) - 1));
+  };
+  auto issue = [&](int k) {
+    const uint32_t slot = ring_base + (k % PF_NBUF) * TILEB;
+#pragma unroll
+    for (int i = wave; i < INSTR; i += PF_TOKS) {
+      const int r = i * RPI + lane / CPR;
+      const int ch = (lane % CPR) ^ pf_swz<CPR>(r);
+      dma16(p.k_idx + cache_row_of(k * PF_KT + r) * ROWB + ch * 16, slot + i * 1024);
+    }
+    if (p.k_scale && wave == PF_TOKS - 1)
+      dma4(p.k_scale + cache_row_of(k * PF_KT + lane), lds_addr(&ksc[k % PF_NBUF][0]));
+  };
+
+  // per-lane LDS offsets of the key operand: key c of the sub-tile, logical
+  // chunk (bf16) 4 ks + g, (e4m3) 4 j + g for k-steps 2 j, 2 j + 1
+  constexpr int NLD = FP8 ? KS / 2 : KS;  // 16-byte operand loads per sub-tile
+  int boff[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) boff[j] = c * ROWB + (((4 * j + g) ^ pf_swz<CPR>(c)) << 4);
+
+  float* srow = p.scores + (int64_t)tok * p.score_stride;
+  uint32_t* my_hist = hist[wave];
+
+#pragma unroll
+  for (int k = 0; k < PF_NBUF - 1; ++k)
+    if (k < ntiles) issue(k);
+
+  for (int k = 0; k < ntiles; ++k) {
+    const int later = min(PF_NBUF - 2, ntiles - 1 - k);
+    if (later >= 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // tile k visible; slot (k - 1) % PF_NBUF free
+    if (k + PF_NBUF - 1 < ntiles) issue(k + PF_NBUF - 1);
+    if (active && k * PF_KT <= t) {
+      const uint8_t* tile = ring + (k % PF_NBUF) * TILEB;
+      float keep = 0.0f;
+#pragma unroll
+      for (int st = 0; st < PF_KT / 16; ++st) {
+        bf16x8 kb[KS];
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+          const u32x4 raw = *(const u32x4*)(tile + st * 16 * ROWB + boff[j]);
+          if (FP8) {
+            const u32x2 a0 = e4m3x4_to_bf16(raw[0], 1.0f), a1 = e4m3x4_to_bf16(raw[1], 1.0f);
+            const u32x2 a2 = e4m3x4_to_bf16(raw[2], 1.0f), a3 = e4m3x4_to_bf16(raw[3], 1.0f);
+            kb[2 * j] = as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]});
+            kb[2 * j + 1] = as_bf16x8(u32x4{a2[0], a2[1], a3[0], a3[1]});
+          } else {
+            kb[j] = as_bf16x8(raw);
+          }
+        }
+        float v = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = mfma16(qa[mt][ks], kb[ks], acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v += w[mt][r] * fmaxf(acc[r], 0.0f);
+        }
+        v = sum_groups(v);
+        if (g == st) keep = v;
+      }
+      const int sk = k * PF_KT + 16 * g + c;  // this lane's key
+      if (p.k_scale) keep *= ksc[k % PF_NBUF][16 * g + c];
+      keep += 0.0f;  // -0 -> +0
+      if (sk <= t) {
+        srow[sk] = keep;
+        atomicAdd(&my_hist[score_key(keep) >> (32 - SCORE_HIST_BITS)], 1u);
+      }
+    }
+  }
+
+  // ---- the complete key histogram of each token's row -------------------------
+  __syncthreads();
+  if (active) {
+    uint32_t* gh = p.hist + (int64_t)tok * SCORE_HIST_BINS;
+    for (int i = lane; i < SCORE_HIST_BINS / 4; i += WAVE) ((u32x4*)gh)[i] = ((const u32x4*)my_hist)[i];
+  }
+}
+
+// true when the prefill kernel can stage the block table of every row
+bool prefill_fits(const SeqView& sv) {
+  return sv.block_table == nullptr || cdiv(sv.max_ctx_len, 1 << sv.page_shift) <= PF_MAX_PAGES;
+}
+
 template <int MT, int KS, bool FP8>
 hipError_t launch_mt(const ScoreParams& p, hipStream_t stream) {
   const SeqView& sv = p.sv;
   const bool decode = sv.max_q_len == 1;
-  if (decode) {
+  if (!decode && prefill_fits(sv)) {
+    dim3 grid(cdiv(sv.max_q_len, PF_TOKS), sv.num_seqs);
+    hipLaunchKernelGGL((score_prefill_kernel<MT, KS, FP8>), grid, dim3(PF_TOKS * WAVE), 0, stream, p);
+  } else if (decode) {
     const int kpw = 1024;
     dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs);
     hipLaunchKernelGGL((score_kernel<MT, KS, FP8, true>), grid, dim3(256), 0, stream, p, kpw);
@@ -217,12 +411,15 @@ hipError_t launch_dt(const ScoreParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream) {
-  // the row histograms are accumulated with atomics: clear them first (a
-  // kernel, not a memset, so the call stays safe to capture in a graph)
-  const int64_t n4 = (int64_t)p.sv.num_tokens * SCORE_HIST_BINS / 4;
-  const int64_t zblocks = std::min<int64_t>((n4 + 255) / 256, 2048);
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream, p.hist, n4);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  // the decode kernel accumulates the row histograms with atomics: clear
+  // them first (a kernel, not a memset, so the call stays safe to capture in
+  // a graph); the prefill kernel writes whole rows
+  if (p.sv.max_q_len == 1 || !prefill_fits(p.sv)) {
+    const int64_t n4 = (int64_t)p.sv.num_tokens * SCORE_HIST_BINS / 4;
+    const int64_t zblocks = std::min<int64_t>((n4 + 255) / 256, 2048);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream, p.hist, n4);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
   timer_before(0, stream);
   hipError_t e = k_fp8 ? launch_dt<true>(p, stream) : launch_dt<false>(p, stream);
   timer_after(0, stream);

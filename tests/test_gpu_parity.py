@@ -89,6 +89,15 @@ def test_key_scale_and_d64():
     _parity_all(generate(wl, "cuda"), U.TOL_BF16, "k_scale")
 
 
+def test_prefill_e4m3_keys_small_pages_and_scales():
+    # e4m3 index keys and FP8 latent rows in a prefill call, paged with 16-row
+    # pages (several pages per key tile), per-row key scales, ragged q_len
+    wl = Workload("prefill e4m3 paged", [1500, 600, 77], [{"seqs": [0, 1, 2], "q_len": [37, 300, 77]}],
+                  top_k=256, k_dtype="e4m3", kv_dtype="fp8_656", paged=True, page_size=16, k_scale=True,
+                  k_range=8, seed=29)
+    _parity_all(generate(wl, "cuda"), U.TOL_FP8, "prefill e4m3 paged")
+
+
 def test_all_equal_scores_take_lowest_positions():
     wl = Workload("zeros", [3000], [{"seqs": [0], "q_len": [5]}], top_k=256, seed=25)
     inp = generate(wl, "cuda")
@@ -130,6 +139,41 @@ def test_attention_skips_invalid_entries_and_empty_rows():
     w_out, w_lse = oracle.attention(osq, U.bits16(inp.q), U.host_raw(inp.kv), "bf16", idx.cpu().numpy(), U.SCALE)
     U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), w_out, w_lse, U.TOL_BF16, "invalid entries")
     assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
+
+
+def test_attention_score_growth_far_beyond_first_tile():
+    """The softmax runs against the first tile's maximum; when later tiles
+    score ~150 (base 2) higher, the p values would overflow fp32, and the
+    kernel must fall back to its second pass with the true maximum."""
+    import indexer_selected_sparse_idx_amd as lib
+    import oracle
+    wl = Workload("growth", [256, 256], [{"seqs": [0, 1], "q_len": None}], H=64, top_k=128, seed=28)
+    inp = generate(wl, "cuda")
+    call = inp.calls[0]
+    s = U.lib_seqs(inp, call)
+    # query: 12 along latent dim 0 for every head; rows: dim 0 = 200 for the
+    # later entries, every value of the first 32 entries scaled to ~0
+    q = torch.zeros_like(inp.q)
+    q[:, :, 0] = 12.0
+    q[:, :, 1:] = inp.q[:, :, 1:] * 0.1
+    kv = inp.kv.clone()
+    idx = torch.stack([torch.arange(0, 256, 2, dtype=torch.int32), torch.arange(1, 256, 2, dtype=torch.int32)])
+    for b in range(2):
+        rows = b * inp.seq_stride + idx[b].long()
+        first, later = rows[:32].cuda(), rows[32:].cuda()
+        kv[first] = (kv[first].float() * 1e-3).to(kv.dtype)
+        big = kv[later].float()
+        big[:, 0] = 200.0 + torch.arange(big.shape[0], device="cuda", dtype=torch.float32) * 0.25
+        kv[later] = big.to(kv.dtype)
+    idx = idx.cuda()
+    out, lse = lib.sparse_mla_attn(s, q, kv, idx, U.SCALE)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    osq = U.oracle_seqs(inp, call)
+    w_out, w_lse = oracle.attention(osq, U.bits16(q), U.host_raw(kv), "bf16", idx.cpu().numpy(), U.SCALE)
+    # scores here reach ~100 (natural log units): compare lse relative to its size
+    U.check_attention(out.cpu().numpy(), lse.cpu().numpy() / 100.0, w_out, w_lse / 100.0, U.TOL_BF16,
+                      "score growth")
 
 
 def test_paged_equals_contiguous_bitwise():
