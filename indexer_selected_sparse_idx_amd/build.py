@@ -35,9 +35,10 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-# per-source extra flags: the attention kernels keep the O^T accumulator in
-# AGPRs through inline asm and want every builtin MFMA in VGPR form
-EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# per-source extra flags: builtin MFMAs in VGPR form (the score kernels read
+# every accumulator with VALU instructions; the attention kernels keep O^T in
+# AGPRs through inline asm and everything else in VGPRs)
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src):

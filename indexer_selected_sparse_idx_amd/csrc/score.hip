@@ -36,6 +36,13 @@ namespace {
 constexpr int SCORE_WAVES = 4;
 constexpr int NT = 4;  // key tiles (16 keys each) per loop iteration
 
+// max(x, 0) as one integer max on the bit pattern: negative floats (-0
+// included) are negative integers (fmaxf costs a second instruction that
+// quiets NaN inputs)
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
 // First dim of the 8-wide slice that lane group g holds at k-step ks.
 template <bool FP8>
 __device__ __forceinline__ int kdim(int ks, int g) {
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) acc = mfma16(qa[mt][ks], kb[nt][ks], acc);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v += w[mt][r] * fmaxf(acc[r] * ksc[nt], 0.0f);
+          for (int r = 0; r < 4; ++r) v += w[mt][r] * relu(acc[r] * ksc[nt]);
         }
         v += shfl_xor(v, 16);
         v += shfl_xor(v, 32);
@@ -209,11 +216,32 @@ __device__ __forceinline__ int pf_swz(int r) {
   return (r / (16 / CPR)) & (CPR - 1);
 }
 
-// lane-group sums across lanes l ^ 16 and l ^ 32 (all four groups end with the total)
-__device__ __forceinline__ float sum_groups(float v) {
-  v += shfl_xor(v, 16);
-  v += shfl_xor(v, 32);
-  return v;
+// Reduce-scatter over the 4 lane groups (rows of 16 lanes): x[st] holds the
+// group's partial for sub-tile st; the result at lane (g, c) is the sum over
+// the four groups of x[g].  Two butterfly steps with the gfx950 row swaps:
+// v_permlane16_swap exchanges rows 1, 3 of its first operand with rows 0, 2 of
+// its second, v_permlane32_swap the upper half of the first with the lower
+// half of the second.  (Inline asm: the builtins fold their two results into
+// one when both inputs are the same value.)
+__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane32_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float reduce_scatter4(const float (&x)[4], int g) {
+  // step 1: rows 2 r and 2 r + 1 exchange; even rows keep sub-tiles 0 and 2,
+  // odd rows 1 and 3
+  float a0 = x[0], b0 = x[1], a1 = x[2], b1 = x[3];
+  permlane16_swap(a0, b0);  // a0: odd rows now hold the even row's x[1]; b0: even rows the odd row's x[0]
+  permlane16_swap(a1, b1);
+  const bool odd = g & 1;
+  const float y = odd ? x[1] + a0 : x[0] + b0;  // sub-tile 0 (even rows) or 1 (odd rows)
+  const float z = odd ? x[3] + a1 : x[2] + b1;  // sub-tile 2 or 3
+  // step 2: rows r and r + 2 exchange; rows 0, 1 keep y, rows 2, 3 keep z
+  float ya = y, zb = z;
+  permlane32_swap(ya, zb);  // ya: upper rows hold the lower rows' z; zb: lower rows the upper rows' y
+  return g < 2 ? y + zb : z + ya;
 }
 
 template <int MT, int KS, bool FP8>
@@ -293,8 +321,11 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
       const int ch = (lane % CPR) ^ pf_swz<CPR>(r);
       dma16(p.k_idx + cache_row_of(k * PF_KT + r) * ROWB + ch * 16, slot + i * 1024);
     }
-    if (p.k_scale && wave == PF_TOKS - 1)
-      dma4(p.k_scale + cache_row_of(k * PF_KT + lane), lds_addr(&ksc[k % PF_NBUF][0]));
+    if (p.k_scale && wave == PF_TOKS - 1) {
+#pragma unroll
+      for (int j = 0; j < PF_KT / 64; ++j)
+        dma4(p.k_scale + cache_row_of(k * PF_KT + j * 64 + lane), lds_addr(&ksc[k % PF_NBUF][j * 64]));
+    }
   };
 
   // per-lane LDS offsets of the key operand: key c of the sub-tile, logical
@@ -317,11 +348,13 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     else wait_vmcnt<0>();
     __syncthreads();  // tile k visible; slot (k - 1) % PF_NBUF free
     if (k + PF_NBUF - 1 < ntiles) issue(k + PF_NBUF - 1);
-    if (active && k * PF_KT <= t) {
-      const uint8_t* tile = ring + (k % PF_NBUF) * TILEB;
-      float keep = 0.0f;
 #pragma unroll
-      for (int st = 0; st < PF_KT / 16; ++st) {
+    for (int qd = 0; qd < PF_KT / 64; ++qd) {  // 64-key quads of the tile
+    if (active && k * PF_KT + qd * 64 <= t) {
+      const uint8_t* tile = ring + (k % PF_NBUF) * TILEB + qd * 64 * ROWB;
+      float xs[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
         bf16x8 kb[KS];
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
@@ -342,18 +375,19 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) acc = mfma16(qa[mt][ks], kb[ks], acc);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v += w[mt][r] * fmaxf(acc[r], 0.0f);
+          for (int r = 0; r < 4; ++r) v += w[mt][r] * relu(acc[r]);
         }
-        v = sum_groups(v);
-        if (g == st) keep = v;
+        xs[st] = v;
       }
-      const int sk = k * PF_KT + 16 * g + c;  // this lane's key
-      if (p.k_scale) keep *= ksc[k % PF_NBUF][16 * g + c];
+      float keep = reduce_scatter4(xs, g);
+      const int sk = k * PF_KT + qd * 64 + 16 * g + c;  // this lane's key
+      if (p.k_scale) keep *= ksc[k % PF_NBUF][qd * 64 + 16 * g + c];
       keep += 0.0f;  // -0 -> +0
       if (sk <= t) {
         srow[sk] = keep;
         atomicAdd(&my_hist[score_key(keep) >> (32 - SCORE_HIST_BITS)], 1u);
       }
+    }
     }
   }
 

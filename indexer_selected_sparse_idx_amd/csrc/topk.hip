@@ -82,24 +82,43 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
   return v;
 }
 
+// Digit passes of the radix select: FIXED top bits are already known to be
+// equal for every key of the list (0, or SCORE_HIST_BITS for the candidates
+// of one histogram bucket); the remaining bits go 8 at a time, the last pass
+// taking what is left.
+template <int FIXED>
+struct Digits {
+  static constexpr int REST = 32 - FIXED;
+  static constexpr int PASSES = (REST + 7) / 8;
+  __device__ __forceinline__ static int width(int pass) { return pass + 1 < PASSES ? 8 : REST - 8 * (PASSES - 1); }
+  __device__ __forceinline__ static int shift(int pass) {
+    int s = REST;
+    for (int q = 0; q <= pass; ++q) s -= width(q);
+    return s;
+  }
+};
+
 // Select the m largest of n keys (ties: lowest index first) and write their
-// positions (pos[i], or i when pos is null) to out[0 .. m).
-template <bool IN_LDS>
+// positions (pos[i], or i when pos is null) to out[0 .. m).  Every key's top
+// FIXED bits equal prefix0.
+template <bool IN_LDS, int FIXED>
 __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out, const int32_t* pos, uint32_t* hist,
-                           uint32_t* whist, uint32_t* wcnt) {
+                           uint32_t* whist, uint32_t* wcnt, uint32_t prefix0) {
+  typedef Digits<FIXED> D;
   __shared__ uint32_t sh_digit, sh_above, sh_whole;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
   // ---- radix passes ----------------------------------------------------------
-  uint32_t prefix = 0;  // digits chosen so far
-  uint32_t rem = m;     // positions still to take inside the current bucket
-  int level = 0;        // number of digits fixed
+  uint32_t prefix = prefix0;  // top bits chosen so far
+  uint32_t rem = m;           // positions still to take inside the current bucket
+  int cshift = 32 - FIXED;    // keys match the prefix on bits >= cshift
   uint32_t* my_hist = whist + wave * 256;
   const int n4 = (n + 3) / 4 * 4;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  for (int pass = 0; pass < D::PASSES; ++pass) {
+    const int shift = D::shift(pass);
+    const uint32_t dmask = (1u << D::width(pass)) - 1u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) my_hist[lane + 64 * j] = 0;
     for (int i0 = 4 * tid; i0 < n4; i0 += 4 * TOPK_THREADS * UNROLL) {
@@ -115,8 +134,8 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t key = k[u][e];
-          const bool in = i + e < n && (pass == 0 || (key >> (shift + 8)) == prefix);
-          if (in) atomicAdd(&my_hist[(key >> shift) & 255u], 1u);
+          const bool in = i + e < n && (cshift >= 32 || (key >> cshift) == prefix);
+          if (in) atomicAdd(&my_hist[(key >> shift) & dmask], 1u);
         }
       }
     }
@@ -155,15 +174,14 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
       }
     }
     __syncthreads();
-    prefix = (prefix << 8) | sh_digit;
+    prefix = (prefix << D::width(pass)) | sh_digit;
     rem -= sh_above;
-    level = pass + 1;
+    cshift = shift;
     const bool whole = sh_whole;
     __syncthreads();
     if (whole) break;
   }
-  // compare keys on their top 8*level bits against `prefix`
-  const int cshift = 32 - 8 * level;
+  // compare keys on their bits >= cshift against `prefix`
   const uint32_t need = rem;       // prefix-equal positions to take
   const uint32_t n_gt = m - need;  // positions above the prefix
 
@@ -278,7 +296,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkParams p) {
   }
   const uint32_t d1 = sh_d1, above1 = sh_above1, cnt1 = sh_cnt1;
   if (cnt1 > (uint32_t)CAP) {  // massive ties: select over the whole row
-    select_row<false>(Keys<false>{nullptr, row, n}, n, m, out, nullptr, hist, whist, wcnt);
+    select_row<false, 0>(Keys<false>{nullptr, row, n}, n, m, out, nullptr, hist, whist, wcnt, 0u);
     return;
   }
 
@@ -339,8 +357,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkParams p) {
   __syncthreads();
 
   // ---- 3. the remaining m - above1 positions come from the candidates -------------
-  select_row<true>(Keys<true>{cand_key, nullptr, (int)cnt1}, (int)cnt1, m - (int)above1, out + above1, cand_pos, hist,
-                   whist, wcnt);
+  select_row<true, SCORE_HIST_BITS>(Keys<true>{cand_key, nullptr, (int)cnt1}, (int)cnt1, m - (int)above1,
+                                    out + above1, cand_pos, hist, whist, wcnt, d1);
 }
 
 }  // namespace
