@@ -107,7 +107,9 @@ typedef struct idx_seqs {
  *
  *   q_idx    [T, H_I, d_I], dtype q_dtype (IDX_BF16)
  *   k_idx    cache rows of d_I values, dtype k_dtype (IDX_BF16 or IDX_E4M3)
- *   k_scale  fp32 per cache row, or NULL for 1.0
+ *   k_scale  fp32 per cache row, or NULL for 1.0.  A quantisation scale, so it
+ *            must be >= 0: ReLU(k * x) = k * ReLU(x) then holds, and prefill
+ *            calls apply it to the head-weighted sum (one multiply per key)
  *   head_w   fp32 [T, H_I]
  *   H_I      1..64 indexer heads;  d_I in {64, 128};  top_k 1..2048
  *   out_idx  int32 [T, top_k]
