@@ -146,6 +146,8 @@ int idx_score_topk(const idx_seqs *seqs,
  *   kv       cache rows, dtype kv_dtype (IDX_BF16: 576 bf16 = 1152 bytes;
  *            IDX_KV_FP8_656: 656-byte packed rows)
  *   idx      int32 [T, top_k] logical positions;  top_k 1..2048
+ *   softmax_scale  finite and > 0 (a softmax temperature; 1/sqrt(576) in
+ *            the pages' models), else IDX_ERR_INVALID_ARG
  *   out      fp32 [T, H, 512];  lse fp32 [T, H] or NULL
  * ------------------------------------------------------------------------ */
 size_t sparse_mla_attn_workspace(const idx_seqs *seqs, int H, int top_k);

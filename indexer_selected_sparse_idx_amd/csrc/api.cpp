@@ -88,8 +88,7 @@ int check_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, int k
   if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return IDX_ERR_INVALID_ARG;
   if (lse && !aligned4(lse)) return IDX_ERR_INVALID_ARG;
   if (H < 1 || top_k < 1) return IDX_ERR_INVALID_ARG;
-  if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
-    return IDX_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.0f) || softmax_scale > 3.0e38f) return IDX_ERR_INVALID_ARG;
   if (kv_dtype != IDX_BF16 && kv_dtype != IDX_KV_FP8_656) return IDX_ERR_UNSUPPORTED;
   if (H > 128 || top_k > 2048) return IDX_ERR_UNSUPPORTED;
   return IDX_OK;

@@ -28,15 +28,17 @@
 // O^T in the accumulation registers.
 //
 // bf16 rows go from HBM straight into LDS (global_load_lds_dwordx4, one wave
-// instruction per 1 KiB latent row) through an NBUF-deep ring, and the loop is
-// software-pipelined: after one barrier per tile, the MFMAs of S for tile k+1
-// are issued together with the softmax of tile k, then P.V of tile k.  FP8
-// rows (656 bytes) go into a raw LDS ring the same way and are dequantised to
-// the bf16 tile layout by the workgroup.  Splits (decode occupancy) are
-// merged by combine_kernel.
+// instruction per 1 KiB latent row) through a 4-deep ring with one barrier per
+// tile, and the loop is software-pipelined: iteration k runs S of tile k
+// with the gathers of tile k + 2 spread over its k-steps, then P.V of tile
+// k - 1 with the softmax of tile k in the shadow of those MFMAs.  FP8 rows
+// (656 bytes) go into a raw LDS ring the same way and are dequantised to the
+// bf16 tile layout by the workgroup.  Splits (decode occupancy) are merged by
+// combine_kernel.
 #include <math.h>
 
 #include <algorithm>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -190,44 +192,41 @@ __device__ __forceinline__ bf16x8 v_operand(const uint8_t* buf, const TileAddr& 
 // S^T[32 keys x 32 heads] of one tile.  The operand of k-step ks + SPRE is
 // read from LDS while the MFMA of k-step ks runs; the scheduling fences keep
 // that order (left alone, the scheduler serialises read -> wait -> MFMA).
-constexpr int SPRE = 4;
+constexpr int SPRE = 3;
 
-__device__ __forceinline__ f32x16 s_phase(const WaveAcc& a, const uint8_t* buf, const TileAddr& ad) {
+// at_step(std::integral_constant<int, ks>) runs after the MFMA of k-step ks
+// is issued (the gathers of a later tile are spread over the k-steps this
+// way).  The k-steps are expanded at compile time so that at_step sees a
+// constant.
+template <int KS, typename F>
+__device__ __forceinline__ void s_step(f32x16& acc, bf16x8 (&op)[SPRE], const WaveAcc& a, const uint8_t* buf,
+                                       const TileAddr& ad, F& at_step) {
+  acc = mfma32(op[KS % SPRE], a.qb[KS], acc);
+  if constexpr (KS + SPRE < KSTEPS) op[KS % SPRE] = s_operand(buf, ad, KS + SPRE);
+  at_step(std::integral_constant<int, KS>());
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename F, int... KS>
+__device__ __forceinline__ f32x16 s_steps(const WaveAcc& a, const uint8_t* buf, const TileAddr& ad, F& at_step,
+                                          std::integer_sequence<int, KS...>) {
   f32x16 acc = {};
   bf16x8 op[SPRE];
 #pragma unroll
   for (int j = 0; j < SPRE; ++j) op[j] = s_operand(buf, ad, j);
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    acc = mfma32(op[ks % SPRE], a.qb[ks], acc);
-    if (ks + SPRE < KSTEPS) op[ks % SPRE] = s_operand(buf, ad, ks + SPRE);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  (s_step<KS>(acc, op, a, buf, ad, at_step), ...);
   return acc;
 }
 
-// Softmax numerators of one S^T tile (base 2) against the reference; the
-// first nv keys of the tile are valid.
-__device__ __forceinline__ void softmax_tile(WaveAcc& a, const f32x16& s, int nv, float scale_log2, int h,
-                                             float (&p)[16]) {
-  float tmax = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int key = 8 * (j >> 2) + 4 * h + (j & 3);
-    p[j] = key < nv ? s[j] * scale_log2 : -INFINITY;
-    tmax = fmaxf(tmax, p[j]);
-  }
-  tmax = pair_max(tmax);
-  if (a.m_ref == -INFINITY) a.m_ref = tmax == -INFINITY ? 0.0f : tmax;
-  a.m_max = fmaxf(a.m_max, tmax);
-  float psum = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    p[j] = __builtin_amdgcn_exp2f(p[j] - a.m_ref);
-    psum += p[j];
-  }
-  a.l_run += psum;
+template <typename F>
+__device__ __forceinline__ f32x16 s_phase(const WaveAcc& a, const uint8_t* buf, const TileAddr& ad, F&& at_step) {
+  return s_steps(a, buf, ad, at_step, std::make_integer_sequence<int, KSTEPS>());
 }
+
+struct NoStep {
+  template <int KS>
+  __device__ __forceinline__ void operator()(std::integral_constant<int, KS>) const {}
+};
 
 // true when some head of the workgroup outgrew its reference.  `flags` is
 // one int per wave in LDS that no wave reads or writes at this point.
@@ -243,82 +242,128 @@ __device__ __forceinline__ bool needs_redo(const WaveAcc& a, int* flags, int wav
   return any != 0;
 }
 
-// S of the next tile with the softmax of the current one interleaved.
-__device__ __forceinline__ f32x16 s_phase_softmax(WaveAcc& a, const uint8_t* buf, const TileAddr& ad,
-                                                  const f32x16& s_cur, int nv, float scale_log2, int h,
-                                                  float (&p)[16]) {
-  const f32x16 s_next = s_phase(a, buf, ad);
-  softmax_tile(a, s_cur, nv, scale_log2, h, p);
-  return s_next;
-}
-
-// O^T += V^T . P^T over the 16 dv tiles.  With SPLITP, P = P_hi + P_lo, both
-// bf16: the product runs twice on the same V^T operand, so P carries ~16
-// mantissa bits instead of 8.
-// P^T operand of a tile (k-step kk takes p values 8 kk .. 8 kk + 7); with
+// P^T operand of a tile (k-step kk takes p values 8 kk .. 8 kk + 7).  With
 // SPLITP, P = P_hi + P_lo, both bf16: the product then runs twice on the same
 // V^T operand, so P carries ~16 mantissa bits instead of 8.
 struct POp {
   bf16x8 hi[2], lo[2];
 };
 
+// Softmax numerators of one S^T tile (base 2) against the reference, the
+// first nv keys of the tile valid, in 16 stages: stage st can run after dv
+// tile st of the previous tile's P.V MFMAs, whose shadow then hides the VALU
+// work.  The scale is positive, so the maximum is taken over the raw scores
+// and p = 2^(scale * x - m_ref) is one FMA and one exp2 per key.
+//   0-3    mask invalid keys to -inf, running maximum
+//   4      start the exchange of the maximum with lane ^ 32 (same head)
+//   6      reference (first tile) and running maximum
+//   7-12   p and its sum
+//   13     running sum
+//   14-15  pack P^T (k-steps 0 and 1)
 template <bool SPLITP>
-__device__ __forceinline__ POp pack_p(const float (&pv)[16]) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+struct SoftmaxTile {
+  float x[16];
+  float tmax, other, psum;
   POp op;
+
+  __device__ __forceinline__ explicit SoftmaxTile(const f32x16& s) : tmax(-INFINITY), other(-INFINITY), psum(0.0f) {
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    u32x4 hi, lo;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float p0 = pv[8 * kk + 2 * j], p1 = pv[8 * kk + 2 * j + 1];
-      const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
-      hi[j] = hw;
-      if (SPLITP) {
-        const float h0 = __builtin_bit_cast(float, hw << 16), h1 = __builtin_bit_cast(float, hw & 0xffff0000u);
-        lo[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0 - h0, p1 - h1}, bf16x2));
-      } else {
-        lo[j] = 0u;
-      }
-    }
-    op.hi[kk] = as_bf16x8(hi);
-    op.lo[kk] = as_bf16x8(lo);
+    for (int j = 0; j < 16; ++j) x[j] = s[j];
   }
-  return op;
+
+  template <int ST>
+  __device__ __forceinline__ void stage(WaveAcc& a, int nv, float scale_log2, int h) {
+    if constexpr (ST < 4) {
+#pragma unroll
+      for (int j = 4 * ST; j < 4 * ST + 4; ++j) {
+        const int key = 8 * (j >> 2) + 4 * h + (j & 3);
+        x[j] = key < nv ? x[j] : -INFINITY;
+        tmax = fmaxf(tmax, x[j]);
+      }
+    } else if constexpr (ST == 4) {
+      other = shfl_xor(tmax, 32);
+    } else if constexpr (ST == 6) {
+      const float m = fmaxf(tmax, other) * scale_log2;
+      if (a.m_ref == -INFINITY) a.m_ref = m == -INFINITY ? 0.0f : m;
+      a.m_max = fmaxf(a.m_max, m);
+    } else if constexpr (ST >= 7 && ST < 13) {
+      constexpr int j0 = ST < 11 ? 3 * (ST - 7) : 12 + 2 * (ST - 11);
+      constexpr int j1 = ST < 11 ? j0 + 3 : j0 + 2;
+#pragma unroll
+      for (int j = j0; j < j1; ++j) {
+        x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], scale_log2, -a.m_ref));
+        psum += x[j];
+      }
+    } else if constexpr (ST == 13) {
+      a.l_run += psum;
+    } else if constexpr (ST >= 14) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      constexpr int kk = ST - 14;
+      u32x4 hi, lo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = x[8 * kk + 2 * j], p1 = x[8 * kk + 2 * j + 1];
+        const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+        hi[j] = hw;
+        if (SPLITP) {
+          const float h0 = __builtin_bit_cast(float, hw << 16), h1 = __builtin_bit_cast(float, hw & 0xffff0000u);
+          lo[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0 - h0, p1 - h1}, bf16x2));
+        } else {
+          lo[j] = 0u;
+        }
+      }
+      op.hi[kk] = as_bf16x8(hi);
+      op.lo[kk] = as_bf16x8(lo);
+    }
+  }
+
+  template <int... ST>
+  __device__ __forceinline__ void stages(WaveAcc& a, int nv, float scale_log2, int h,
+                                         std::integer_sequence<int, ST...>) {
+    (stage<ST>(a, nv, scale_log2, h), ...);
+  }
+  // every stage in order (no P.V to hide behind)
+  __device__ __forceinline__ void run_all(WaveAcc& a, int nv, float scale_log2, int h) {
+    stages(a, nv, scale_log2, h, std::make_integer_sequence<int, 16>());
+  }
+};
+
+// O^T += V^T . P^T over the 16 dv tiles.  The operands of dv tile nt + 1 are
+// read while the MFMAs of tile nt run; after them at_step(nt) runs (the
+// softmax stages of the next tile).  The first MFMAs wait one state in case P
+// was just written by VALU instructions.
+template <bool SPLITP, int NT, typename F>
+__device__ __forceinline__ void v_step(WaveAcc& a, const uint8_t* buf, const TileAddr& ad, const POp& op,
+                                       bf16x8 (&v)[2][2], F& at_step) {
+  constexpr int c = NT & 1;
+  if constexpr (NT + 1 < DV_TILES) {
+    v[c ^ 1][0] = v_operand(buf, ad, NT + 1, 0);
+    v[c ^ 1][1] = v_operand(buf, ad, NT + 1, 1);
+  }
+  constexpr bool NOP = NT == 0;
+  mfma32_acc<NOP>(a.o[NT], v[c][0], op.hi[0]);
+  mfma32_acc<NOP>(a.o[NT], v[c][1], op.hi[1]);
+  if (SPLITP) {
+    mfma32_acc<NOP>(a.o[NT], v[c][0], op.lo[0]);
+    mfma32_acc<NOP>(a.o[NT], v[c][1], op.lo[1]);
+  }
+  at_step(std::integral_constant<int, NT>());
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// O^T += V^T . P^T over dv tiles [NT0, NT1).  The operands of dv tile nt + 1
-// are read while the MFMAs of tile nt run.  FIRST: P was just written by VALU
-// instructions (the first MFMAs then wait one state).
-template <bool SPLITP, int NT0, int NT1, bool FIRST>
-__device__ __forceinline__ void v_phase(WaveAcc& a, const uint8_t* buf, const TileAddr& ad, const POp& op) {
-  bf16x8 v0 = v_operand(buf, ad, NT0, 0), v1 = v_operand(buf, ad, NT0, 1);
-#pragma unroll
-  for (int nt = NT0; nt < NT1; ++nt) {
-    bf16x8 n0 = v0, n1 = v1;
-    if (nt + 1 < NT1) {
-      n0 = v_operand(buf, ad, nt + 1, 0);
-      n1 = v_operand(buf, ad, nt + 1, 1);
-    }
-    if (FIRST && nt == NT0) {
-      mfma32_acc<true>(a.o[nt], v0, op.hi[0]);
-      mfma32_acc<true>(a.o[nt], v1, op.hi[1]);
-      if (SPLITP) {
-        mfma32_acc<true>(a.o[nt], v0, op.lo[0]);
-        mfma32_acc<true>(a.o[nt], v1, op.lo[1]);
-      }
-    } else {
-      mfma32_acc<false>(a.o[nt], v0, op.hi[0]);
-      mfma32_acc<false>(a.o[nt], v1, op.hi[1]);
-      if (SPLITP) {
-        mfma32_acc<false>(a.o[nt], v0, op.lo[0]);
-        mfma32_acc<false>(a.o[nt], v1, op.lo[1]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    v0 = n0;
-    v1 = n1;
-  }
+template <bool SPLITP, typename F, int... NT>
+__device__ __forceinline__ void v_steps(WaveAcc& a, const uint8_t* buf, const TileAddr& ad, const POp& op,
+                                        F& at_step, std::integer_sequence<int, NT...>) {
+  bf16x8 v[2][2];
+  v[0][0] = v_operand(buf, ad, 0, 0);
+  v[0][1] = v_operand(buf, ad, 0, 1);
+  (v_step<SPLITP, NT>(a, buf, ad, op, v, at_step), ...);
+}
+
+template <bool SPLITP, typename F>
+__device__ __forceinline__ void v_phase(WaveAcc& a, const uint8_t* buf, const TileAddr& ad, const POp& op,
+                                        F&& at_step) {
+  v_steps<SPLITP>(a, buf, ad, op, at_step, std::make_integer_sequence<int, DV_TILES>());
 }
 
 // Normalise and store the wave's O^T (and lse) for its 32 heads.
@@ -426,31 +471,59 @@ struct Bf16Rows {
   static constexpr int LOADS = INSTR / NW;
   static_assert(INSTR % NW == 0, "gathers must split evenly over the waves");
 
-  // The wave's rows are wave-uniform: each gather takes its row from LDS
-  // into a scalar register and addresses the row with an SGPR base, so only
-  // the lane's chunk offset lives in a VGPR.
+  // The gathers of a tile as 4 blocks of 9 instructions: 8 latent rows, then
+  // the rope parts of those 8 rows.  Lane j (mod 32) reads the cache row of
+  // tile row j once (prepare); a latent-row gather takes its row from that
+  // register into a scalar register (v_readlane) and addresses the row with
+  // an SGPR base, so only the lane's chunk offset lives in a VGPR; a rope
+  // gather takes its per-lane rows through the LDS crossbar.
+  struct Tile {
+    int rowv;
+    uint32_t buf;
+  };
+  __device__ __forceinline__ static Tile prepare(const int* rows, uint32_t buf, int lane) {
+    return Tile{rows[lane & (TILE - 1)], buf};
+  }
+  // instruction i = 9 b + m of the tile (wave-uniform)
+  template <int M>
+  __device__ __forceinline__ static void issue_one(const AttnParams& p, const Tile& t, int b, int lane) {
+    if constexpr (M < 8) {
+      const int r = 8 * b + M;
+      const int row = __builtin_amdgcn_readlane(t.rowv, r);
+      dma16_s(p.kv + (int64_t)row * (ROW * 2), (uint32_t)((lane ^ lat_swz(r)) << 4), t.buf + r * LAT_STRIDE);
+    } else {
+      const int r = 8 * b + (lane >> 3);
+      const int row = __builtin_amdgcn_ds_bpermute(r << 2, t.rowv);
+      dma16(p.kv + (int64_t)row * (ROW * 2) + LATENT * 2 + (((lane & 7) ^ rope_swz(r)) << 4),
+            t.buf + LAT_TILE_BYTES + b * 1024);
+    }
+  }
+  // every gather of this wave for one tile: instructions wave * LOADS + j
   __device__ __forceinline__ static void issue(const AttnParams& p, const int* rows, uint32_t buf, int wave,
                                                int lane) {
-    int rv[LOADS];
+    const Tile t = prepare(rows, buf, lane);
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int i = wave * LOADS + j;
-      rv[j] = rows[i < TILE ? i : (i - TILE) * 8];  // rope: first row of the instruction (unused)
-    }
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      const int i = wave * LOADS + j;  // wave-uniform
-      if (i < TILE) {
-        const int r = i;
-        const int row = __builtin_amdgcn_readfirstlane(rv[j]);
-        dma16_s(p.kv + (int64_t)row * (ROW * 2), (uint32_t)((lane ^ lat_swz(r)) << 4), buf + r * LAT_STRIDE);
+      const int b = i / 9, m = i - 9 * b;
+      if (m < 8) {
+        const int r = 8 * b + m;
+        const int row = __builtin_amdgcn_readlane(t.rowv, r);
+        dma16_s(p.kv + (int64_t)row * (ROW * 2), (uint32_t)((lane ^ lat_swz(r)) << 4), t.buf + r * LAT_STRIDE);
       } else {
-        const int r = (i - TILE) * 8 + (lane >> 3);
-        const int row = rows[r];
-        dma16(p.kv + (int64_t)row * (ROW * 2) + LATENT * 2 + (((lane & 7) ^ rope_swz(r)) << 4),
-              buf + LAT_TILE_BYTES + (i - TILE) * 1024);
+        issue_one<8>(p, t, b, lane);
       }
     }
+  }
+  // With one block per wave (4 waves), the gathers of this wave
+  // can be spread over the k-steps of an S phase: the j-th goes out after
+  // k-step (j * KSTEPS) / LOADS, so the wave never stalls behind a full memory
+  // queue while its MFMAs wait.
+  static constexpr bool SPREAD = LOADS == 9;
+  template <int KS>
+  __device__ __forceinline__ static void issue_at_step(const AttnParams& p, const Tile& t, int wave, int lane) {
+    constexpr int J = KS * LOADS / KSTEPS;  // KSTEPS = 4 LOADS
+    if constexpr (KS % (KSTEPS / LOADS) == 0) issue_one<J>(p, t, wave, lane);
   }
 };
 
@@ -499,7 +572,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF_BYTES];
   __shared__ int rows_sh[MAXE];
   // per-wave scratch ints in the last ring slot: it is first filled by the
-  // gather issued in iteration 0, after every use of the scratch
+  // gathers of tile NBUF - 1, issued in the loop after every use of the scratch
   int* wsum = (int*)(smem + (NBUF - 1) * BUF_BYTES);
   typedef Bf16Rows<NW> R;
   const int tid = threadIdx.x;
@@ -524,28 +597,49 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
   float m_ref = -INFINITY;
   for (int attempt = 0; attempt < 2; ++attempt) {
     reset_acc(a, m_ref);
-#pragma unroll
-    for (int k = 0; k < NBUF - 1; ++k)
+    for (int k = 0; k < NBUF - 2; ++k)
       if (k < ntiles) R::issue(p, rows_sh + k * TILE, smem_base + k * BUF_BYTES, wave, lane);
     // queries and the first tiles landed: no compiler-inserted waits in the loop
     wait_vmcnt<0>();
-    // Iteration k: wait for this wave's gathers of tile k (later tiles stay
+    // Iteration k: wait for this wave's gathers of tile k (tile k + 1 stays
     // in flight), one barrier (tile k visible to every wave; ring slot
-    // (k - 1) % NBUF free again), issue tile k + NBUF - 1, compute tile k.
-    for (int k = 0; k < ntiles; ++k) {
-      const int later = min(NBUF - 2, ntiles - 1 - k);
-      if (later >= 2) wait_vmcnt<2 * R::LOADS>();
-      else if (later == 1) wait_vmcnt<R::LOADS>();
+    // (k + 2) % NBUF, last read by P.V of tile k - 2, free again), S of tile
+    // k with the gathers of tile k + 2 spread over its k-steps, then P.V of
+    // tile k - 1 with the softmax of tile k in the shadow of its MFMAs.
+    // Iteration 0 (no P.V before it) is peeled: a branch around the P.V
+    // inside the loop makes the compiler shuffle the AGPR-resident O^T.
+    auto s_of_tile = [&](int k) {
+      if (k + 1 < ntiles) wait_vmcnt<R::LOADS>();
       else wait_vmcnt<0>();
       __syncthreads();
-      if (k + NBUF - 1 < ntiles)
-        R::issue(p, rows_sh + (k + NBUF - 1) * TILE, smem_base + ((k + NBUF - 1) % NBUF) * BUF_BYTES, wave, lane);
+      const bool more = k + NBUF - 2 < ntiles;  // uniform
+      const int slot_next = (k + NBUF - 2) % NBUF;
       const uint8_t* buf = smem + (k % NBUF) * BUF_BYTES;
-      const f32x16 s = s_phase(a, buf, ad);
-      float pv[16];
-      softmax_tile(a, s, min(TILE, n - k * TILE), p.scale_log2, h, pv);
-      v_phase<SPLITP, 0, DV_TILES, true>(a, buf, ad, pack_p<SPLITP>(pv));
+      if (R::SPREAD && more) {
+        const typename R::Tile nt = R::prepare(rows_sh + (k + NBUF - 2) * TILE, smem_base + slot_next * BUF_BYTES, lane);
+        return s_phase(a, buf, ad, [&](auto ks) { R::template issue_at_step<decltype(ks)::value>(p, nt, wave, lane); });
+      }
+      if (more) R::issue(p, rows_sh + (k + NBUF - 2) * TILE, smem_base + slot_next * BUF_BYTES, wave, lane);
+      return s_phase(a, buf, ad, NoStep());
+    };
+    POp op_prev;
+    if (ntiles > 0) {
+      SoftmaxTile<SPLITP> sm(s_of_tile(0));
+      sm.run_all(a, min(TILE, n), p.scale_log2, h);
+      op_prev = sm.op;
     }
+    // Nothing the compiler tracks may be in flight when the loop starts (a
+    // spill reload still pending here would make it wait for every gather in
+    // every iteration); this waits once for the gathers of tile 2.
+    wait_vmcnt<0>();
+    for (int k = 1; k < ntiles; ++k) {
+      SoftmaxTile<SPLITP> sm(s_of_tile(k));
+      const int nv = min(TILE, n - k * TILE);
+      v_phase<SPLITP>(a, smem + ((k - 1) % NBUF) * BUF_BYTES, ad, op_prev,
+                      [&](auto st) { sm.template stage<decltype(st)::value>(a, nv, p.scale_log2, h); });
+      op_prev = sm.op;
+    }
+    if (ntiles > 0) v_phase<SPLITP>(a, smem + ((ntiles - 1) % NBUF) * BUF_BYTES, ad, op_prev, NoStep());
     o_fence(a);
     if (!needs_redo<NW>(a, wsum, wave, lane)) break;
     m_ref = a.m_max;
@@ -605,10 +699,10 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
       uint8_t* buf = smem + (k & 1) * BUF_BYTES;
       R::convert(raw + (k % NRAW) * RAW_TILE_BYTES, buf, tid);
       __syncthreads();
-      const f32x16 s = s_phase(a, buf, ad);
-      float pv[16];
-      softmax_tile(a, s, min(TILE, n - k * TILE), p.scale_log2, h, pv);
-      v_phase<false, 0, DV_TILES, true>(a, buf, ad, pack_p<false>(pv));
+      const f32x16 s = s_phase(a, buf, ad, NoStep());
+      SoftmaxTile<false> sm(s);
+      sm.run_all(a, min(TILE, n - k * TILE), p.scale_log2, h);
+      v_phase<false>(a, buf, ad, sm.op, NoStep());
     }
     o_fence(a);
     if (!needs_redo<NW>(a, wsum, wave, lane)) break;
@@ -618,8 +712,17 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
 }
 
 // Merge split partials: lse = log sum_s exp(lse_s); O = sum_s exp(lse_s - lse) O_s.
-__global__ __launch_bounds__(128) void combine_kernel(AttnParams p) {
-  const int th = blockIdx.x;
+// One workgroup per (token, pair of heads), 128 lanes per head, each lane 4
+// of the 512 values.  The partials of COMBINE_BATCH splits are loaded before
+// any is used (one memory latency per batch, not per split); a split whose
+// weight is zero (no valid entry) contributes nothing even if its values are
+// not finite.
+constexpr int COMBINE_BATCH = 4;
+
+__global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
+  const int th = blockIdx.x * 2 + (threadIdx.x >> 7);
+  if (th >= p.sv.num_tokens * p.H) return;
+  const int lane = threadIdx.x & 127;
   const int tok = th / p.H, h = th % p.H;
   const int S = p.num_splits;
   const int64_t base = (int64_t)tok * S * p.H + h;
@@ -628,19 +731,27 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnParams p) {
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float wsum = 0.0f;
   if (mx != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const int64_t pi = base + (int64_t)s * p.H;
-      const float wgt = expf(p.part_lse[pi] - mx);
-      if (wgt > 0.0f) {
-        wsum += wgt;
-        acc += wgt * *(const f32x4*)(p.part_o + pi * LATENT + threadIdx.x * 4);
+    for (int s0 = 0; s0 < S; s0 += COMBINE_BATCH) {
+      f32x4 v[COMBINE_BATCH];
+      float wgt[COMBINE_BATCH];
+#pragma unroll
+      for (int j = 0; j < COMBINE_BATCH; ++j) {
+        const int64_t pi = base + (int64_t)min(s0 + j, S - 1) * p.H;
+        v[j] = *(const f32x4*)(p.part_o + pi * LATENT + lane * 4);
+        wgt[j] = s0 + j < S ? expf(p.part_lse[pi] - mx) : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < COMBINE_BATCH; ++j) {
+        if (wgt[j] > 0.0f) {
+          wsum += wgt[j];
+          acc += wgt[j] * v[j];
+        }
       }
     }
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  *(f32x4*)(p.out + ((int64_t)tok * p.H + h) * LATENT + threadIdx.x * 4) = acc * inv;
-  if (threadIdx.x == 0 && p.lse)
-    p.lse[(int64_t)tok * p.H + h] = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
+  *(f32x4*)(p.out + ((int64_t)tok * p.H + h) * LATENT + lane * 4) = acc * inv;
+  if (lane == 0 && p.lse) p.lse[(int64_t)tok * p.H + h] = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
 }
 
 template <typename K>
@@ -678,7 +789,7 @@ hipError_t launch_attn(const AttnParams& p, bool kv_fp8, hipStream_t stream) {
   timer_after(2, stream);
   if (e != hipSuccess || p.num_splits == 1) return e;
   timer_before(3, stream);
-  hipLaunchKernelGGL(combine_kernel, dim3(p.sv.num_tokens * p.H), dim3(128), 0, stream, p);
+  hipLaunchKernelGGL(combine_kernel, dim3(cdiv(p.sv.num_tokens * p.H, 2)), dim3(256), 0, stream, p);
   e = hipGetLastError();
   timer_after(3, stream);
   return e;

@@ -116,6 +116,7 @@ def test_bad_batches_rejected(L, skw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(kv=None), -1), (dict(idx=None), -1), (dict(out=None), -1),
     (dict(out=MIS), -1), (dict(H=0), -1), (dict(K=0), -1), (dict(scale=float("nan")), -1),
+    (dict(scale=0.0), -1), (dict(scale=-0.5), -1), (dict(scale=float("inf")), -1),
     (dict(H=129), -2), (dict(kvdt=2), -2), (dict(K=4096), -2),
     (dict(ws=None), -3), (dict(wsb=100), -3),
 ])
