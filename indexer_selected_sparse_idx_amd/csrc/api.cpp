@@ -98,8 +98,14 @@ int check_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, int k
 size_t score_rows_bytes(const idx_seqs* s) {
   return align_up((size_t)std::max(s->num_tokens, 0) * (size_t)score_stride(s) * sizeof(float));
 }
+size_t score_hist_bytes(const idx_seqs* s) {
+  return align_up((size_t)std::max(s->num_tokens, 0) * SCORE_HIST_BINS * sizeof(uint32_t));
+}
+int topk_nch(const idx_seqs* s) { return std::max(1, (s->max_ctx_len + TOPK_CHUNK - 1) / TOPK_CHUNK); }
+size_t topk_rows_bytes(const idx_seqs* s) { return align_up((size_t)std::max(s->num_tokens, 0) * sizeof(TopkRow)); }
 size_t score_ws_bytes(const idx_seqs* s) {
-  return score_rows_bytes(s) + align_up((size_t)std::max(s->num_tokens, 0) * SCORE_HIST_BINS * sizeof(uint32_t));
+  return score_rows_bytes(s) + score_hist_bytes(s) + topk_rows_bytes(s) +
+         align_up((size_t)std::max(s->num_tokens, 0) * topk_nch(s) * 2 * sizeof(uint32_t));
 }
 
 size_t attn_ws_bytes(const idx_seqs* s, int H, int top_k) {
@@ -126,13 +132,20 @@ int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int 
   sp.d_I = d_I;
   sp.scores = static_cast<float*>(ws);
   sp.score_stride = score_stride(seqs);
-  sp.hist = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + score_rows_bytes(seqs));
+  uint8_t* const base = static_cast<uint8_t*>(ws);
+  const size_t hist_off = score_rows_bytes(seqs);
+  const size_t rows_off = hist_off + score_hist_bytes(seqs);
+  const size_t cnt_off = rows_off + topk_rows_bytes(seqs);
+  sp.hist = reinterpret_cast<uint32_t*>(base + hist_off);
   if (launch_score(sp, k_dtype == IDX_E4M3, stream) != hipSuccess) return IDX_ERR_HIP;
   TopkParams tp;
   tp.sv = sp.sv;
   tp.scores = sp.scores;
   tp.score_stride = sp.score_stride;
   tp.hist = sp.hist;
+  tp.rows = reinterpret_cast<TopkRow*>(base + rows_off);
+  tp.chunk_cnt = reinterpret_cast<uint32_t*>(base + cnt_off);
+  tp.nch_stride = topk_nch(seqs);
   tp.top_k = top_k;
   tp.out_idx = out_idx;
   if (launch_topk(tp, stream) != hipSuccess) return IDX_ERR_HIP;

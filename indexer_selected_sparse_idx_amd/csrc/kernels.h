@@ -53,14 +53,25 @@ struct ScoreParams {
   uint32_t* hist;          // [T, SCORE_HIST_BINS] histogram of the top key bits (zeroed by the launcher)
 };
 
+// Per-row threshold record of the selection (see topk.hip).
+struct TopkRow {
+  uint32_t mode, d1, above1, cnt1;
+};
+
 struct TopkParams {
   SeqView sv;
-  const float* scores;
+  float* scores;           // [T, score_stride]; the selection reuses each row's storage
   int64_t score_stride;
   const uint32_t* hist;    // [T, SCORE_HIST_BINS] from the score kernel
+  TopkRow* rows;           // [T]
+  uint32_t* chunk_cnt;     // [T, nch_stride, 2]
+  int nch_stride;          // ceil(max_ctx_len / TOPK_CHUNK)
   int top_k;
   int32_t* out_idx;        // [T, top_k]
 };
+
+// Keys per workgroup of the selection's compaction pass.
+constexpr int TOPK_CHUNK = 2048;
 
 // The score kernel histograms the top SCORE_HIST_BITS bits of every score's
 // order-preserving key per row; the selection kernel starts from it.

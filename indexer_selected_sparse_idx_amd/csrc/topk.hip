@@ -7,19 +7,16 @@
 // Inference Support for New LLM Architectures; the in-place index selection
 // of its fused indexer sketch; the tie rule is this library's reading).
 //
-// One workgroup (16 waves) per row:
-// 1. The score kernel has already histogrammed the top 11 bits of every key
-//    of the row.  A block-wide suffix scan of that histogram gives the bucket
-//    d1 holding the m-th largest key, the count above it and its size.
-// 2. One ordered streaming pass over the fp32 score row (4 keys per lane per
-//    access): keys in buckets above d1 are emitted directly; keys in d1 are
-//    appended, with their positions, to an LDS candidate list, in position
-//    order (wavefront prefix sums over per-lane counts, one barrier per 4096
-//    keys).
-// 3. The candidates (a few thousand at most for smooth score distributions)
-//    go through the radix select below; when d1 holds more than the LDS
-//    capacity (massive ties) the whole row goes through it instead, read from
-//    the score row.
+// The score kernel has already histogrammed the top 11 bits of every key of
+// the row, so the bucket d1 holding the m-th largest key is known before the
+// row is read again.  Three launches then select (details below, above the
+// kernels): a per-row threshold, a compaction pass that many workgroups run
+// over chunks of every row (keys above d1 are taken, keys in d1 kept as
+// candidates, both in position order), and one workgroup per row that
+// gathers them and runs the radix select over the candidates (a few thousand
+// at most for smooth score distributions); when d1 holds more than the LDS
+// capacity (massive ties) the radix select runs over the whole score row.
+//
 // Radix select over a key list:
 // a. Up to four 8-bit digit passes, most significant first, histogram the
 //    keys that share the digits chosen so far.  Every wave owns a private
@@ -244,128 +241,214 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
   }
 }
 
-__global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(TopkParams p) {
-  __shared__ __attribute__((aligned(16))) uint32_t cand_key[CAP];
-  __shared__ __attribute__((aligned(16))) int32_t cand_pos[CAP];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t whist[TOPK_WAVES * 256];
-  __shared__ uint32_t wcnt[2 * TOPK_WAVES];
-  __shared__ uint32_t wtot[2][TOPK_WAVES][2];
-  __shared__ uint32_t sh_d1, sh_above1, sh_cnt1;
+// ---------------------------------------------------------------------------
+// The selection as three launches.
+//   thresh  one wave per row: from the row histogram, the bucket d1 holding
+//           the m-th largest key, the count above it and its size.
+//   emit    one workgroup per (row, TOPK_CHUNK keys): the chunk's keys above
+//           d1 and in d1 are compacted, in position order, into the chunk's
+//           own part of the score row (just read, and read by no one else):
+//           first the positions above d1, then the d1 keys packed as
+//           (low 21 key bits << 11) | (offset in the chunk); the two counts
+//           go to a per-chunk table.
+//   select  one workgroup per row: the positions above d1 go to the output,
+//           chunk after chunk; the d1 keys go into LDS in position order and
+//           the radix select above takes the remaining m - above1 of them.
+// Rows with t + 1 <= K take every position.  Rows whose d1 bucket exceeds the
+// LDS capacity (massive ties), or with more chunks than the select tracks,
+// are left alone by emit and select over the whole score row.
+// ---------------------------------------------------------------------------
+constexpr int TKE_THREADS = 256;                     // 8 keys per thread
+constexpr int TKE_WAVES = TKE_THREADS / WAVE;
+constexpr int TK_MAXCH = 512;                        // chunks per row the select tracks
+constexpr uint32_t TK_PARTIAL = 0, TK_ALL = 1, TK_WHOLE_ROW = 2;
+static_assert(TOPK_CHUNK == 2048 && TOPK_CHUNK == 8 * TKE_THREADS, "11-bit chunk offsets, 8 keys per thread");
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const SeqView& sv = p.sv;
-  const int tok = blockIdx.x;
+// t + 1 for the query token `tok`
+__device__ __forceinline__ int row_len(const SeqView& sv, int tok) {
   const int b = seq_of_token(sv, tok);
-  const int ql = q_len(sv, b);
-  const int t = sv.ctx_len[b] - ql + (tok - first_token(sv, b));
-  const int n = t + 1;
-  const int K = p.top_k;
-  const int m = min(K, n);
-  const float* row = p.scores + (int64_t)tok * p.score_stride;
-  int32_t* out = p.out_idx + (int64_t)tok * K;
+  return sv.ctx_len[b] - q_len(sv, b) + (tok - first_token(sv, b)) + 1;
+}
 
-  for (int i = m + tid; i < K; i += TOPK_THREADS) out[i] = -1;
-  if (m == n) {
-    for (int i = tid; i < n; i += TOPK_THREADS) out[i] = i;
-    return;
-  }
-
-  // ---- 1. the bucket of the m-th largest key, from the row histogram ----------
-  {
-    const uint32_t* gh = p.hist + (int64_t)tok * SCORE_HIST_BINS;
-    const uint32_t h0 = gh[2 * tid], h1 = gh[2 * tid + 1];
-    uint32_t suf = h0 + h1;  // suffix over this wave's lanes >= lane
+__global__ __launch_bounds__(256) void topk_thresh_kernel(TopkParams p) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= p.sv.num_tokens) return;
+  const int n = row_len(p.sv, tok);
+  const uint32_t m = (uint32_t)min(p.top_k, n);
+  TopkRow r = {TK_ALL, 0u, 0u, 0u};
+  if (m < (uint32_t)n) {
+    // lane L holds bins 32 L .. 32 L + 31
+    const u32x4* gh = (const u32x4*)(p.hist + (int64_t)tok * SCORE_HIST_BINS + 32 * lane);
+    uint32_t h[32];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 v = gh[j];
+      h[4 * j] = v[0]; h[4 * j + 1] = v[1]; h[4 * j + 2] = v[2]; h[4 * j + 3] = v[3];
+    }
+    uint32_t tot = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) tot += h[j];
+    uint32_t suf = tot;  // keys in the bins of lanes >= L
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const uint32_t o = __shfl_down(suf, off);
       if (lane + off < 64) suf += o;
     }
-    if (lane == 0) wcnt[wave] = suf;
-    __syncthreads();
-    uint32_t above_waves = 0;
-    for (int w = wave + 1; w < TOPK_WAVES; ++w) above_waves += wcnt[w];
-    const uint32_t s0 = suf + above_waves;  // keys in bins >= 2 tid
-    const uint32_t s1 = s0 - h0, s2 = s1 - h1;
-    const uint32_t um = (uint32_t)m;
-    if (s1 >= um && s2 < um) { sh_d1 = 2 * tid + 1; sh_above1 = s2; sh_cnt1 = h1; }
-    else if (s0 >= um && s1 < um) { sh_d1 = 2 * tid; sh_above1 = s1; sh_cnt1 = h0; }
-    __syncthreads();
+    uint32_t run = suf - tot;  // keys in the bins above this lane's
+    uint32_t d1 = 0, above1 = 0, cnt1 = 0;
+    bool found = false;
+#pragma unroll
+    for (int j = 31; j >= 0; --j) {
+      if (run < m && run + h[j] >= m) {
+        found = true;
+        d1 = 32 * lane + j;
+        above1 = run;
+        cnt1 = h[j];
+      }
+      run += h[j];
+    }
+    const uint64_t fm = __builtin_amdgcn_ballot_w64(found);
+    if (fm == 0) {
+      r.mode = TK_WHOLE_ROW;  // (a histogram that does not add up to the row: select from the scores)
+    } else {
+      const int src = __builtin_ctzll(fm);
+      r.d1 = __builtin_amdgcn_readlane(d1, src);
+      r.above1 = __builtin_amdgcn_readlane(above1, src);
+      r.cnt1 = __builtin_amdgcn_readlane(cnt1, src);
+      r.mode = (r.cnt1 > (uint32_t)CAP || cdiv(n, TOPK_CHUNK) > TK_MAXCH) ? TK_WHOLE_ROW : TK_PARTIAL;
+    }
   }
-  const uint32_t d1 = sh_d1, above1 = sh_above1, cnt1 = sh_cnt1;
-  if (cnt1 > (uint32_t)CAP) {  // massive ties: select over the whole row
+  if (lane == 0) p.rows[tok] = r;
+}
+
+__global__ __launch_bounds__(TKE_THREADS) void topk_emit_kernel(TopkParams p) {
+  __shared__ uint32_t wt[2][TKE_WAVES];
+  const int tok = blockIdx.x, chunk = blockIdx.y;
+  const TopkRow r = p.rows[tok];
+  if (r.mode != TK_PARTIAL) return;
+  const int n = row_len(p.sv, tok);
+  const int c0 = chunk * TOPK_CHUNK;
+  if (c0 >= n) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* row = p.scores + (int64_t)tok * p.score_stride;
+  const Keys<false> src{nullptr, row, n};
+  const int i = c0 + 8 * tid;
+  const u32x4 k0 = i < n ? src.get4(i) : u32x4{0u, 0u, 0u, 0u};
+  const u32x4 k1 = i + 4 < n ? src.get4(i + 4) : u32x4{0u, 0u, 0u, 0u};
+  const uint32_t key[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+  uint32_t fg = 0, fe = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t top = key[e] >> (32 - SCORE_HIST_BITS);
+    const bool valid = i + e < n;
+    fg |= (uint32_t)(valid && top > r.d1) << e;
+    fe |= (uint32_t)(valid && top == r.d1) << e;
+  }
+  const uint32_t ng = __popc(fg), ne = __popc(fe);
+  const uint32_t sg = wave_incl_scan(ng, lane), se = wave_incl_scan(ne, lane);
+  if (lane == 63) { wt[0][wave] = sg; wt[1][wave] = se; }
+  __syncthreads();  // every key of the chunk has been read: its storage is free
+  uint32_t og = sg - ng, oe = se - ne, tg = 0, te = 0;
+#pragma unroll
+  for (int w = 0; w < TKE_WAVES; ++w) {
+    const uint32_t a = wt[0][w], c = wt[1][w];
+    if (w < wave) { og += a; oe += c; }
+    tg += a;
+    te += c;
+  }
+  uint32_t* seg = (uint32_t*)(row + c0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if ((fg >> e) & 1u) seg[og++] = (uint32_t)(i + e);
+    if ((fe >> e) & 1u) seg[tg + oe++] = ((key[e] & ((1u << (32 - SCORE_HIST_BITS)) - 1u)) << 11) | (uint32_t)(i + e - c0);
+  }
+  if (tid == 0) {
+    uint32_t* cc = p.chunk_cnt + ((int64_t)tok * p.nch_stride + chunk) * 2;
+    cc[0] = tg;
+    cc[1] = te;
+  }
+}
+
+__global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkParams p) {
+  __shared__ __attribute__((aligned(16))) uint32_t cand_key[CAP];
+  __shared__ __attribute__((aligned(16))) int32_t cand_pos[CAP];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t whist[TOPK_WAVES * 256];
+  __shared__ uint32_t wcnt[2 * TOPK_WAVES];
+  __shared__ uint32_t choff[2][TK_MAXCH], chcnt[2][TK_MAXCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int tok = blockIdx.x;
+  const int n = row_len(p.sv, tok);
+  const int K = p.top_k;
+  const int m = min(K, n);
+  const float* row = p.scores + (int64_t)tok * p.score_stride;
+  int32_t* out = p.out_idx + (int64_t)tok * K;
+  for (int i = m + tid; i < K; i += TOPK_THREADS) out[i] = -1;
+  const TopkRow r = p.rows[tok];
+  if (r.mode == TK_ALL) {
+    for (int i = tid; i < n; i += TOPK_THREADS) out[i] = i;
+    return;
+  }
+  if (r.mode == TK_WHOLE_ROW) {
     select_row<false, 0>(Keys<false>{nullptr, row, n}, n, m, out, nullptr, hist, whist, wcnt, 0u);
     return;
   }
 
-  // ---- 2. ordered extraction: above d1 -> output, in d1 -> candidates ------------
-  const Keys<false> src{nullptr, row, n};
-  const int n4 = (n + 3) / 4 * 4;
-  uint32_t base_g = 0, base_c = 0;
-  int par = 0;
-  constexpr int CHUNK = 4 * TOPK_THREADS;
-  for (int s0 = 0; s0 < n4; s0 += CHUNK * UNROLL) {
-    u32x4 kk[UNROLL];
+  // chunk offsets: exclusive prefix sums of the per-chunk counts (wave 0,
+  // lane L owns chunks 8 L .. 8 L + 7)
+  const int nch = cdiv(n, TOPK_CHUNK);
+  if (wave == 0) {
+    const uint32_t* cc = p.chunk_cnt + (int64_t)tok * p.nch_stride * 2;
+    uint32_t g[8], e[8], tg = 0, te = 0;
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int i = s0 + u * CHUNK + 4 * tid;
-      kk[u] = i < n4 ? src.get4(i) : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 8; ++j) {
+      const int c = 8 * lane + j;
+      g[j] = c < nch ? cc[2 * c] : 0u;
+      e[j] = c < nch ? cc[2 * c + 1] : 0u;
+      tg += g[j];
+      te += e[j];
     }
+    uint32_t og = wave_incl_scan(tg, lane) - tg, oe = wave_incl_scan(te, lane) - te;
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int c0 = s0 + u * CHUNK;
-      if (c0 >= n4) break;  // uniform
-      const int i = c0 + 4 * tid;
-      uint32_t fg = 0, fc = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t top = kk[u][e] >> (32 - SCORE_HIST_BITS);
-        const bool valid = i + e < n;
-        fg |= (uint32_t)(valid && top > d1) << e;
-        fc |= (uint32_t)(valid && top == d1) << e;
+    for (int j = 0; j < 8; ++j) {
+      const int c = 8 * lane + j;
+      if (c < nch) {
+        choff[0][c] = og; choff[1][c] = oe;
+        chcnt[0][c] = g[j]; chcnt[1][c] = e[j];
       }
-      const uint32_t ng = __popc(fg), nc = __popc(fc);
-      const uint32_t sg = wave_incl_scan(ng, lane), sc = wave_incl_scan(nc, lane);
-      if (lane == 63) { wtot[par][wave][0] = sg; wtot[par][wave][1] = sc; }
-      __syncthreads();
-      uint32_t og = base_g + sg - ng, oc = base_c + sc - nc, tg = 0, tc = 0;
-#pragma unroll
-      for (int w = 0; w < TOPK_WAVES; ++w) {
-        const uint32_t a = wtot[par][w][0], c = wtot[par][w][1];
-        if (w < wave) { og += a; oc += c; }
-        tg += a;
-        tc += c;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((fg >> e) & 1u) {
-          if (og < above1) out[og] = i + e;
-          ++og;
-        }
-        if ((fc >> e) & 1u) {
-          if (oc < (uint32_t)CAP) { cand_key[oc] = kk[u][e]; cand_pos[oc] = i + e; }
-          ++oc;
-        }
-      }
-      base_g += tg;
-      base_c += tc;
-      par ^= 1;
+      og += g[j];
+      oe += e[j];
     }
   }
   __syncthreads();
-
-  // ---- 3. the remaining m - above1 positions come from the candidates -------------
-  select_row<true, SCORE_HIST_BITS>(Keys<true>{cand_key, nullptr, (int)cnt1}, (int)cnt1, m - (int)above1,
-                                    out + above1, cand_pos, hist, whist, wcnt, d1);
+  // positions above d1 to the output; d1 keys to LDS, both in chunk order
+  for (int c = wave; c < nch; c += TOPK_WAVES) {
+    const uint32_t* seg = (const uint32_t*)(row + (int64_t)c * TOPK_CHUNK);
+    const uint32_t ng = chcnt[0][c], ne = chcnt[1][c], og = choff[0][c], oe = choff[1][c];
+    for (uint32_t j = lane; j < ng; j += WAVE) out[og + j] = (int32_t)seg[j];
+    for (uint32_t j = lane; j < ne; j += WAVE) {
+      const uint32_t w = seg[ng + j];
+      cand_key[oe + j] = (r.d1 << (32 - SCORE_HIST_BITS)) | (w >> 11);
+      cand_pos[oe + j] = c * TOPK_CHUNK + (int32_t)(w & (TOPK_CHUNK - 1));
+    }
+  }
+  __syncthreads();
+  select_row<true, SCORE_HIST_BITS>(Keys<true>{cand_key, nullptr, (int)r.cnt1}, (int)r.cnt1, m - (int)r.above1,
+                                    out + r.above1, cand_pos, hist, whist, wcnt, r.d1);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
+  const int T = p.sv.num_tokens;
   timer_before(1, stream);
-  hipLaunchKernelGGL(topk_kernel, dim3(p.sv.num_tokens), dim3(TOPK_THREADS), 0, stream, p);
+  hipLaunchKernelGGL(topk_thresh_kernel, dim3(cdiv(T, 4)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(topk_emit_kernel, dim3(T, p.nch_stride), dim3(TKE_THREADS), 0, stream, p);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(T), dim3(TOPK_THREADS), 0, stream, p);
   hipError_t e = hipGetLastError();
   timer_after(1, stream);
   return e;
