@@ -137,7 +137,10 @@ int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int 
   const size_t rows_off = hist_off + score_hist_bytes(seqs);
   const size_t cnt_off = rows_off + topk_rows_bytes(seqs);
   sp.hist = reinterpret_cast<uint32_t*>(base + hist_off);
+  sp.top_k = top_k;
+  sp.out_idx = out_idx;
   if (launch_score(sp, k_dtype == IDX_E4M3, stream) != hipSuccess) return IDX_ERR_HIP;
+  if (score_selects(sp.sv)) return IDX_OK;
   TopkParams tp;
   tp.sv = sp.sv;
   tp.scores = sp.scores;

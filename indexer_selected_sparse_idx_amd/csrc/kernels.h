@@ -51,6 +51,8 @@ struct ScoreParams {
   float* scores;           // [T, score_stride]
   int64_t score_stride;
   uint32_t* hist;          // [T, SCORE_HIST_BINS] histogram of the top key bits (zeroed by the launcher)
+  int top_k;
+  int32_t* out_idx;        // [T, top_k]: written by the prefill kernel, which also selects
 };
 
 // Per-row threshold record of the selection (see topk.hip).
@@ -97,6 +99,8 @@ struct AttnParams {
 // Kernel launchers (asynchronous, on `stream`).  Each records the armed
 // timing events of its kernel, if any.
 hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream);
+// true when launch_score also runs the Top-K selection (out_idx is then final)
+bool score_selects(const SeqView& sv);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool kv_fp8, hipStream_t stream);
 

@@ -199,8 +199,9 @@ __global__ void zero_kernel(uint32_t* p, int64_t n4) {
 // groups (4 heads each per M-tile) are summed across lanes.  Lane (g, c)
 // keeps sub-tile g, so one 256-byte store per tile writes the token's 64
 // scores.  Because the workgroup covers the whole row of each of its
-// tokens, it builds the rows' key histograms in LDS and writes them out
-// whole: no global atomics and no clearing pass.
+// tokens, it builds the rows' key histograms in LDS and, once every score is
+// written, each wave selects its token's Top-K itself (wave_select above):
+// no global atomics, no clearing pass and no separate selection launch.
 //
 // Key rows in LDS: the 16-byte chunk ch of key row r sits at chunk
 // ch ^ swz(r) of the row, so the 16 keys of a sub-tile read at one logical
@@ -242,6 +243,214 @@ __device__ __forceinline__ float reduce_scatter4(const float (&x)[4], int g) {
   float ya = y, zb = z;
   permlane32_swap(ya, zb);  // ya: upper rows hold the lower rows' z; zb: lower rows the upper rows' y
   return g < 2 ? y + zb : z + ya;
+}
+
+// ---------------------------------------------------------------------------
+// Top-K of a complete score row by one wave, at the end of the prefill
+// kernel: the m = min(K, t + 1) largest scores, ties to the lower position
+// (the selection of the fused indexer: "Internal Fusion of the Indexer" in
+// Day 0 Inference Support for New LLM Architectures; the tie rule is this
+// library's reading).  The row's key histogram (top 11 bits of the
+// order-preserving key) is already in the wave's LDS histogram.  One pass over
+// the row (from L2) histograms the next 11 key bits of the keys in the chosen
+// top bucket; a second pass writes, in position order, the positions of the
+// keys above the chosen 22-bit prefix and keeps those with the prefix
+// (usually a handful: one score value for integer-valued scores) in LDS,
+// where a 10-bit histogram fixes the exact threshold key tau and the first
+// keys equal to it are taken.  When the prefix holds more keys than the LDS
+// list, a third pass histograms the last 10 bits over the row instead and a
+// fourth writes the positions.
+// ---------------------------------------------------------------------------
+
+// The bin d of an NB-bin LDS histogram (bins in key order) holding the
+// want-th largest key: S(> d) < want <= S(>= d); above = S(> d), cnt = h[d].
+template <int NB>
+__device__ __forceinline__ void wave_pick(const uint32_t* h, uint32_t want, int lane, uint32_t& d, uint32_t& above,
+                                          uint32_t& cnt) {
+  constexpr int PER = NB / WAVE;
+  uint32_t v[PER];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    v[j] = h[PER * lane + j];
+    tot += v[j];
+  }
+  uint32_t suf = tot;  // keys in the bins of lanes >= this one
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const uint32_t o = __shfl_down(suf, off);
+    if (lane + off < WAVE) suf += o;
+  }
+  uint32_t run = suf - tot, fd = 0, fa = 0, fc = 0;
+  bool found = false;
+#pragma unroll
+  for (int j = PER - 1; j >= 0; --j) {
+    if (run < want && run + v[j] >= want) {
+      found = true;
+      fd = PER * lane + j;
+      fa = run;
+      fc = v[j];
+    }
+    run += v[j];
+  }
+  const int src = __builtin_ctzll(__builtin_amdgcn_ballot_w64(found));
+  d = __builtin_amdgcn_readlane(fd, src);
+  above = __builtin_amdgcn_readlane(fa, src);
+  cnt = __builtin_amdgcn_readlane(fc, src);
+}
+
+// keys i .. i + 3 of a score row of n keys (positions >= n read as key 0,
+// below every score)
+__device__ __forceinline__ u32x4 row_keys4(const float* row, int i, int n) {
+  u32x4 k;
+  if (i + 3 < n) {
+    const f32x4 f = *(const f32x4*)(row + i);
+    k = u32x4{score_key(f[0]), score_key(f[1]), score_key(f[2]), score_key(f[3])};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k[e] = i + e < n ? score_key(row[i + e]) : 0u;
+  }
+  return k;
+}
+
+// f(i, keys i .. i + 3) over the row, 16 KiB in flight per wave
+template <typename F>
+__device__ __forceinline__ void stream_row(const float* row, int n, int lane, F&& f) {
+  constexpr int U = 16;
+  for (int i0 = 0; i0 < n; i0 += 256 * U) {
+    u32x4 k[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + 256 * u + 4 * lane;
+      k[u] = i < n ? row_keys4(row, i, n) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) f(i0 + 256 * u + 4 * lane, k[u]);
+  }
+}
+
+// Positions of the keys selected by `take(key)` (ballot per element), in
+// position order, to out[o ..); o advances by their count.
+template <typename P>
+__device__ __forceinline__ void emit_ordered(int i, const u32x4& k, int n, int lane, int32_t* out, uint32_t& o,
+                                             P&& take) {
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint64_t bm[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bm[e] = __builtin_amdgcn_ballot_w64(i + e < n && take(k[e]));
+  uint32_t pos = o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pos += __popcll(bm[e] & below);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if ((bm[e] >> lane) & 1ull) out[pos++] = i + e;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o += __popcll(bm[e]);
+}
+
+// h: the wave's 2048-bin LDS histogram of the row's top 11 key bits; list:
+// the wave's LDS scratch of list_cap words
+__device__ void wave_select(const float* row, int n, int K, int32_t* out, uint32_t* h, uint32_t* list, int list_cap,
+                            int lane) {
+  const int m = min(K, n);
+  for (int i = m + lane; i < K; i += WAVE) out[i] = -1;
+  if (m == n) {
+    for (int i = lane; i < n; i += WAVE) out[i] = i;
+    return;
+  }
+  uint32_t d1, above1, cnt1, d2, above2, cnt2, d3, above3, cnt3;
+  wave_pick<SCORE_HIST_BINS>(h, (uint32_t)m, lane, d1, above1, cnt1);
+  const uint32_t rem1 = (uint32_t)m - above1;
+  // key bits 20..10 of the keys in bucket d1
+  for (int j = lane; j < SCORE_HIST_BINS; j += WAVE) h[j] = 0u;
+  stream_row(row, n, lane, [&](int i, u32x4 k) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (i + e < n && (k[e] >> 21) == d1) atomicAdd(&h[(k[e] >> 10) & 2047u], 1u);
+  });
+  wave_pick<SCORE_HIST_BINS>(h, rem1, lane, d2, above2, cnt2);
+  const uint32_t rem2 = rem1 - above2;
+  const uint32_t pre22 = (d1 << 11) | d2;
+  const uint32_t n_above22 = above1 + above2;  // keys whose 22-bit prefix is larger
+  for (int j = lane; j < 1024; j += WAVE) h[j] = 0u;
+
+  if (cnt2 <= (uint32_t)list_cap && n <= (1 << 22)) {
+    // positions above the prefix to the output; the prefix keys to the list
+    // as (low 10 key bits << 22 | position), both in position order, and
+    // their low 10 bits into the histogram
+    uint32_t og = 0, ol = 0;
+    const uint64_t below = (1ull << lane) - 1ull;
+    stream_row(row, n, lane, [&](int i, u32x4 k) {
+      emit_ordered(i, k, n, lane, out, og, [&](uint32_t key) { return (key >> 10) > pre22; });
+      uint64_t bm[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bm[e] = __builtin_amdgcn_ballot_w64(i + e < n && (k[e] >> 10) == pre22);
+      uint32_t q = ol;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q += __popcll(bm[e] & below);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((bm[e] >> lane) & 1ull) {
+          list[q++] = ((k[e] & 1023u) << 22) | (uint32_t)(i + e);
+          atomicAdd(&h[k[e] & 1023u], 1u);
+        }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ol += __popcll(bm[e]);
+    });
+    wave_pick<1024>(h, rem2, lane, d3, above3, cnt3);
+    const uint32_t need = rem2 - above3;  // list keys equal to tau taken, lowest positions first
+    int32_t* out_a = out + n_above22;     // list keys above tau, then the `need` first equal ones
+    int32_t* out_e = out_a + above3;
+    uint32_t oa = 0, oe = 0;
+    for (uint32_t j0 = 0; j0 < cnt2; j0 += WAVE) {
+      const uint32_t j = j0 + lane;
+      const uint32_t v = j < cnt2 ? list[j] : 0u;
+      const uint32_t low = v >> 22;
+      const uint64_t ma = __builtin_amdgcn_ballot_w64(j < cnt2 && low > d3);
+      const uint64_t me = __builtin_amdgcn_ballot_w64(j < cnt2 && low == d3);
+      const int32_t pos = (int32_t)(v & ((1u << 22) - 1u));
+      if ((ma >> lane) & 1ull) out_a[oa + __popcll(ma & below)] = pos;
+      if ((me >> lane) & 1ull) {
+        const uint32_t r = oe + __popcll(me & below);
+        if (r < need) out_e[r] = pos;
+      }
+      oa += __popcll(ma);
+      oe += __popcll(me);
+    }
+    return;
+  }
+
+  // the prefix holds too many keys for the list: key bits 9..0 over the row
+  stream_row(row, n, lane, [&](int i, u32x4 k) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (i + e < n && (k[e] >> 10) == pre22) atomicAdd(&h[k[e] & 1023u], 1u);
+  });
+  wave_pick<1024>(h, rem2, lane, d3, above3, cnt3);
+  const uint32_t tau = (pre22 << 10) | d3;
+  const uint32_t need = rem2 - above3;  // keys equal to tau taken, lowest positions first
+  const uint32_t n_gt = (uint32_t)m - need;
+  // positions, in order: keys above tau to out[0 .. n_gt), the first `need`
+  // keys equal to tau after them
+  uint32_t og = 0, oe = 0;
+  stream_row(row, n, lane, [&](int i, u32x4 k) {
+    emit_ordered(i, k, n, lane, out, og, [&](uint32_t key) { return key > tau; });
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint64_t be[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) be[e] = __builtin_amdgcn_ballot_w64(i + e < n && k[e] == tau);
+    uint32_t pe = oe;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pe += __popcll(be[e] & below);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((be[e] >> lane) & 1ull) {
+        if (pe < need) out[n_gt + pe] = i + e;
+        ++pe;
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) oe += __popcll(be[e]);
+  });
 }
 
 template <int MT, int KS, bool FP8>
@@ -391,11 +600,14 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     }
   }
 
-  // ---- the complete key histogram of each token's row -------------------------
+  // ---- each wave selects the Top-K of its token's complete row -----------------
   __syncthreads();
   if (active) {
-    uint32_t* gh = p.hist + (int64_t)tok * SCORE_HIST_BINS;
-    for (int i = lane; i < SCORE_HIST_BINS / 4; i += WAVE) ((u32x4*)gh)[i] = ((const u32x4*)my_hist)[i];
+    wait_vmcnt<0>();  // the wave's score stores have completed
+    // the tile ring is free now: each wave takes an equal share as its list
+    constexpr int LIST = PF_NBUF * TILEB / 4 / PF_TOKS;
+    wave_select(srow, t + 1, p.top_k, p.out_idx + (int64_t)tok * p.top_k, my_hist,
+                (uint32_t*)ring + wave * LIST, LIST, lane);
   }
 }
 
@@ -403,6 +615,12 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
 bool prefill_fits(const SeqView& sv) {
   return sv.block_table == nullptr || cdiv(sv.max_ctx_len, 1 << sv.page_shift) <= PF_MAX_PAGES;
 }
+
+}  // namespace
+
+bool score_selects(const SeqView& sv) { return sv.max_q_len > 1 && prefill_fits(sv); }
+
+namespace {
 
 template <int MT, int KS, bool FP8>
 hipError_t launch_mt(const ScoreParams& p, hipStream_t stream) {
@@ -447,7 +665,7 @@ hipError_t launch_dt(const ScoreParams& p, hipStream_t stream) {
 hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream) {
   // the decode kernel accumulates the row histograms with atomics: clear
   // them first (a kernel, not a memset, so the call stays safe to capture in
-  // a graph); the prefill kernel writes whole rows
+  // a graph); the prefill kernel keeps its histograms in LDS
   if (p.sv.max_q_len == 1 || !prefill_fits(p.sv)) {
     const int64_t n4 = (int64_t)p.sv.num_tokens * SCORE_HIST_BINS / 4;
     const int64_t zblocks = std::min<int64_t>((n4 + 255) / 256, 2048);
