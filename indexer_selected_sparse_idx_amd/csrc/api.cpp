@@ -102,9 +102,8 @@ size_t score_hist_bytes(const idx_seqs* s) {
   return align_up((size_t)std::max(s->num_tokens, 0) * SCORE_HIST_BINS * sizeof(uint32_t));
 }
 int topk_nch(const idx_seqs* s) { return std::max(1, (s->max_ctx_len + TOPK_CHUNK - 1) / TOPK_CHUNK); }
-size_t topk_rows_bytes(const idx_seqs* s) { return align_up((size_t)std::max(s->num_tokens, 0) * sizeof(TopkRow)); }
 size_t score_ws_bytes(const idx_seqs* s) {
-  return score_rows_bytes(s) + score_hist_bytes(s) + topk_rows_bytes(s) +
+  return score_rows_bytes(s) + score_hist_bytes(s) +
          align_up((size_t)std::max(s->num_tokens, 0) * topk_nch(s) * 2 * sizeof(uint32_t));
 }
 
@@ -134,8 +133,7 @@ int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int 
   sp.score_stride = score_stride(seqs);
   uint8_t* const base = static_cast<uint8_t*>(ws);
   const size_t hist_off = score_rows_bytes(seqs);
-  const size_t rows_off = hist_off + score_hist_bytes(seqs);
-  const size_t cnt_off = rows_off + topk_rows_bytes(seqs);
+  const size_t cnt_off = hist_off + score_hist_bytes(seqs);
   sp.hist = reinterpret_cast<uint32_t*>(base + hist_off);
   sp.top_k = top_k;
   sp.out_idx = out_idx;
@@ -146,7 +144,6 @@ int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int 
   tp.scores = sp.scores;
   tp.score_stride = sp.score_stride;
   tp.hist = sp.hist;
-  tp.rows = reinterpret_cast<TopkRow*>(base + rows_off);
   tp.chunk_cnt = reinterpret_cast<uint32_t*>(base + cnt_off);
   tp.nch_stride = topk_nch(seqs);
   tp.top_k = top_k;

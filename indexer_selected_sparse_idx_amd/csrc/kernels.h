@@ -55,17 +55,11 @@ struct ScoreParams {
   int32_t* out_idx;        // [T, top_k]: written by the prefill kernel, which also selects
 };
 
-// Per-row threshold record of the selection (see topk.hip).
-struct TopkRow {
-  uint32_t mode, d1, above1, cnt1;
-};
-
 struct TopkParams {
   SeqView sv;
   float* scores;           // [T, score_stride]; the selection reuses each row's storage
   int64_t score_stride;
   const uint32_t* hist;    // [T, SCORE_HIST_BINS] from the score kernel
-  TopkRow* rows;           // [T]
   uint32_t* chunk_cnt;     // [T, nch_stride, 2]
   int nch_stride;          // ceil(max_ctx_len / TOPK_CHUNK)
   int top_k;

@@ -7,15 +7,18 @@
 // Inference Support for New LLM Architectures; the in-place index selection
 // of its fused indexer sketch; the tie rule is this library's reading).
 //
-// The score kernel has already histogrammed the top 11 bits of every key of
-// the row, so the bucket d1 holding the m-th largest key is known before the
-// row is read again.  Three launches then select (details below, above the
-// kernels): a per-row threshold, a compaction pass that many workgroups run
-// over chunks of every row (keys above d1 are taken, keys in d1 kept as
-// candidates, both in position order), and one workgroup per row that
-// gathers them and runs the radix select over the candidates (a few thousand
-// at most for smooth score distributions); when d1 holds more than the LDS
-// capacity (massive ties) the radix select runs over the whole score row.
+// These kernels select for the decode score kernel (and for prefill batches
+// whose block tables the prefill kernel cannot stage; the prefill kernel
+// otherwise selects on its own).  The score kernel has already histogrammed
+// the top 11 bits of every key of the row, so the bucket d1 holding the m-th
+// largest key is known before the row is read again.  Two launches then
+// select (details below, above the kernels): a compaction pass that many
+// workgroups run over chunks of every row (keys above d1 are taken, keys in
+// d1 kept as candidates, both in position order), and one workgroup per row
+// that gathers them and runs the radix select over the candidates (a few
+// thousand at most for smooth score distributions); when d1 holds more than
+// the LDS capacity (massive ties) the radix select runs over the whole score
+// row.
 //
 // Radix select over a key list:
 // a. Up to four 8-bit digit passes, most significant first, histogram the
@@ -242,9 +245,10 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
 }
 
 // ---------------------------------------------------------------------------
-// The selection as three launches.
-//   thresh  one wave per row: from the row histogram, the bucket d1 holding
-//           the m-th largest key, the count above it and its size.
+// The selection as two launches.
+// Both launches start from the row's threshold: the bucket d1 holding the
+// m-th largest key, the count above it and its size, which one wave derives
+// from the row histogram (every workgroup of a row derives the same).
 //   emit    one workgroup per (row, TOPK_CHUNK keys): the chunk's keys above
 //           d1 and in d1 are compacted, in position order, into the chunk's
 //           own part of the score row (just read, and read by no one else):
@@ -270,63 +274,63 @@ __device__ __forceinline__ int row_len(const SeqView& sv, int tok) {
   return sv.ctx_len[b] - q_len(sv, b) + (tok - first_token(sv, b)) + 1;
 }
 
-__global__ __launch_bounds__(256) void topk_thresh_kernel(TopkParams p) {
-  const int lane = threadIdx.x & 63;
-  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tok >= p.sv.num_tokens) return;
-  const int n = row_len(p.sv, tok);
+// The row's threshold record, computed by one wave from the row histogram
+// (lane L holds bins 32 L .. 32 L + 31): d1, the bucket holding the m-th
+// largest key, above1 = the keys in higher buckets, cnt1 = the keys in d1.
+struct TopkRow {
+  uint32_t mode, d1, above1, cnt1;
+};
+
+__device__ TopkRow row_threshold(const TopkParams& p, int tok, int n, int lane) {
   const uint32_t m = (uint32_t)min(p.top_k, n);
   TopkRow r = {TK_ALL, 0u, 0u, 0u};
-  if (m < (uint32_t)n) {
-    // lane L holds bins 32 L .. 32 L + 31
-    const u32x4* gh = (const u32x4*)(p.hist + (int64_t)tok * SCORE_HIST_BINS + 32 * lane);
-    uint32_t h[32];
+  if (m == (uint32_t)n) return r;
+  const u32x4* gh = (const u32x4*)(p.hist + (int64_t)tok * SCORE_HIST_BINS + 32 * lane);
+  uint32_t h[32];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x4 v = gh[j];
-      h[4 * j] = v[0]; h[4 * j + 1] = v[1]; h[4 * j + 2] = v[2]; h[4 * j + 3] = v[3];
-    }
-    uint32_t tot = 0;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) tot += h[j];
-    uint32_t suf = tot;  // keys in the bins of lanes >= L
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_down(suf, off);
-      if (lane + off < 64) suf += o;
-    }
-    uint32_t run = suf - tot;  // keys in the bins above this lane's
-    uint32_t d1 = 0, above1 = 0, cnt1 = 0;
-    bool found = false;
-#pragma unroll
-    for (int j = 31; j >= 0; --j) {
-      if (run < m && run + h[j] >= m) {
-        found = true;
-        d1 = 32 * lane + j;
-        above1 = run;
-        cnt1 = h[j];
-      }
-      run += h[j];
-    }
-    const uint64_t fm = __builtin_amdgcn_ballot_w64(found);
-    if (fm == 0) {
-      r.mode = TK_WHOLE_ROW;  // (a histogram that does not add up to the row: select from the scores)
-    } else {
-      const int src = __builtin_ctzll(fm);
-      r.d1 = __builtin_amdgcn_readlane(d1, src);
-      r.above1 = __builtin_amdgcn_readlane(above1, src);
-      r.cnt1 = __builtin_amdgcn_readlane(cnt1, src);
-      r.mode = (r.cnt1 > (uint32_t)CAP || cdiv(n, TOPK_CHUNK) > TK_MAXCH) ? TK_WHOLE_ROW : TK_PARTIAL;
-    }
+  for (int j = 0; j < 8; ++j) {
+    const u32x4 v = gh[j];
+    h[4 * j] = v[0]; h[4 * j + 1] = v[1]; h[4 * j + 2] = v[2]; h[4 * j + 3] = v[3];
   }
-  if (lane == 0) p.rows[tok] = r;
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) tot += h[j];
+  uint32_t suf = tot;  // keys in the bins of lanes >= L
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_down(suf, off);
+    if (lane + off < 64) suf += o;
+  }
+  uint32_t run = suf - tot;  // keys in the bins above this lane's
+  uint32_t d1 = 0, above1 = 0, cnt1 = 0;
+  bool found = false;
+#pragma unroll
+  for (int j = 31; j >= 0; --j) {
+    if (run < m && run + h[j] >= m) {
+      found = true;
+      d1 = 32 * lane + j;
+      above1 = run;
+      cnt1 = h[j];
+    }
+    run += h[j];
+  }
+  const uint64_t fm = __builtin_amdgcn_ballot_w64(found);
+  if (fm == 0) {
+    r.mode = TK_WHOLE_ROW;  // (a histogram that does not add up to the row: select from the scores)
+  } else {
+    const int src = __builtin_ctzll(fm);
+    r.d1 = __builtin_amdgcn_readlane(d1, src);
+    r.above1 = __builtin_amdgcn_readlane(above1, src);
+    r.cnt1 = __builtin_amdgcn_readlane(cnt1, src);
+    r.mode = (r.cnt1 > (uint32_t)CAP || cdiv(n, TOPK_CHUNK) > TK_MAXCH) ? TK_WHOLE_ROW : TK_PARTIAL;
+  }
+  return r;
 }
 
 __global__ __launch_bounds__(TKE_THREADS) void topk_emit_kernel(TopkParams p) {
   __shared__ uint32_t wt[2][TKE_WAVES];
+  __shared__ TopkRow sh_r;
   const int tok = blockIdx.x, chunk = blockIdx.y;
-  const TopkRow r = p.rows[tok];
-  if (r.mode != TK_PARTIAL) return;
   const int n = row_len(p.sv, tok);
   const int c0 = chunk * TOPK_CHUNK;
   if (c0 >= n) return;
@@ -336,6 +340,14 @@ __global__ __launch_bounds__(TKE_THREADS) void topk_emit_kernel(TopkParams p) {
   const int i = c0 + 8 * tid;
   const u32x4 k0 = i < n ? src.get4(i) : u32x4{0u, 0u, 0u, 0u};
   const u32x4 k1 = i + 4 < n ? src.get4(i + 4) : u32x4{0u, 0u, 0u, 0u};
+  // every workgroup of the row derives the same threshold from the histogram
+  if (wave == 0) {
+    const TopkRow rr = row_threshold(p, tok, n, lane);
+    if (lane == 0) sh_r = rr;
+  }
+  __syncthreads();
+  const TopkRow r = sh_r;
+  if (r.mode != TK_PARTIAL) return;
   const uint32_t key[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
   uint32_t fg = 0, fe = 0;
 #pragma unroll
@@ -377,6 +389,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkParams p)
   __shared__ uint32_t whist[TOPK_WAVES * 256];
   __shared__ uint32_t wcnt[2 * TOPK_WAVES];
   __shared__ uint32_t choff[2][TK_MAXCH], chcnt[2][TK_MAXCH];
+  __shared__ TopkRow sh_r;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -388,7 +401,12 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkParams p)
   const float* row = p.scores + (int64_t)tok * p.score_stride;
   int32_t* out = p.out_idx + (int64_t)tok * K;
   for (int i = m + tid; i < K; i += TOPK_THREADS) out[i] = -1;
-  const TopkRow r = p.rows[tok];
+  if (wave == 0) {
+    const TopkRow rr = row_threshold(p, tok, n, lane);
+    if (lane == 0) sh_r = rr;
+  }
+  __syncthreads();
+  const TopkRow r = sh_r;
   if (r.mode == TK_ALL) {
     for (int i = tid; i < n; i += TOPK_THREADS) out[i] = i;
     return;
@@ -446,7 +464,6 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkParams p)
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
   const int T = p.sv.num_tokens;
   timer_before(1, stream);
-  hipLaunchKernelGGL(topk_thresh_kernel, dim3(cdiv(T, 4)), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(topk_emit_kernel, dim3(T, p.nch_stride), dim3(TKE_THREADS), 0, stream, p);
   hipLaunchKernelGGL(topk_select_kernel, dim3(T), dim3(TOPK_THREADS), 0, stream, p);
   hipError_t e = hipGetLastError();

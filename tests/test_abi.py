@@ -143,10 +143,10 @@ def test_fused_workspace_check(L):
 def test_workspace_sizes(L):
     s = seqs(num_seqs=3, num_tokens=3, max_ctx_len=1000, seq_stride=1000)
     # one fp32 score row per token padded to 64 columns, one 2048-bin key
-    # histogram per token, a 16-byte selection record per token and two
-    # counts per 2048-key chunk of a row, each part rounded to 256 bytes
+    # histogram per token and two counts per 2048-key chunk of a row, each
+    # part rounded to 256 bytes
     up = lambda b: -(-b // 256) * 256
-    want = up(3 * 1024 * 4) + up(3 * 2048 * 4) + up(3 * 16) + up(3 * 1 * 8)
+    want = up(3 * 1024 * 4) + up(3 * 2048 * 4) + up(3 * 1 * 8)
     assert L.idx_score_topk_workspace(ctypes.byref(s), 64, 128, 2048) == want
     assert L.sparse_mla_attn_workspace(ctypes.byref(s), 128, 2048) > 0     # decode splits
     big = seqs(num_seqs=1, num_tokens=4096, cu_q=FAKE, max_q_len=4096, max_ctx_len=8192,
