@@ -616,7 +616,10 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
       const int slot_next = (k + NBUF - 2) % NBUF;
       const uint8_t* buf = smem + (k % NBUF) * BUF_BYTES;
       if (R::SPREAD && more) {
-        const typename R::Tile nt = R::prepare(rows_sh + (k + NBUF - 2) * TILE, smem_base + slot_next * BUF_BYTES, lane);
+        // (the tile index goes through a scalar register so that the compiler
+        // does not carry the row pointer as a VGPR induction variable)
+        const int kn = __builtin_amdgcn_readfirstlane(k + NBUF - 2);
+        const typename R::Tile nt = R::prepare(rows_sh + kn * TILE, smem_base + slot_next * BUF_BYTES, lane);
         return s_phase(a, buf, ad, [&](auto ks) { R::template issue_at_step<decltype(ks)::value>(p, nt, wave, lane); });
       }
       if (more) R::issue(p, rows_sh + (k + NBUF - 2) * TILE, smem_base + slot_next * BUF_BYTES, wave, lane);
@@ -628,10 +631,6 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
       sm.run_all(a, min(TILE, n), p.scale_log2, h);
       op_prev = sm.op;
     }
-    // Nothing the compiler tracks may be in flight when the loop starts (a
-    // spill reload still pending here would make it wait for every gather in
-    // every iteration); this waits once for the gathers of tile 2.
-    wait_vmcnt<0>();
     for (int k = 1; k < ntiles; ++k) {
       SoftmaxTile<SPLITP> sm(s_of_tile(k));
       const int nv = min(TILE, n - k * TILE);
