@@ -349,9 +349,10 @@ __device__ __forceinline__ void emit_ordered(int i, const u32x4& k, int n, int l
 }
 
 // h: the wave's 2048-bin LDS histogram of the row's top 11 key bits; list:
-// the wave's LDS scratch of list_cap words
-__device__ void wave_select(const float* row, int n, int K, int32_t* out, uint32_t* h, uint32_t* list, int list_cap,
-                            int lane) {
+// the wave's LDS scratch of list_cap words.  The general form, for rows of
+// any length: every pass reads the whole row.
+__device__ void wave_select_rows(const float* row, int n, int K, int32_t* out, uint32_t* h, uint32_t* list,
+                                 int list_cap, int lane) {
   const int m = min(K, n);
   for (int i = m + lane; i < K; i += WAVE) out[i] = -1;
   if (m == n) {
@@ -450,6 +451,152 @@ __device__ void wave_select(const float* row, int n, int K, int32_t* out, uint32
       }
 #pragma unroll
     for (int e = 0; e < 4; ++e) oe += __popcll(be[e]);
+  });
+}
+
+// The usual form, for rows of up to 64 chunks of SEL_CHUNK keys: the one pass
+// over the whole row also compacts the keys of the top bucket d1, in position
+// order, into the storage of their chunk (just read by this wave, needed by
+// no one else) as (low 21 key bits << 11 | offset in the chunk); lane c keeps
+// chunk c's count.  Every later pass reads only those (about a tenth of the
+// row for smooth score distributions).
+constexpr int SEL_CHUNK = 2048;
+__device__ void wave_select(float* row, int n, int K, int32_t* out, uint32_t* h, uint32_t* list, int list_cap,
+                            int lane) {
+  const int nch = cdiv(n, SEL_CHUNK);
+  if (nch > WAVE) {
+    wave_select_rows(row, n, K, out, h, list, list_cap, lane);
+    return;
+  }
+  const int m = min(K, n);
+  for (int i = m + lane; i < K; i += WAVE) out[i] = -1;
+  if (m == n) {
+    for (int i = lane; i < n; i += WAVE) out[i] = i;
+    return;
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t d1, above1, cnt1, d2, above2, cnt2, d3, above3, cnt3;
+  wave_pick<SCORE_HIST_BINS>(h, (uint32_t)m, lane, d1, above1, cnt1);
+  const uint32_t rem1 = (uint32_t)m - above1;
+  for (int j = lane; j < SCORE_HIST_BINS; j += WAVE) h[j] = 0u;
+
+  // pass over the row: positions above d1 to out[0 .. above1); d1 keys
+  // compacted into their chunk, their key bits 20..10 into the histogram
+  uint32_t* words = (uint32_t*)row;
+  uint32_t og = 0, ccnt = 0;
+  for (int c = 0; c < nch; ++c) {
+    const int c0 = c * SEL_CHUNK;
+    u32x4 k[SEL_CHUNK / 256];
+#pragma unroll
+    for (int u = 0; u < SEL_CHUNK / 256; ++u) {
+      const int i = c0 + 256 * u + 4 * lane;
+      k[u] = i < n ? row_keys4(row, i, n) : u32x4{0u, 0u, 0u, 0u};
+    }
+    uint32_t oc = 0;
+#pragma unroll
+    for (int u = 0; u < SEL_CHUNK / 256; ++u) {
+      const int i = c0 + 256 * u + 4 * lane;
+      emit_ordered(i, k[u], n, lane, out, og, [&](uint32_t key) { return (key >> 21) > d1; });
+      uint64_t bm[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bm[e] = __builtin_amdgcn_ballot_w64(i + e < n && (k[u][e] >> 21) == d1);
+      uint32_t q = oc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q += __popcll(bm[e] & below);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((bm[e] >> lane) & 1ull) {
+          // (the compacted entries stay below the keys still to be read: a
+          // chunk's keys are all loaded before its first entry is written)
+          words[c0 + q++] = ((k[u][e] & 0x1FFFFFu) << 11) | (uint32_t)(i + e - c0);
+          atomicAdd(&h[(k[u][e] >> 10) & 2047u], 1u);
+        }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oc += __popcll(bm[e]);
+    }
+    if (lane == c) ccnt = oc;
+  }
+  wave_pick<SCORE_HIST_BINS>(h, rem1, lane, d2, above2, cnt2);
+  const uint32_t rem2 = rem1 - above2;
+  for (int j = lane; j < 1024; j += WAVE) h[j] = 0u;
+  int32_t* out_2 = out + above1;  // d1 keys above d2, then what the last bits decide
+  wait_vmcnt<0>();  // the compacted entries are written
+
+  // f(entry, valid, c0) over the compacted d1 keys, chunk after chunk (read
+  // at device scope: this wave's own stores must not be shadowed by lines of
+  // the scores it read before)
+  auto over_d1 = [&](auto&& f) {
+    for (int c = 0; c < nch; ++c) {
+      const uint32_t cc = __builtin_amdgcn_readlane(ccnt, c);
+      for (uint32_t j0 = 0; j0 < cc; j0 += WAVE) {
+        const uint32_t j = j0 + lane;
+        const uint32_t w =
+            j < cc ? __hip_atomic_load(words + c * SEL_CHUNK + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+        f(w, j < cc, c * SEL_CHUNK);
+      }
+    }
+  };
+  if (cnt2 <= (uint32_t)list_cap && n <= (1 << 22)) {
+    // d1 keys above d2 to the output; those in d2 to the list as (low 10
+    // key bits << 22 | position), with their low bits into the histogram
+    uint32_t oa = 0, ol = 0;
+    over_d1([&](uint32_t w, bool ok, int c0) {
+      const uint32_t sub = w >> 21;
+      const int32_t pos = c0 + (int32_t)(w & (SEL_CHUNK - 1));
+      const uint64_t ma = __builtin_amdgcn_ballot_w64(ok && sub > d2);
+      const uint64_t mb = __builtin_amdgcn_ballot_w64(ok && sub == d2);
+      if ((ma >> lane) & 1ull) out_2[oa + __popcll(ma & below)] = pos;
+      if ((mb >> lane) & 1ull) {
+        list[ol + __popcll(mb & below)] = (((w >> 11) & 1023u) << 22) | (uint32_t)pos;
+        atomicAdd(&h[(w >> 11) & 1023u], 1u);
+      }
+      oa += __popcll(ma);
+      ol += __popcll(mb);
+    });
+    wave_pick<1024>(h, rem2, lane, d3, above3, cnt3);
+    const uint32_t need = rem2 - above3;  // list keys equal to tau taken, lowest positions first
+    int32_t* out_a = out_2 + above2;
+    int32_t* out_e = out_a + above3;
+    uint32_t oa3 = 0, oe = 0;
+    for (uint32_t j0 = 0; j0 < cnt2; j0 += WAVE) {
+      const uint32_t j = j0 + lane;
+      const uint32_t v = j < cnt2 ? list[j] : 0u;
+      const uint32_t low = v >> 22;
+      const uint64_t ma = __builtin_amdgcn_ballot_w64(j < cnt2 && low > d3);
+      const uint64_t me = __builtin_amdgcn_ballot_w64(j < cnt2 && low == d3);
+      const int32_t pos = (int32_t)(v & ((1u << 22) - 1u));
+      if ((ma >> lane) & 1ull) out_a[oa3 + __popcll(ma & below)] = pos;
+      if ((me >> lane) & 1ull) {
+        const uint32_t r = oe + __popcll(me & below);
+        if (r < need) out_e[r] = pos;
+      }
+      oa3 += __popcll(ma);
+      oe += __popcll(me);
+    }
+    return;
+  }
+  // d2 holds more keys than the list: the low 10 bits over the d1 keys, then
+  // the positions above tau and the first `need` equal to it
+  over_d1([&](uint32_t w, bool ok, int) {
+    if (ok && (w >> 21) == d2) atomicAdd(&h[(w >> 11) & 1023u], 1u);
+  });
+  wave_pick<1024>(h, rem2, lane, d3, above3, cnt3);
+  const uint32_t lowtau = (d2 << 10) | d3;  // key bits 20..0 of tau
+  const uint32_t need = rem2 - above3;
+  const uint32_t n_gt = above2 + above3;  // d1 keys above tau
+  uint32_t og2 = 0, oe = 0;
+  over_d1([&](uint32_t w, bool ok, int c0) {
+    const uint32_t low21 = w >> 11;
+    const int32_t pos = c0 + (int32_t)(w & (SEL_CHUNK - 1));
+    const uint64_t mg = __builtin_amdgcn_ballot_w64(ok && low21 > lowtau);
+    const uint64_t me = __builtin_amdgcn_ballot_w64(ok && low21 == lowtau);
+    if ((mg >> lane) & 1ull) out_2[og2 + __popcll(mg & below)] = pos;
+    if ((me >> lane) & 1ull) {
+      const uint32_t r = oe + __popcll(me & below);
+      if (r < need) out_2[n_gt + r] = pos;
+    }
+    og2 += __popcll(mg);
+    oe += __popcll(me);
   });
 }
 
