@@ -108,6 +108,28 @@ def test_all_equal_scores_take_lowest_positions():
     assert np.array_equal(got, np.tile(np.arange(256, dtype=np.int32), (5, 1)))
 
 
+def test_decode_all_equal_scores_whole_row_select():
+    # every score 0: the threshold bucket holds the whole row (13,000 keys, more
+    # than the candidate list), so decode selection runs over the whole row
+    wl = Workload("zeros decode", [13000, 9000], [{"seqs": [0, 1], "q_len": None}], top_k=512, H=32, seed=30)
+    inp = generate(wl, "cuda")
+    inp.q_idx.zero_()
+    call = inp.calls[0]
+    out, lse, idx = U.run_fused(inp, call)
+    got = np.sort(idx.cpu().numpy(), axis=1)
+    assert np.array_equal(got, np.tile(np.arange(512, dtype=np.int32), (2, 1)))
+    w_idx, w_out, w_lse = U.oracle_rows(inp, call, [0, 1])
+    U.check_indices(idx.cpu().numpy(), w_idx, "zeros decode")
+    U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), w_out, w_lse, U.TOL_BF16, "zeros decode")
+
+
+def test_prefill_rows_longer_than_the_compacted_path():
+    # rows of more than 64 x 2048 keys: the prefill selection reads the whole
+    # row in every pass (the form for rows of any length)
+    wl = Workload("long rows", [140000], [{"seqs": [0], "q_len": [3]}], top_k=256, H_I=4, d_I=64, H=8, seed=31)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "long rows")
+
+
 def test_separate_entry_points_match_fused():
     import indexer_selected_sparse_idx_amd as lib
     inp = generate(config(2, scale=1 / 16), "cuda")
