@@ -196,15 +196,19 @@ const char *idx_status_string(int status);
 
 /* ------------------------------------------------------------------------ *
  * Measurement hook.  idx_timer_arm(kernel, start, stop) makes the NEXT
- * launch of `kernel` by any entry point record the hipEvent_t `start` just
- * before it and `stop` just after it, on the stream it is launched on, and
- * then disarms.  One arm per kernel at a time; not thread-safe (a
- * measurement aid, not part of the compute path).  Returns IDX_OK or
- * IDX_ERR_INVALID_ARG.
+ * launch of `kernel` by any entry point record the hipEvent_t `start` at the
+ * start of its (first) dispatch and `stop` at the end of its (last), on the
+ * stream it is launched on, and then disarms.  The dispatches record the
+ * events themselves (hipExtLaunchKernelGGL), so an armed launch runs back to
+ * back with its neighbours like an unarmed one.  One arm per kernel at a
+ * time; not thread-safe (a measurement aid, not part of the compute path).
+ * Returns IDX_OK or IDX_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------ */
 typedef enum {
   IDX_KERNEL_SCORE = 0,     /* indexer score                                  */
-  IDX_KERNEL_TOPK = 1,      /* per-row radix select                           */
+  IDX_KERNEL_TOPK = 1,      /* Top-K selection of the decode indexer (the
+                               prefill indexer selects inside its score
+                               kernel)                                       */
   IDX_KERNEL_ATTN = 2,      /* sparse latent attention                        */
   IDX_KERNEL_COMBINE = 3,   /* split merge of the attention partials (only
                                launched when a call splits the index lists) */

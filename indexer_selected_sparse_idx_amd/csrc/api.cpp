@@ -138,7 +138,13 @@ int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int 
   sp.top_k = top_k;
   sp.out_idx = out_idx;
   if (launch_score(sp, k_dtype == IDX_E4M3, stream) != hipSuccess) return IDX_ERR_HIP;
-  if (score_selects(sp.sv)) return IDX_OK;
+  if (score_selects(sp.sv)) {
+    // the score kernel has selected: an armed Top-K timer measures nothing
+    const TimerEvents t = timer_take(IDX_KERNEL_TOPK);
+    if (t.start) (void)hipEventRecord(t.start, stream);
+    if (t.stop) (void)hipEventRecord(t.stop, stream);
+    return IDX_OK;
+  }
   TopkParams tp;
   tp.sv = sp.sv;
   tp.scores = sp.scores;
@@ -180,15 +186,12 @@ int run_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, int kv_
 
 }  // namespace
 
-void timer_before(int kernel, hipStream_t stream) {
-  if (g_timers[kernel].start) (void)hipEventRecord(g_timers[kernel].start, stream);
-}
-
-void timer_after(int kernel, hipStream_t stream) {
-  if (g_timers[kernel].stop) {
-    (void)hipEventRecord(g_timers[kernel].stop, stream);
-    g_timers[kernel] = Timer{};
-  }
+TimerEvents timer_take(int kernel) {
+  TimerEvents e;
+  e.start = g_timers[kernel].start;
+  e.stop = g_timers[kernel].stop;
+  g_timers[kernel] = Timer{};
+  return e;
 }
 
 }  // namespace idxs

@@ -754,17 +754,16 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
 }
 
 template <typename K>
-hipError_t launch_grid(K kernel, const AttnParams& p, int waves, hipStream_t stream) {
+hipError_t launch_grid(K kernel, const AttnParams& p, int waves, hipStream_t stream, const TimerEvents& t) {
   const int blocks = cdiv(p.sv.num_tokens, 8) * 8 * p.num_splits;
-  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(waves * WAVE), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(kernel, dim3(blocks), dim3(waves * WAVE), stream, t.start, t.stop, p);
 }
 
 template <int NW>
-hipError_t launch_nw(const AttnParams& p, bool fp8, hipStream_t stream) {
-  if (fp8) return launch_grid(attn_fp8_kernel<NW, 3, 2048>, p, NW, stream);
-  if (p.split_len <= 1024) return launch_grid(attn_bf16_kernel<NW, 4, 1024, true>, p, NW, stream);
-  return launch_grid(attn_bf16_kernel<NW, 4, 2048, true>, p, NW, stream);
+hipError_t launch_nw(const AttnParams& p, bool fp8, hipStream_t stream, const TimerEvents& t) {
+  if (fp8) return launch_grid(attn_fp8_kernel<NW, 3, 2048>, p, NW, stream, t);
+  if (p.split_len <= 1024) return launch_grid(attn_bf16_kernel<NW, 4, 1024, true>, p, NW, stream, t);
+  return launch_grid(attn_bf16_kernel<NW, 4, 2048, true>, p, NW, stream, t);
 }
 
 }  // namespace
@@ -779,19 +778,16 @@ int attn_num_splits(int num_tokens, int H, int top_k) {
 }
 
 hipError_t launch_attn(const AttnParams& p, bool kv_fp8, hipStream_t stream) {
-  timer_before(2, stream);
+  const TimerEvents t = timer_take(2);
   hipError_t e;
-  if (p.H <= 32) e = launch_nw<1>(p, kv_fp8, stream);
-  else if (p.H <= 64) e = launch_nw<2>(p, kv_fp8, stream);
-  else if (p.H <= 96) e = launch_nw<3>(p, kv_fp8, stream);
-  else e = launch_nw<4>(p, kv_fp8, stream);
-  timer_after(2, stream);
+  if (p.H <= 32) e = launch_nw<1>(p, kv_fp8, stream, t);
+  else if (p.H <= 64) e = launch_nw<2>(p, kv_fp8, stream, t);
+  else if (p.H <= 96) e = launch_nw<3>(p, kv_fp8, stream, t);
+  else e = launch_nw<4>(p, kv_fp8, stream, t);
   if (e != hipSuccess || p.num_splits == 1) return e;
-  timer_before(3, stream);
-  hipLaunchKernelGGL(combine_kernel, dim3(cdiv(p.sv.num_tokens * p.H, 2)), dim3(256), 0, stream, p);
-  e = hipGetLastError();
-  timer_after(3, stream);
-  return e;
+  const TimerEvents tc = timer_take(3);
+  return launch_kernel(combine_kernel, dim3(cdiv(p.sv.num_tokens * p.H, 2)), dim3(256), stream, tc.start, tc.stop,
+                       p);
 }
 
 }  // namespace idxs

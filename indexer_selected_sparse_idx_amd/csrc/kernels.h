@@ -1,6 +1,7 @@
 // Internal interface between the C ABI (api.cpp) and the HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -98,9 +99,23 @@ bool score_selects(const SeqView& sv);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool kv_fp8, hipStream_t stream);
 
-// Timing hook (api.cpp).
-void timer_before(int kernel, hipStream_t stream);
-void timer_after(int kernel, hipStream_t stream);
+// Timing hook (api.cpp): the events armed for the next launch of `kernel`
+// (null when none), disarmed by the call.
+struct TimerEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+TimerEvents timer_take(int kernel);
+
+// A kernel launch that, given events, has the dispatch itself record them
+// (hipExtLaunchKernelGGL: the start and end timestamps of the kernel, with
+// no separate event packets between kernels on the stream).
+template <typename K, typename... A>
+hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                         A... args) {
+  if (start || stop) hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, args...);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  return hipGetLastError();
+}
 
 // Attention split heuristic shared by the workspace query and the launcher.
 int attn_num_splits(int num_tokens, int H, int top_k);

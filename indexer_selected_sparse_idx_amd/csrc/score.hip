@@ -770,40 +770,39 @@ bool score_selects(const SeqView& sv) { return sv.max_q_len > 1 && prefill_fits(
 namespace {
 
 template <int MT, int KS, bool FP8>
-hipError_t launch_mt(const ScoreParams& p, hipStream_t stream) {
+hipError_t launch_mt(const ScoreParams& p, hipStream_t stream, const TimerEvents& t) {
   const SeqView& sv = p.sv;
   const bool decode = sv.max_q_len == 1;
   if (!decode && prefill_fits(sv)) {
     dim3 grid(cdiv(sv.max_q_len, PF_TOKS), sv.num_seqs);
-    hipLaunchKernelGGL((score_prefill_kernel<MT, KS, FP8>), grid, dim3(PF_TOKS * WAVE), 0, stream, p);
-  } else if (decode) {
+    return launch_kernel(score_prefill_kernel<MT, KS, FP8>, grid, dim3(PF_TOKS * WAVE), stream, t.start, t.stop, p);
+  }
+  if (decode) {
     const int kpw = 1024;
     dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs);
-    hipLaunchKernelGGL((score_kernel<MT, KS, FP8, true>), grid, dim3(256), 0, stream, p, kpw);
-  } else {
-    const int kpw = 256;
-    dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs * cdiv(sv.max_q_len, SCORE_WAVES));
-    hipLaunchKernelGGL((score_kernel<MT, KS, FP8, false>), grid, dim3(256), 0, stream, p, kpw);
+    return launch_kernel(score_kernel<MT, KS, FP8, true>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
   }
-  return hipGetLastError();
+  const int kpw = 256;
+  dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs * cdiv(sv.max_q_len, SCORE_WAVES));
+  return launch_kernel(score_kernel<MT, KS, FP8, false>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
 }
 
 template <bool FP8>
-hipError_t launch_dt(const ScoreParams& p, hipStream_t stream) {
+hipError_t launch_dt(const ScoreParams& p, hipStream_t stream, const TimerEvents& t) {
   const int mt = cdiv(p.H_I, 16);
   if (p.d_I == 128) {
     switch (mt) {
-      case 1: return launch_mt<1, 4, FP8>(p, stream);
-      case 2: return launch_mt<2, 4, FP8>(p, stream);
-      case 3: return launch_mt<3, 4, FP8>(p, stream);
-      default: return launch_mt<4, 4, FP8>(p, stream);
+      case 1: return launch_mt<1, 4, FP8>(p, stream, t);
+      case 2: return launch_mt<2, 4, FP8>(p, stream, t);
+      case 3: return launch_mt<3, 4, FP8>(p, stream, t);
+      default: return launch_mt<4, 4, FP8>(p, stream, t);
     }
   }
   switch (mt) {
-    case 1: return launch_mt<1, 2, FP8>(p, stream);
-    case 2: return launch_mt<2, 2, FP8>(p, stream);
-    case 3: return launch_mt<3, 2, FP8>(p, stream);
-    default: return launch_mt<4, 2, FP8>(p, stream);
+    case 1: return launch_mt<1, 2, FP8>(p, stream, t);
+    case 2: return launch_mt<2, 2, FP8>(p, stream, t);
+    case 3: return launch_mt<3, 2, FP8>(p, stream, t);
+    default: return launch_mt<4, 2, FP8>(p, stream, t);
   }
 }
 
@@ -819,10 +818,8 @@ hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream) {
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream, p.hist, n4);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
-  timer_before(0, stream);
-  hipError_t e = k_fp8 ? launch_dt<true>(p, stream) : launch_dt<false>(p, stream);
-  timer_after(0, stream);
-  return e;
+  const TimerEvents t = timer_take(0);
+  return k_fp8 ? launch_dt<true>(p, stream, t) : launch_dt<false>(p, stream, t);
 }
 
 }  // namespace idxs

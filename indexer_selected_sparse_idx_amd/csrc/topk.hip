@@ -463,12 +463,10 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkParams p)
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
   const int T = p.sv.num_tokens;
-  timer_before(1, stream);
-  hipLaunchKernelGGL(topk_emit_kernel, dim3(T, p.nch_stride), dim3(TKE_THREADS), 0, stream, p);
-  hipLaunchKernelGGL(topk_select_kernel, dim3(T), dim3(TOPK_THREADS), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  timer_after(1, stream);
-  return e;
+  const TimerEvents t = timer_take(1);  // start of the compaction, end of the select
+  hipError_t e = launch_kernel(topk_emit_kernel, dim3(T, p.nch_stride), dim3(TKE_THREADS), stream, t.start, nullptr, p);
+  if (e != hipSuccess) return e;
+  return launch_kernel(topk_select_kernel, dim3(T), dim3(TOPK_THREADS), stream, nullptr, t.stop, p);
 }
 
 }  // namespace idxs
