@@ -34,7 +34,9 @@ namespace idxs {
 namespace {
 
 constexpr int SCORE_WAVES = 4;
-constexpr int NT = 4;  // key tiles (16 keys each) per loop iteration
+constexpr int NT = 2;            // key tiles (16 keys each) per pipeline stage
+constexpr int SCORE_MAX_KPW = 1024;  // keys per workgroup the LDS page table covers
+constexpr int SCORE_WAVE_KEYS = 256;  // keys per wave: decode 1024 / 4 waves, prefill 256 (all waves)
 
 // max(x, 0) as one integer max on the bit pattern: negative floats (-0
 // included) are negative integers (fmaxf costs a second instruction that
@@ -53,13 +55,29 @@ __device__ __forceinline__ int kdim(int ks, int g) {
 // decode: the 4 waves of a workgroup split one token's key block.
 // prefill: the 4 waves are 4 consecutive query tokens of one sequence and
 //          all scan the workgroup's key block (shared through L1/L2).
+//
+// Each wave runs a two-stage register pipeline over its keys: the 16-byte
+// loads of the next NT key tiles are issued before the MFMAs and the
+// epilogue of the current ones, so a wave always has a stage of keys in
+// flight (a wave that waited for its loads and then computed left HBM idle
+// whenever the waves of a SIMD all computed at once).  A paged cache's block
+// table entries for the workgroup's key block are staged in LDS first, so no
+// key address waits on a dependent global load, and the scores are collected
+// in LDS and written once the wave's keys are done: a global store inside the
+// loop would make the next stage's address registers wait for the store, and
+// so for every load issued before it.
 template <int MT, int KS, bool FP8, bool DECODE>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_wg) {
+  constexpr int LD = FP8 ? KS / 2 : KS;  // 16-byte loads per key tile and lane
   // decode: one histogram shared by the 4 waves (one token);
   // prefill: one histogram per wave (one token each)
   __shared__ uint32_t lhist[DECODE ? 1 : SCORE_WAVES][SCORE_HIST_BINS];
+  __shared__ int pages[SCORE_MAX_KPW];
+  __shared__ float sbuf[SCORE_WAVES][SCORE_WAVE_KEYS];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform (scalar) so that the key loop is a uniform loop: a divergent
+  // one merges its exit paths and waits for every load at the loop head
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int c = lane & 15;
   const SeqView& sv = p.sv;
@@ -68,11 +86,11 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_
 
   int b, tok, t, key_lo, key_hi;  // wave's keys: [key_lo, key_hi]
   bool active = true;
+  const int wg_lo = blockIdx.x * keys_per_wg;
   if (DECODE) {
     b = blockIdx.y;
     tok = first_token(sv, b);
     t = sv.ctx_len[b] - 1;
-    const int wg_lo = blockIdx.x * keys_per_wg;
     const int per_wave = keys_per_wg / SCORE_WAVES;
     key_lo = wg_lo + wave * per_wave;
     key_hi = min(t, key_lo + per_wave - 1);
@@ -84,10 +102,17 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_
     active = i < ql;
     tok = first_token(sv, b) + (active ? i : 0);
     t = sv.ctx_len[b] - ql + i;
-    key_lo = blockIdx.x * keys_per_wg;
+    key_lo = wg_lo;
     key_hi = min(t, key_lo + keys_per_wg - 1);
   }
   active = active && key_lo <= key_hi;
+  // block table entries of the pages that hold keys wg_lo .. min(ctx_len, wg_lo + keys_per_wg) - 1
+  const int page0 = wg_lo >> sv.page_shift;
+  if (sv.block_table) {
+    const int last = min(sv.ctx_len[b], wg_lo + keys_per_wg) - 1;
+    const int np = last >= wg_lo ? (last >> sv.page_shift) - page0 + 1 : 0;
+    for (int i = threadIdx.x; i < np; i += 256) pages[i] = sv.block_table[(int64_t)b * sv.bt_stride + page0 + i];
+  }
   uint32_t* my_hist = lhist[DECODE ? 0 : wave];
   __syncthreads();
 
@@ -114,42 +139,46 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_
 
     const int row_bytes = FP8 ? p.d_I : p.d_I * 2;
     float* srow = p.scores + (int64_t)tok * p.score_stride;
+    const int pmask = (1 << sv.page_shift) - 1;
+    const int64_t seq_base = (int64_t)b * sv.seq_stride;
 
-    for (int s0 = key_lo; s0 <= key_hi; s0 += 16 * NT) {
-      bf16x8 kb[NT][KS];
-      float ksc[NT];
+    // keys s0 + 16 nt + c (clamped to key_hi: rows past it are masked at the
+    // store) -> raw 16-byte words; bf16 keys: word j = dims kdim(j, g) .. +8,
+    // e4m3 keys: word j = dims 64 j + 16 g .. +16 (k-steps 2j and 2j + 1)
+    auto load = [&](int s0, u32x4 (&raw)[NT][LD], float (&ksc)[NT]) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int s = min(s0 + nt * 16 + c, key_hi);  // clamp: rows past key_hi are masked below
-        const int64_t row = cache_row(sv, b, s);
+        const int s = min(s0 + nt * 16 + c, key_hi);
+        const int64_t row = sv.block_table ? ((int64_t)pages[(s >> sv.page_shift) - page0] << sv.page_shift) + (s & pmask)
+                                           : seq_base + s;
         const uint8_t* krow = p.k_idx + row * row_bytes;
         ksc[nt] = p.k_scale ? p.k_scale[row] : 1.0f;
-        if (FP8) {
 #pragma unroll
-          for (int j = 0; j < KS / 2; ++j) {
-            const u32x4 raw = *(const u32x4*)(krow + j * 64 + g * 16);
-            u32x4 lo, hi;
-            u32x2 a0 = e4m3x4_to_bf16(raw[0], 1.0f), a1 = e4m3x4_to_bf16(raw[1], 1.0f);
-            u32x2 a2 = e4m3x4_to_bf16(raw[2], 1.0f), a3 = e4m3x4_to_bf16(raw[3], 1.0f);
-            lo[0] = a0[0]; lo[1] = a0[1]; lo[2] = a1[0]; lo[3] = a1[1];
-            hi[0] = a2[0]; hi[1] = a2[1]; hi[2] = a3[0]; hi[3] = a3[1];
-            kb[nt][2 * j] = as_bf16x8(lo);
-            kb[nt][2 * j + 1] = as_bf16x8(hi);
-          }
-        } else {
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            kb[nt][ks] = as_bf16x8(*(const u32x4*)(krow + kdim<false>(ks, g) * 2));
-        }
+        for (int j = 0; j < LD; ++j)
+          raw[nt][j] = *(const u32x4*)(krow + (FP8 ? j * 64 + g * 16 : kdim<false>(j, g) * 2));
       }
+    };
+    auto compute = [&](int s0, const u32x4 (&raw)[NT][LD], const float (&ksc)[NT]) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
+        bf16x8 kb[KS];
+#pragma unroll
+        for (int j = 0; j < LD; ++j) {
+          if (FP8) {
+            const u32x2 a0 = e4m3x4_to_bf16(raw[nt][j][0], 1.0f), a1 = e4m3x4_to_bf16(raw[nt][j][1], 1.0f);
+            const u32x2 a2 = e4m3x4_to_bf16(raw[nt][j][2], 1.0f), a3 = e4m3x4_to_bf16(raw[nt][j][3], 1.0f);
+            kb[2 * j] = as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]});
+            kb[2 * j + 1] = as_bf16x8(u32x4{a2[0], a2[1], a3[0], a3[1]});
+          } else {
+            kb[j] = as_bf16x8(raw[nt][j]);
+          }
+        }
         float v = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = mfma16(qa[mt][ks], kb[nt][ks], acc);
+          for (int ks = 0; ks < KS; ++ks) acc = mfma16(qa[mt][ks], kb[ks], acc);
 #pragma unroll
           for (int r = 0; r < 4; ++r) v += w[mt][r] * relu(acc[r] * ksc[nt]);
         }
@@ -157,11 +186,30 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_
         v += shfl_xor(v, 32);
         const int s = s0 + nt * 16 + c;
         if (g == 0 && s <= key_hi) {
-          srow[s] = v;
+          sbuf[wave][s - key_lo] = v;
           atomicAdd(&my_hist[score_key(v) >> (32 - SCORE_HIST_BITS)], 1u);
         }
       }
+    };
+
+    // stage pairs in a loop with its one exit at the bottom (a second exit
+    // would join the back edge with the other stage's loads still pending,
+    // and the loop head would then wait for all of them), odd stage after it
+    u32x4 ra[NT][LD], rb[NT][LD];
+    float sa[NT], sb[NT];
+    const int stages = (key_hi - key_lo) / (16 * NT) + 1;
+    int s0 = key_lo;
+    load(s0, ra, sa);
+    for (int i = 0; i + 2 <= stages; i += 2) {
+      load(s0 + 16 * NT, rb, sb);
+      compute(s0, ra, sa);
+      load(s0 + 32 * NT, ra, sa);
+      compute(s0 + 16 * NT, rb, sb);
+      s0 += 32 * NT;
     }
+    if (stages & 1) compute(s0, ra, sa);
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i <= key_hi - key_lo; i += WAVE) srow[key_lo + i] = sbuf[wave][i];
   }
 
   // ---- merge the workgroup's histogram(s) into the row histogram(s) ---------
@@ -777,6 +825,8 @@ hipError_t launch_mt(const ScoreParams& p, hipStream_t stream, const TimerEvents
     dim3 grid(cdiv(sv.max_q_len, PF_TOKS), sv.num_seqs);
     return launch_kernel(score_prefill_kernel<MT, KS, FP8>, grid, dim3(PF_TOKS * WAVE), stream, t.start, t.stop, p);
   }
+  static_assert(SCORE_MAX_KPW >= 1024 && SCORE_WAVE_KEYS * SCORE_WAVES >= 1024 && SCORE_WAVE_KEYS >= 256,
+                "the LDS page table and score buffers must cover a workgroup's keys");
   if (decode) {
     const int kpw = 1024;
     dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs);
