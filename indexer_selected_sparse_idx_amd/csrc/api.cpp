@@ -111,7 +111,7 @@ size_t attn_ws_bytes(const idx_seqs* s, int H, int top_k) {
   const int S = attn_num_splits(s->num_tokens, H, top_k);
   if (S <= 1) return 0;
   const size_t parts = (size_t)std::max(s->num_tokens, 0) * S * H;
-  return align_up(parts * 512 * sizeof(float)) + align_up(parts * sizeof(float));
+  return align_up(parts * 512 * sizeof(uint16_t)) + align_up(parts * 2 * sizeof(float));
 }
 
 size_t idx_buf_bytes(const idx_seqs* s, int top_k) {
@@ -174,11 +174,11 @@ int run_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, int kv_
   ap.split_len = (top_k + ap.num_splits - 1) / ap.num_splits;
   ap.split_len = (ap.split_len + ATTN_TILE - 1) / ATTN_TILE * ATTN_TILE;
   ap.part_o = nullptr;
-  ap.part_lse = nullptr;
+  ap.part_ls = nullptr;
   if (ap.num_splits > 1) {
     const size_t parts = (size_t)seqs->num_tokens * ap.num_splits * H;
-    ap.part_o = static_cast<float*>(ws);
-    ap.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up(parts * 512 * sizeof(float)));
+    ap.part_o = static_cast<uint16_t*>(ws);
+    ap.part_ls = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up(parts * 512 * sizeof(uint16_t)));
   }
   if (launch_attn(ap, kv_dtype == IDX_KV_FP8_656, stream) != hipSuccess) return IDX_ERR_HIP;
   return IDX_OK;

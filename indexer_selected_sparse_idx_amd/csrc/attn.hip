@@ -366,31 +366,50 @@ __device__ __forceinline__ void v_phase(WaveAcc& a, const uint8_t* buf, const Ti
   v_steps<SPLITP>(a, buf, ad, op, at_step, std::make_integer_sequence<int, DV_TILES>());
 }
 
-// Normalise and store the wave's O^T (and lse) for its 32 heads.
+// Normalise and store the wave's O^T (and lse) for its 32 heads.  A split's
+// partial O goes out as fp16 times a power-of-two scale per (token, split,
+// head): the head's largest |O| is brought just below 2^15, so every value
+// keeps 11 significant bits relative to that maximum (the split weights of
+// the merge are at most 1), at half the bytes of fp32 partials.
 __device__ __forceinline__ void write_result(const WaveAcc& a, const AttnParams& p, int tok, int split, int head,
                                              bool head_ok, int h) {
   const float l_tot = pair_sum(a.l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_v = l_tot > 0.0f ? (a.m_ref + __builtin_amdgcn_logf(l_tot)) * LN2 : -INFINITY;
-  if (!head_ok) return;
-  float* orow;
-  float* lrow;
   if (p.num_splits == 1) {
-    orow = p.out + ((int64_t)tok * p.H + head) * LATENT;
-    lrow = p.lse ? p.lse + (int64_t)tok * p.H + head : nullptr;
-  } else {
-    const int64_t pi = ((int64_t)tok * p.num_splits + split) * p.H + head;
-    orow = p.part_o + pi * LATENT;
-    lrow = p.part_lse + pi;
+    if (!head_ok) return;
+    float* orow = p.out + ((int64_t)tok * p.H + head) * LATENT;
+#pragma unroll
+    for (int nt = 0; nt < DV_TILES; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 v = {a.o[nt][4 * i], a.o[nt][4 * i + 1], a.o[nt][4 * i + 2], a.o[nt][4 * i + 3]};
+        *(f32x4*)(orow + nt * 32 + i * 8 + h * 4) = v * inv;
+      }
+    if (h == 0 && p.lse) p.lse[(int64_t)tok * p.H + head] = lse_v;
+    return;
   }
+  float amax = 0.0f;
+#pragma unroll
+  for (int nt = 0; nt < DV_TILES; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(a.o[nt][r]));
+  amax = pair_max(amax) * inv;
+  // amax < 2^e; exponents below -100 are raised so the factor stays finite
+  const int e = amax > 0.0f ? max(__builtin_amdgcn_frexp_expf(amax), -100) : 0;
+  const float f = __builtin_amdgcn_ldexpf(inv, 15 - e);
+  const float sc = amax > 0.0f ? __builtin_amdgcn_ldexpf(1.0f, e - 15) : 0.0f;
+  if (!head_ok) return;
+  const int64_t pi = ((int64_t)tok * p.num_splits + split) * p.H + head;
+  uint16_t* orow = p.part_o + pi * LATENT;
 #pragma unroll
   for (int nt = 0; nt < DV_TILES; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x4 v = {a.o[nt][4 * i], a.o[nt][4 * i + 1], a.o[nt][4 * i + 2], a.o[nt][4 * i + 3]};
-      *(f32x4*)(orow + nt * 32 + i * 8 + h * 4) = v * inv;
+      const f32x4 v = f32x4{a.o[nt][4 * i], a.o[nt][4 * i + 1], a.o[nt][4 * i + 2], a.o[nt][4 * i + 3]} * f;
+      *(f16x4*)(orow + nt * 32 + i * 8 + h * 4) = __builtin_convertvector(v, f16x4);
     }
-  if (h == 0 && lrow) *lrow = lse_v;
+  if (h == 0) *(f32x2*)(p.part_ls + 2 * pi) = f32x2{lse_v, sc};
 }
 
 // Work item of a workgroup.  Workgroups are dispatched round-robin over the
@@ -710,7 +729,8 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
   write_result(a, p, w.tok, w.split, head, head_ok, h);
 }
 
-// Merge split partials: lse = log sum_s exp(lse_s); O = sum_s exp(lse_s - lse) O_s.
+// Merge split partials: lse = log sum_s exp(lse_s); O = sum_s exp(lse_s - lse) O_s,
+// with O_s = scale_s * (stored fp16 values).
 // One workgroup per (token, pair of heads), 128 lanes per head, each lane 4
 // of the 512 values.  The partials of COMBINE_BATCH splits are loaded before
 // any is used (one memory latency per batch, not per split); a split whose
@@ -726,24 +746,25 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
   const int S = p.num_splits;
   const int64_t base = (int64_t)tok * S * p.H + h;
   float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, p.part_lse[base + (int64_t)s * p.H]);
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, p.part_ls[2 * (base + (int64_t)s * p.H)]);
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float wsum = 0.0f;
   if (mx != -INFINITY) {
     for (int s0 = 0; s0 < S; s0 += COMBINE_BATCH) {
-      f32x4 v[COMBINE_BATCH];
-      float wgt[COMBINE_BATCH];
+      f16x4 v[COMBINE_BATCH];
+      f32x2 ls[COMBINE_BATCH];
 #pragma unroll
       for (int j = 0; j < COMBINE_BATCH; ++j) {
         const int64_t pi = base + (int64_t)min(s0 + j, S - 1) * p.H;
-        v[j] = *(const f32x4*)(p.part_o + pi * LATENT + lane * 4);
-        wgt[j] = s0 + j < S ? expf(p.part_lse[pi] - mx) : 0.0f;
+        v[j] = *(const f16x4*)(p.part_o + pi * LATENT + lane * 4);
+        ls[j] = *(const f32x2*)(p.part_ls + 2 * pi);
       }
 #pragma unroll
       for (int j = 0; j < COMBINE_BATCH; ++j) {
-        if (wgt[j] > 0.0f) {
-          wsum += wgt[j];
-          acc += wgt[j] * v[j];
+        const float wgt = s0 + j < S ? expf(ls[j][0] - mx) : 0.0f;
+        if (wgt > 0.0f) {
+          wsum += wgt;
+          acc += (wgt * ls[j][1]) * __builtin_convertvector(v[j], f32x4);
         }
       }
     }

@@ -87,8 +87,8 @@ struct AttnParams {
   float* lse;              // [T, H] nullable
   int num_splits;
   int split_len;           // index entries per split (multiple of the tile)
-  float* part_o;           // [T, num_splits, H, 512] when num_splits > 1
-  float* part_lse;         // [T, num_splits, H]
+  uint16_t* part_o;        // fp16 [T, num_splits, H, 512] when num_splits > 1: split O / its scale
+  float* part_ls;          // [T, num_splits, H, 2]: (lse of the split, power-of-two scale of its stored O)
 };
 
 // Kernel launchers (asynchronous, on `stream`).  Each records the armed

@@ -140,6 +140,7 @@ def attn_error(got, want):
 
 def check_attention(got_out, got_lse, want_out, want_lse, tol, context=""):
     err = attn_error(got_out, want_out)
+    log("%s: attention max-abs error %.3g x RMS (bound %.3g)" % (context, err, tol))
     assert err <= tol, "%s: max-abs error / RMS = %.4g > %.3g" % (context, err, tol)
     finite = np.isfinite(want_lse)
     assert np.array_equal(np.isfinite(got_lse), finite), context + ": lse finiteness"
