@@ -45,30 +45,57 @@ namespace {
 
 constexpr int TOPK_THREADS = 1024;
 constexpr int TOPK_WAVES = TOPK_THREADS / WAVE;
-constexpr int CAP = 12288;   // LDS candidate capacity (keys + positions)
+constexpr int CAP = 32768;   // LDS candidate capacity (one packed word each)
 constexpr int UNROLL = 4;   // 4-key vector accesses in flight per lane
 
-// Key source: the LDS copy of the row, or the fp32 score row itself.
+// Key source: candidate words in LDS (low key bits << 11 | offset in the
+// chunk, as the compaction pass packs them; `hi` supplies the key bits above
+// them), or the fp32 score row itself.
 template <bool IN_LDS>
 struct Keys {
   const uint32_t* lds;
   const float* row;
   int n;
+  uint32_t hi;
+  __device__ __forceinline__ uint32_t from_word(uint32_t w) const { return (w >> 11) | hi; }
   // keys i .. i+3 (i % 4 == 0); positions >= n read as 0 (never selected)
   __device__ __forceinline__ u32x4 get4(int i) const {
     u32x4 k;
     if (i + 3 < n) {
       if (IN_LDS) {
-        k = *(const u32x4*)(lds + i);
+        const u32x4 w = *(const u32x4*)(lds + i);
+        k = u32x4{from_word(w[0]), from_word(w[1]), from_word(w[2]), from_word(w[3])};
       } else {
         const f32x4 f = *(const f32x4*)(row + i);
         k = u32x4{score_key(f[0]), score_key(f[1]), score_key(f[2]), score_key(f[3])};
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) k[e] = i + e < n ? (IN_LDS ? lds[i + e] : score_key(row[i + e])) : 0u;
+      for (int e = 0; e < 4; ++e) k[e] = i + e < n ? (IN_LDS ? from_word(lds[i + e]) : score_key(row[i + e])) : 0u;
     }
     return k;
+  }
+};
+
+// Position of list entry i: the entry itself (a whole score row), or, for
+// the candidate words, the chunk holding entry i (the last chunk whose first
+// candidate is at or before i, from the exclusive prefix sums of the
+// per-chunk counts) plus the word's offset.  Only entries that are written
+// out are looked up.
+struct RowPos {
+  __device__ __forceinline__ int operator()(int i) const { return i; }
+};
+struct CandPos {
+  const uint32_t* w;
+  const uint32_t* choff;
+  int nch;
+  __device__ __forceinline__ int operator()(int i) const {
+    int lo = 0, hi = nch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (choff[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
+    }
+    return lo * TOPK_CHUNK + (int)(w[i] & (TOPK_CHUNK - 1));
   }
 };
 
@@ -99,10 +126,9 @@ struct Digits {
 };
 
 // Select the m largest of n keys (ties: lowest index first) and write their
-// positions (pos[i], or i when pos is null) to out[0 .. m).  Every key's top
-// FIXED bits equal prefix0.
-template <bool IN_LDS, int FIXED>
-__device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out, const int32_t* pos, uint32_t* hist,
+// positions pos(i) to out[0 .. m).  Every key's top FIXED bits equal prefix0.
+template <bool IN_LDS, int FIXED, typename Pos>
+__device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out, const Pos& pos, uint32_t* hist,
                            uint32_t* whist, uint32_t* wcnt, uint32_t prefix0) {
   typedef Digits<FIXED> D;
   __shared__ uint32_t sh_digit, sh_above, sh_whole;
@@ -231,11 +257,11 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if ((fg >> e) & 1u) {
-        if (pg < n_gt) out[pg] = pos ? pos[i + e] : i + e;
+        if (pg < n_gt) out[pg] = pos(i + e);
         ++pg;
       }
       if ((fe >> e) & 1u) {
-        if (pe < need) out[n_gt + pe] = pos ? pos[i + e] : i + e;
+        if (pe < need) out[n_gt + pe] = pos(i + e);
         ++pe;
       }
     }
@@ -256,8 +282,10 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
 //           (low 21 key bits << 11) | (offset in the chunk); the two counts
 //           go to a per-chunk table.
 //   select  one workgroup per row: the positions above d1 go to the output,
-//           chunk after chunk; the d1 keys go into LDS in position order and
-//           the radix select above takes the remaining m - above1 of them.
+//           chunk after chunk; the packed d1 words go into LDS in position
+//           order (4 bytes each; a selected word's chunk is found from the
+//           per-chunk offsets) and the radix select above takes the
+//           remaining m - above1 of them.
 // Rows with t + 1 <= K take every position.  Rows whose d1 bucket exceeds the
 // LDS capacity (massive ties), or with more chunks than the select tracks,
 // are left alone by emit and select over the whole score row.
@@ -336,7 +364,7 @@ __global__ __launch_bounds__(TKE_THREADS) void topk_emit_kernel(TopkParams p) {
   if (c0 >= n) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float* row = p.scores + (int64_t)tok * p.score_stride;
-  const Keys<false> src{nullptr, row, n};
+  const Keys<false> src{nullptr, row, n, 0u};
   const int i = c0 + 8 * tid;
   const u32x4 k0 = i < n ? src.get4(i) : u32x4{0u, 0u, 0u, 0u};
   const u32x4 k1 = i + 4 < n ? src.get4(i + 4) : u32x4{0u, 0u, 0u, 0u};
@@ -383,8 +411,7 @@ __global__ __launch_bounds__(TKE_THREADS) void topk_emit_kernel(TopkParams p) {
 }
 
 __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkParams p) {
-  __shared__ __attribute__((aligned(16))) uint32_t cand_key[CAP];
-  __shared__ __attribute__((aligned(16))) int32_t cand_pos[CAP];
+  __shared__ __attribute__((aligned(16))) uint32_t cand_w[CAP];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t whist[TOPK_WAVES * 256];
   __shared__ uint32_t wcnt[2 * TOPK_WAVES];
@@ -412,7 +439,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkParams p)
     return;
   }
   if (r.mode == TK_WHOLE_ROW) {
-    select_row<false, 0>(Keys<false>{nullptr, row, n}, n, m, out, nullptr, hist, whist, wcnt, 0u);
+    select_row<false, 0>(Keys<false>{nullptr, row, n, 0u}, n, m, out, RowPos{}, hist, whist, wcnt, 0u);
     return;
   }
 
@@ -448,15 +475,12 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkParams p)
     const uint32_t* seg = (const uint32_t*)(row + (int64_t)c * TOPK_CHUNK);
     const uint32_t ng = chcnt[0][c], ne = chcnt[1][c], og = choff[0][c], oe = choff[1][c];
     for (uint32_t j = lane; j < ng; j += WAVE) out[og + j] = (int32_t)seg[j];
-    for (uint32_t j = lane; j < ne; j += WAVE) {
-      const uint32_t w = seg[ng + j];
-      cand_key[oe + j] = (r.d1 << (32 - SCORE_HIST_BITS)) | (w >> 11);
-      cand_pos[oe + j] = c * TOPK_CHUNK + (int32_t)(w & (TOPK_CHUNK - 1));
-    }
+    for (uint32_t j = lane; j < ne; j += WAVE) cand_w[oe + j] = seg[ng + j];
   }
   __syncthreads();
-  select_row<true, SCORE_HIST_BITS>(Keys<true>{cand_key, nullptr, (int)r.cnt1}, (int)r.cnt1, m - (int)r.above1,
-                                    out + r.above1, cand_pos, hist, whist, wcnt, r.d1);
+  select_row<true, SCORE_HIST_BITS>(Keys<true>{cand_w, nullptr, (int)r.cnt1, r.d1 << (32 - SCORE_HIST_BITS)},
+                                    (int)r.cnt1, m - (int)r.above1, out + r.above1, CandPos{cand_w, choff[1], nch},
+                                    hist, whist, wcnt, r.d1);
 }
 
 }  // namespace
