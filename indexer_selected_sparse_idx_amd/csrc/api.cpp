@@ -27,8 +27,6 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 int log2i(int v) { int s = 0; while ((1 << s) < v) ++s; return s; }
 
-// Rows of the score workspace are padded to a multiple of 64 floats.
-int64_t score_stride(const idx_seqs* s) { return ((int64_t)s->max_ctx_len + 63) / 64 * 64; }
 
 int check_seqs(const idx_seqs* s) {
   if (!s) return IDX_ERR_INVALID_ARG;
@@ -94,7 +92,17 @@ int check_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, int k
   return IDX_OK;
 }
 
-// score workspace: fp32 score rows, then the per-row key histograms
+// Pitch of a score-workspace row in 4-byte words: one fp32 score per
+// position (positions padded to a multiple of 64) for the decode-style
+// kernels; for the prefill kernel two words (a (key, position) candidate
+// pair) per position plus one spare pair (its 16-byte list loads read pairs
+// two at a time), padded the same way.
+int64_t score_stride(const idx_seqs* s) {
+  if (score_selects(make_view(s))) return 2 * (((int64_t)s->max_ctx_len + 1 + 63) / 64 * 64);
+  return ((int64_t)s->max_ctx_len + 63) / 64 * 64;
+}
+
+// score workspace: score rows, then the per-row key histograms
 size_t score_rows_bytes(const idx_seqs* s) {
   return align_up((size_t)std::max(s->num_tokens, 0) * (size_t)score_stride(s) * sizeof(float));
 }

@@ -245,11 +245,13 @@ __global__ void zero_kernel(uint32_t* p, int64_t n4) {
 // keys x 32 dims) with the query operand in registers and the key operand
 // read from LDS; ReLU and the head weights fold into registers; the 4 lane
 // groups (4 heads each per M-tile) are summed across lanes.  Lane (g, c)
-// keeps sub-tile g, so one 256-byte store per tile writes the token's 64
-// scores.  Because the workgroup covers the whole row of each of its
-// tokens, it builds the rows' key histograms in LDS and, once every score is
-// written, each wave selects its token's Top-K itself (wave_select above):
-// no global atomics, no clearing pass and no separate selection launch.
+// keeps sub-tile g: the wave's 64 scores of a tile, one per lane in position
+// order, go into the row's LDS histogram and, where they reach the running
+// threshold bound, into the row's candidate list (one ballot, one store).
+// Because the workgroup covers the whole row of each of its tokens, each
+// wave then selects its token's Top-K itself from the list (wave_select_list
+// above): no global atomics, no clearing pass and no separate selection
+// launch.
 //
 // Key rows in LDS: the 16-byte chunk ch of key row r sits at chunk
 // ch ^ swz(r) of the row, so the 16 keys of a sub-tile read at one logical
@@ -298,22 +300,29 @@ __device__ __forceinline__ float reduce_scatter4(const float (&x)[4], int g) {
 // kernel: the m = min(K, t + 1) largest scores, ties to the lower position
 // (the selection of the fused indexer: "Internal Fusion of the Indexer" in
 // Day 0 Inference Support for New LLM Architectures; the tie rule is this
-// library's reading).  The row's key histogram (top 11 bits of the
-// order-preserving key) is already in the wave's LDS histogram.  One pass over
-// the row (from L2) histograms the next 11 key bits of the keys in the chosen
-// top bucket; a second pass writes, in position order, the positions of the
-// keys above the chosen 22-bit prefix and keeps those with the prefix
-// (usually a handful: one score value for integer-valued scores) in LDS,
-// where a 10-bit histogram fixes the exact threshold key tau and the first
-// keys equal to it are taken.  When the prefix holds more keys than the LDS
-// list, a third pass histograms the last 10 bits over the row instead and a
-// fourth writes the positions.
+// library's reading).
+//
+// The score loop keeps, per row, a candidate list instead of the scores: in
+// position order, (order-preserving key, position) for every key whose top
+// 11 bits reach a running lower bound of the row's threshold bucket (the
+// bucket of the K-th largest key seen so far, refreshed from the row's LDS
+// histogram every 16 tiles).  The K-th largest of a prefix never exceeds
+// the K-th largest of the row, so the list holds every key the selection can
+// take.  The row's complete histogram of the top 11 bits then fixes the
+// threshold bucket d1; one pass over the list writes the positions above d1
+// and compacts the d1 keys in place (still in position order) while
+// histogramming their next 11 bits; a pass over those picks the 22-bit
+// prefix and keeps the keys with it (usually a handful: one score value for
+// integer-valued scores) in LDS, where a 10-bit histogram fixes the exact
+// threshold key tau and the first keys equal to it are taken.  When the
+// prefix holds more keys than the LDS list, two more passes over the d1 keys
+// do the same without it.
 // ---------------------------------------------------------------------------
 
 // The bin d of an NB-bin LDS histogram (bins in key order) holding the
 // want-th largest key: S(> d) < want <= S(>= d); above = S(> d), cnt = h[d].
-template <int NB>
-__device__ __forceinline__ void wave_pick(const uint32_t* h, uint32_t want, int lane, uint32_t& d, uint32_t& above,
+template <int NB, typename H>
+__device__ __forceinline__ void wave_pick(const H* h, uint32_t want, int lane, uint32_t& d, uint32_t& above,
                                           uint32_t& cnt) {
   constexpr int PER = NB / WAVE;
   uint32_t v[PER];
@@ -347,175 +356,28 @@ __device__ __forceinline__ void wave_pick(const uint32_t* h, uint32_t want, int 
   cnt = __builtin_amdgcn_readlane(fc, src);
 }
 
-// keys i .. i + 3 of a score row of n keys (positions >= n read as key 0,
-// below every score)
-__device__ __forceinline__ u32x4 row_keys4(const float* row, int i, int n) {
-  u32x4 k;
-  if (i + 3 < n) {
-    const f32x4 f = *(const f32x4*)(row + i);
-    k = u32x4{score_key(f[0]), score_key(f[1]), score_key(f[2]), score_key(f[3])};
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) k[e] = i + e < n ? score_key(row[i + e]) : 0u;
-  }
-  return k;
+// The selection reads and writes the score rows and the output through
+// global-address-space pointers (plain global loads and stores; through a
+// generic pointer every access is a FLAT one that also waits on the LDS
+// counter).
+typedef __attribute__((address_space(1))) float g_f32;
+typedef __attribute__((address_space(1))) const f32x4 g_f32x4;
+typedef __attribute__((address_space(1))) uint32_t g_u32;
+typedef __attribute__((address_space(1))) int32_t g_i32;
+typedef __attribute__((address_space(3))) uint32_t l_u32;   // LDS
+__device__ __forceinline__ void lds_inc(l_u32* p) {
+  __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// f(i, keys i .. i + 3) over the row, 16 KiB in flight per wave
-template <typename F>
-__device__ __forceinline__ void stream_row(const float* row, int n, int lane, F&& f) {
-  constexpr int U = 16;
-  for (int i0 = 0; i0 < n; i0 += 256 * U) {
-    u32x4 k[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + 256 * u + 4 * lane;
-      k[u] = i < n ? row_keys4(row, i, n) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) f(i0 + 256 * u + 4 * lane, k[u]);
-  }
-}
-
-// Positions of the keys selected by `take(key)` (ballot per element), in
-// position order, to out[o ..); o advances by their count.
-template <typename P>
-__device__ __forceinline__ void emit_ordered(int i, const u32x4& k, int n, int lane, int32_t* out, uint32_t& o,
-                                             P&& take) {
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint64_t bm[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) bm[e] = __builtin_amdgcn_ballot_w64(i + e < n && take(k[e]));
-  uint32_t pos = o;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) pos += __popcll(bm[e] & below);
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if ((bm[e] >> lane) & 1ull) out[pos++] = i + e;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) o += __popcll(bm[e]);
-}
-
-// h: the wave's 2048-bin LDS histogram of the row's top 11 key bits; list:
-// the wave's LDS scratch of list_cap words.  The general form, for rows of
-// any length: every pass reads the whole row.
-__device__ void wave_select_rows(const float* row, int n, int K, int32_t* out, uint32_t* h, uint32_t* list,
-                                 int list_cap, int lane) {
-  const int m = min(K, n);
-  for (int i = m + lane; i < K; i += WAVE) out[i] = -1;
-  if (m == n) {
-    for (int i = lane; i < n; i += WAVE) out[i] = i;
-    return;
-  }
-  uint32_t d1, above1, cnt1, d2, above2, cnt2, d3, above3, cnt3;
-  wave_pick<SCORE_HIST_BINS>(h, (uint32_t)m, lane, d1, above1, cnt1);
-  const uint32_t rem1 = (uint32_t)m - above1;
-  // key bits 20..10 of the keys in bucket d1
-  for (int j = lane; j < SCORE_HIST_BINS; j += WAVE) h[j] = 0u;
-  stream_row(row, n, lane, [&](int i, u32x4 k) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (i + e < n && (k[e] >> 21) == d1) atomicAdd(&h[(k[e] >> 10) & 2047u], 1u);
-  });
-  wave_pick<SCORE_HIST_BINS>(h, rem1, lane, d2, above2, cnt2);
-  const uint32_t rem2 = rem1 - above2;
-  const uint32_t pre22 = (d1 << 11) | d2;
-  const uint32_t n_above22 = above1 + above2;  // keys whose 22-bit prefix is larger
-  for (int j = lane; j < 1024; j += WAVE) h[j] = 0u;
-
-  if (cnt2 <= (uint32_t)list_cap && n <= (1 << 22)) {
-    // positions above the prefix to the output; the prefix keys to the list
-    // as (low 10 key bits << 22 | position), both in position order, and
-    // their low 10 bits into the histogram
-    uint32_t og = 0, ol = 0;
-    const uint64_t below = (1ull << lane) - 1ull;
-    stream_row(row, n, lane, [&](int i, u32x4 k) {
-      emit_ordered(i, k, n, lane, out, og, [&](uint32_t key) { return (key >> 10) > pre22; });
-      uint64_t bm[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bm[e] = __builtin_amdgcn_ballot_w64(i + e < n && (k[e] >> 10) == pre22);
-      uint32_t q = ol;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) q += __popcll(bm[e] & below);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((bm[e] >> lane) & 1ull) {
-          list[q++] = ((k[e] & 1023u) << 22) | (uint32_t)(i + e);
-          atomicAdd(&h[k[e] & 1023u], 1u);
-        }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ol += __popcll(bm[e]);
-    });
-    wave_pick<1024>(h, rem2, lane, d3, above3, cnt3);
-    const uint32_t need = rem2 - above3;  // list keys equal to tau taken, lowest positions first
-    int32_t* out_a = out + n_above22;     // list keys above tau, then the `need` first equal ones
-    int32_t* out_e = out_a + above3;
-    uint32_t oa = 0, oe = 0;
-    for (uint32_t j0 = 0; j0 < cnt2; j0 += WAVE) {
-      const uint32_t j = j0 + lane;
-      const uint32_t v = j < cnt2 ? list[j] : 0u;
-      const uint32_t low = v >> 22;
-      const uint64_t ma = __builtin_amdgcn_ballot_w64(j < cnt2 && low > d3);
-      const uint64_t me = __builtin_amdgcn_ballot_w64(j < cnt2 && low == d3);
-      const int32_t pos = (int32_t)(v & ((1u << 22) - 1u));
-      if ((ma >> lane) & 1ull) out_a[oa + __popcll(ma & below)] = pos;
-      if ((me >> lane) & 1ull) {
-        const uint32_t r = oe + __popcll(me & below);
-        if (r < need) out_e[r] = pos;
-      }
-      oa += __popcll(ma);
-      oe += __popcll(me);
-    }
-    return;
-  }
-
-  // the prefix holds too many keys for the list: key bits 9..0 over the row
-  stream_row(row, n, lane, [&](int i, u32x4 k) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (i + e < n && (k[e] >> 10) == pre22) atomicAdd(&h[k[e] & 1023u], 1u);
-  });
-  wave_pick<1024>(h, rem2, lane, d3, above3, cnt3);
-  const uint32_t tau = (pre22 << 10) | d3;
-  const uint32_t need = rem2 - above3;  // keys equal to tau taken, lowest positions first
-  const uint32_t n_gt = (uint32_t)m - need;
-  // positions, in order: keys above tau to out[0 .. n_gt), the first `need`
-  // keys equal to tau after them
-  uint32_t og = 0, oe = 0;
-  stream_row(row, n, lane, [&](int i, u32x4 k) {
-    emit_ordered(i, k, n, lane, out, og, [&](uint32_t key) { return key > tau; });
-    const uint64_t below = (1ull << lane) - 1ull;
-    uint64_t be[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) be[e] = __builtin_amdgcn_ballot_w64(i + e < n && k[e] == tau);
-    uint32_t pe = oe;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pe += __popcll(be[e] & below);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if ((be[e] >> lane) & 1ull) {
-        if (pe < need) out[n_gt + pe] = i + e;
-        ++pe;
-      }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) oe += __popcll(be[e]);
-  });
-}
-
-// The usual form, for rows of up to 64 chunks of SEL_CHUNK keys: the one pass
-// over the whole row also compacts the keys of the top bucket d1, in position
-// order, into the storage of their chunk (just read by this wave, needed by
-// no one else) as (low 21 key bits << 11 | offset in the chunk); lane c keeps
-// chunk c's count.  Every later pass reads only those (about a tenth of the
-// row for smooth score distributions).
-constexpr int SEL_CHUNK = 2048;
-__device__ void wave_select(float* row, int n, int K, int32_t* out, uint32_t* h, uint32_t* list, int list_cap,
-                            int lane) {
-  const int nch = cdiv(n, SEL_CHUNK);
-  if (nch > WAVE) {
-    wave_select_rows(row, n, K, out, h, list, list_cap, lane);
-    return;
-  }
+// h: the row's 2048-bin LDS histogram of the top 11 key bits (the whole
+// row); cand: the row's L candidate pairs (key, position) in position order;
+// list: the wave's LDS scratch of list_cap words.
+__device__ void wave_select_list(uint32_t* cand_, uint32_t L, int n, int K, int32_t* out_, uint32_t* h_,
+                                 uint32_t* list_, int list_cap, int lane) {
+  l_u32* h = (l_u32*)h_;
+  l_u32* list = (l_u32*)list_;
+  g_u32* cand = (g_u32*)cand_;
+  g_i32* out = (g_i32*)out_;
   const int m = min(K, n);
   for (int i = m + lane; i < K; i += WAVE) out[i] = -1;
   if (m == n) {
@@ -528,83 +390,111 @@ __device__ void wave_select(float* row, int n, int K, int32_t* out, uint32_t* h,
   const uint32_t rem1 = (uint32_t)m - above1;
   for (int j = lane; j < SCORE_HIST_BINS; j += WAVE) h[j] = 0u;
 
-  // pass over the row: positions above d1 to out[0 .. above1); d1 keys
-  // compacted into their chunk, their key bits 20..10 into the histogram
-  uint32_t* words = (uint32_t*)row;
-  uint32_t og = 0, ccnt = 0;
-  for (int c = 0; c < nch; ++c) {
-    const int c0 = c * SEL_CHUNK;
-    u32x4 k[SEL_CHUNK / 256];
+  // Pass over the list, 128 pairs per 16-byte load of the wave (lane l holds
+  // pairs 2 l and 2 l + 1 of a group, so lane order is position order), the
+  // next batch of groups loaded before the current one is processed:
+  // positions above d1 to out[0 .. above1); d1 pairs compacted in place at
+  // the front of the list (they land behind every pair still to be read),
+  // their key bits 20..10 into the histogram.
+  constexpr int UB = 4;  // groups per batch
+  // groups past the list load its last pairs (the row holds one spare pair
+  // beyond the longest list, so a load never leaves the row)
+  const uint32_t last = L > 0 ? (L - 1) & ~1u : 0u;
+  auto load_batch = [&](uint32_t b0, u32x4 (&r)[UB]) {
 #pragma unroll
-    for (int u = 0; u < SEL_CHUNK / 256; ++u) {
-      const int i = c0 + 256 * u + 4 * lane;
-      k[u] = i < n ? row_keys4(row, i, n) : u32x4{0u, 0u, 0u, 0u};
-    }
-    uint32_t oc = 0;
+    for (int u = 0; u < UB; ++u) r[u] = *(const __attribute__((address_space(1))) u32x4*)(
+        cand + 2 * min(b0 + 128u * u + 2u * lane, last));
+  };
+  uint32_t og = 0, cw = 0;
+  auto do_batch = [&](uint32_t b0, const u32x4 (&r)[UB]) {
 #pragma unroll
-    for (int u = 0; u < SEL_CHUNK / 256; ++u) {
-      const int i = c0 + 256 * u + 4 * lane;
-      emit_ordered(i, k[u], n, lane, out, og, [&](uint32_t key) { return (key >> 21) > d1; });
-      uint64_t bm[4];
+    for (int u = 0; u < UB; ++u) {
+      const uint32_t j = b0 + 128u * u + 2u * lane;
+      const uint32_t key[2] = {r[u][0], r[u][2]};
+      const uint32_t pos[2] = {r[u][1], r[u][3]};
+      uint64_t ba[2], bd[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bm[e] = __builtin_amdgcn_ballot_w64(i + e < n && (k[u][e] >> 21) == d1);
-      uint32_t q = oc;
+      for (int e = 0; e < 2; ++e) {
+        const bool ok = j + e < L;
+        ba[e] = __builtin_amdgcn_ballot_w64(ok && (key[e] >> 21) > d1);
+        bd[e] = __builtin_amdgcn_ballot_w64(ok && (key[e] >> 21) == d1);
+      }
+      uint32_t pa = og + __popcll(ba[0] & below) + __popcll(ba[1] & below);
+      uint32_t pd = cw + __popcll(bd[0] & below) + __popcll(bd[1] & below);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) q += __popcll(bm[e] & below);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((bm[e] >> lane) & 1ull) {
-          // (the compacted entries stay below the keys still to be read: a
-          // chunk's keys are all loaded before its first entry is written)
-          words[c0 + q++] = ((k[u][e] & 0x1FFFFFu) << 11) | (uint32_t)(i + e - c0);
-          atomicAdd(&h[(k[u][e] >> 10) & 2047u], 1u);
+      for (int e = 0; e < 2; ++e) {
+        if (((ba[e] >> lane) & 1ull) && pa < above1) out[pa] = (int32_t)pos[e];
+        pa += (ba[e] >> lane) & 1ull;
+        if ((bd[e] >> lane) & 1ull) {
+          *(__attribute__((address_space(1))) u32x2*)(cand + 2 * pd++) = u32x2{key[e], pos[e]};
+          lds_inc(&h[(key[e] >> 10) & 2047u]);
         }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) oc += __popcll(bm[e]);
+      }
+      og += __popcll(ba[0]) + __popcll(ba[1]);
+      cw += __popcll(bd[0]) + __popcll(bd[1]);
     }
-    if (lane == c) ccnt = oc;
+  };
+  if (L > 0) {
+    // straight-line body (loads clamped, entries past the list are no-ops):
+    // with a conditional half the compiler waits for every load in flight
+    // at the loop head
+    u32x4 ra[UB], rb[UB];
+    constexpr uint32_t STEP = 128u * UB;
+    load_batch(0, ra);
+    for (uint32_t b0 = 0; b0 < L; b0 += 2 * STEP) {
+      load_batch(b0 + STEP, rb);
+      do_batch(b0, ra);
+      load_batch(b0 + 2 * STEP, ra);
+      do_batch(b0 + STEP, rb);
+    }
   }
   wave_pick<SCORE_HIST_BINS>(h, rem1, lane, d2, above2, cnt2);
   const uint32_t rem2 = rem1 - above2;
   for (int j = lane; j < 1024; j += WAVE) h[j] = 0u;
-  int32_t* out_2 = out + above1;  // d1 keys above d2, then what the last bits decide
-  wait_vmcnt<0>();  // the compacted entries are written
+  g_i32* out_2 = out + above1;  // d1 keys above d2, then what the last bits decide
+  wait_vmcnt<0>();  // the compacted pairs are written
+  // (the list holds every key of the row at or above d1, so og == above1
+  // and cw == cnt1; the passes below go by the pairs actually compacted and
+  // the writes stay inside the row's m entries regardless)
+  const uint32_t nd1 = min(cw, cnt1);
 
-  // f(entry, valid, c0) over the compacted d1 keys, chunk after chunk (read
-  // at device scope: this wave's own stores must not be shadowed by lines of
-  // the scores it read before)
+  // f(key, position, valid) over the nd1 compacted d1 pairs, 4 per lane in
+  // flight (read at device scope: this wave's own stores must not be
+  // shadowed by lines of the list it read before)
   auto over_d1 = [&](auto&& f) {
-    for (int c = 0; c < nch; ++c) {
-      const uint32_t cc = __builtin_amdgcn_readlane(ccnt, c);
-      for (uint32_t j0 = 0; j0 < cc; j0 += WAVE) {
-        const uint32_t j = j0 + lane;
-        const uint32_t w =
-            j < cc ? __hip_atomic_load(words + c * SEL_CHUNK + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-        f(w, j < cc, c * SEL_CHUNK);
+    const uint64_t* pairs = (const uint64_t*)cand_;
+    for (uint32_t j0 = 0; j0 < nd1; j0 += 4 * WAVE) {
+      uint64_t w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t j = j0 + WAVE * u + lane;
+        w[u] = j < nd1 ? __hip_atomic_load(pairs + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) f((uint32_t)w[u], (uint32_t)(w[u] >> 32), j0 + WAVE * u + lane < nd1);
     }
   };
   if (cnt2 <= (uint32_t)list_cap && n <= (1 << 22)) {
     // d1 keys above d2 to the output; those in d2 to the list as (low 10
     // key bits << 22 | position), with their low bits into the histogram
     uint32_t oa = 0, ol = 0;
-    over_d1([&](uint32_t w, bool ok, int c0) {
-      const uint32_t sub = w >> 21;
-      const int32_t pos = c0 + (int32_t)(w & (SEL_CHUNK - 1));
+    over_d1([&](uint32_t key, uint32_t pos, bool ok) {
+      const uint32_t sub = (key >> 10) & 2047u;
       const uint64_t ma = __builtin_amdgcn_ballot_w64(ok && sub > d2);
       const uint64_t mb = __builtin_amdgcn_ballot_w64(ok && sub == d2);
-      if ((ma >> lane) & 1ull) out_2[oa + __popcll(ma & below)] = pos;
-      if ((mb >> lane) & 1ull) {
-        list[ol + __popcll(mb & below)] = (((w >> 11) & 1023u) << 22) | (uint32_t)pos;
-        atomicAdd(&h[(w >> 11) & 1023u], 1u);
+      const uint32_t ra = oa + __popcll(ma & below), rb = ol + __popcll(mb & below);
+      if (((ma >> lane) & 1ull) && ra < above2) out_2[ra] = (int32_t)pos;
+      if (((mb >> lane) & 1ull) && rb < cnt2) {
+        list[rb] = ((key & 1023u) << 22) | pos;
+        lds_inc(&h[key & 1023u]);
       }
       oa += __popcll(ma);
       ol += __popcll(mb);
     });
     wave_pick<1024>(h, rem2, lane, d3, above3, cnt3);
     const uint32_t need = rem2 - above3;  // list keys equal to tau taken, lowest positions first
-    int32_t* out_a = out_2 + above2;
-    int32_t* out_e = out_a + above3;
+    g_i32* out_a = out_2 + above2;
+    g_i32* out_e = out_a + above3;
     uint32_t oa3 = 0, oe = 0;
     for (uint32_t j0 = 0; j0 < cnt2; j0 += WAVE) {
       const uint32_t j = j0 + lane;
@@ -613,7 +503,8 @@ __device__ void wave_select(float* row, int n, int K, int32_t* out, uint32_t* h,
       const uint64_t ma = __builtin_amdgcn_ballot_w64(j < cnt2 && low > d3);
       const uint64_t me = __builtin_amdgcn_ballot_w64(j < cnt2 && low == d3);
       const int32_t pos = (int32_t)(v & ((1u << 22) - 1u));
-      if ((ma >> lane) & 1ull) out_a[oa3 + __popcll(ma & below)] = pos;
+      const uint32_t ra = oa3 + __popcll(ma & below);
+      if (((ma >> lane) & 1ull) && ra < above3) out_a[ra] = pos;
       if ((me >> lane) & 1ull) {
         const uint32_t r = oe + __popcll(me & below);
         if (r < need) out_e[r] = pos;
@@ -625,23 +516,23 @@ __device__ void wave_select(float* row, int n, int K, int32_t* out, uint32_t* h,
   }
   // d2 holds more keys than the list: the low 10 bits over the d1 keys, then
   // the positions above tau and the first `need` equal to it
-  over_d1([&](uint32_t w, bool ok, int) {
-    if (ok && (w >> 21) == d2) atomicAdd(&h[(w >> 11) & 1023u], 1u);
+  over_d1([&](uint32_t key, uint32_t, bool ok) {
+    if (ok && ((key >> 10) & 2047u) == d2) lds_inc(&h[key & 1023u]);
   });
   wave_pick<1024>(h, rem2, lane, d3, above3, cnt3);
   const uint32_t lowtau = (d2 << 10) | d3;  // key bits 20..0 of tau
   const uint32_t need = rem2 - above3;
   const uint32_t n_gt = above2 + above3;  // d1 keys above tau
   uint32_t og2 = 0, oe = 0;
-  over_d1([&](uint32_t w, bool ok, int c0) {
-    const uint32_t low21 = w >> 11;
-    const int32_t pos = c0 + (int32_t)(w & (SEL_CHUNK - 1));
+  over_d1([&](uint32_t key, uint32_t pos, bool ok) {
+    const uint32_t low21 = key & 0x1FFFFFu;
     const uint64_t mg = __builtin_amdgcn_ballot_w64(ok && low21 > lowtau);
     const uint64_t me = __builtin_amdgcn_ballot_w64(ok && low21 == lowtau);
-    if ((mg >> lane) & 1ull) out_2[og2 + __popcll(mg & below)] = pos;
+    const uint32_t rg = og2 + __popcll(mg & below);
+    if (((mg >> lane) & 1ull) && rg < n_gt) out_2[rg] = (int32_t)pos;
     if ((me >> lane) & 1ull) {
       const uint32_t r = oe + __popcll(me & below);
-      if (r < need) out_2[n_gt + r] = pos;
+      if (r < need) out_2[n_gt + r] = (int32_t)pos;
     }
     og2 += __popcll(mg);
     oe += __popcll(me);
@@ -739,8 +630,13 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
 #pragma unroll
   for (int j = 0; j < NLD; ++j) boff[j] = c * ROWB + (((4 * j + g) ^ pf_swz<CPR>(c)) << 4);
 
-  float* srow = p.scores + (int64_t)tok * p.score_stride;
+  // the row's candidate pairs (key, position); the row pitch holds two words
+  // per position
+  uint32_t* cand = (uint32_t*)(p.scores + (int64_t)tok * p.score_stride);
   uint32_t* my_hist = hist[wave];
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t d1_run = 0;  // lower bound of the row's threshold bucket
+  uint32_t ncand = 0;   // candidate pairs written (wave-uniform)
 
 #pragma unroll
   for (int k = 0; k < PF_NBUF - 1; ++k)
@@ -787,22 +683,29 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
       const int sk = k * PF_KT + qd * 64 + 16 * g + c;  // this lane's key
       if (p.k_scale) keep *= ksc[k % PF_NBUF][qd * 64 + 16 * g + c];
       keep += 0.0f;  // -0 -> +0
-      if (sk <= t) {
-        srow[sk] = keep;
-        atomicAdd(&my_hist[score_key(keep) >> (32 - SCORE_HIST_BITS)], 1u);
-      }
+      const uint32_t key = score_key(keep);
+      const bool ok = sk <= t;
+      if (ok) atomicAdd(&my_hist[key >> (32 - SCORE_HIST_BITS)], 1u);
+      const uint64_t cm = __builtin_amdgcn_ballot_w64(ok && (key >> (32 - SCORE_HIST_BITS)) >= d1_run);
+      if ((cm >> lane) & 1ull) *(u32x2*)(cand + 2 * (ncand + __popcll(cm & below))) = u32x2{key, (uint32_t)sk};
+      ncand += __popcll(cm);
     }
+    }
+    // refresh the bound: the bucket of the K-th largest key of the row so far
+    if (active && (k & 15) == 15 && min(t + 1, (k + 1) * PF_KT) > p.top_k) {
+      uint32_t a_, c_;
+      wave_pick<SCORE_HIST_BINS>(my_hist, (uint32_t)p.top_k, lane, d1_run, a_, c_);
     }
   }
 
   // ---- each wave selects the Top-K of its token's complete row -----------------
   __syncthreads();
   if (active) {
-    wait_vmcnt<0>();  // the wave's score stores have completed
+    wait_vmcnt<0>();  // the wave's candidate stores have completed
     // the tile ring is free now: each wave takes an equal share as its list
     constexpr int LIST = PF_NBUF * TILEB / 4 / PF_TOKS;
-    wave_select(srow, t + 1, p.top_k, p.out_idx + (int64_t)tok * p.top_k, my_hist,
-                (uint32_t*)ring + wave * LIST, LIST, lane);
+    wave_select_list(cand, ncand, t + 1, p.top_k, p.out_idx + (int64_t)tok * p.top_k, my_hist,
+                     (uint32_t*)ring + wave * LIST, LIST, lane);
   }
 }
 
