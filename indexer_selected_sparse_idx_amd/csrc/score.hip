@@ -258,9 +258,9 @@ __global__ void zero_kernel(uint32_t* p, int64_t n4) {
 // chunk (16 lanes of a 128-bit read) hit 16 different bank windows.
 // ---------------------------------------------------------------------------
 constexpr int PF_TOKS = 8;        // tokens (= waves) per workgroup
-constexpr int PF_KT = 64;         // keys per tile
-constexpr int PF_NBUF = 3;        // tile ring depth
-constexpr int PF_MAX_PAGES = 8192;  // block-table entries a workgroup can stage
+constexpr int PF_KT = 128;        // keys per tile (one barrier per tile)
+constexpr int PF_NBUF = 2;        // tile ring depth (tile k + 1 loads while tile k is computed)
+constexpr int PF_MAX_PAGES = 4096;  // block-table entries a workgroup can stage
 
 template <int CPR>
 __device__ __forceinline__ int pf_swz(int r) {
@@ -306,7 +306,7 @@ __device__ __forceinline__ float reduce_scatter4(const float (&x)[4], int g) {
 // position order, (order-preserving key, position) for every key whose top
 // 11 bits reach a running lower bound of the row's threshold bucket (the
 // bucket of the K-th largest key seen so far, refreshed from the row's LDS
-// histogram every 16 tiles).  The K-th largest of a prefix never exceeds
+// histogram every 1024 keys).  The K-th largest of a prefix never exceeds
 // the K-th largest of the row, so the list holds every key the selection can
 // take.  The row's complete histogram of the top 11 bits then fixes the
 // threshold bucket d1; one pass over the list writes the positions above d1
@@ -691,8 +691,9 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
       ncand += __popcll(cm);
     }
     }
-    // refresh the bound: the bucket of the K-th largest key of the row so far
-    if (active && (k & 15) == 15 && min(t + 1, (k + 1) * PF_KT) > p.top_k) {
+    // refresh the bound every 1024 keys: the bucket of the K-th largest key
+    // of the row so far
+    if (active && ((k + 1) * PF_KT) % 1024 == 0 && min(t + 1, (k + 1) * PF_KT) > p.top_k) {
       uint32_t a_, c_;
       wave_pick<SCORE_HIST_BINS>(my_hist, (uint32_t)p.top_k, lane, d1_run, a_, c_);
     }
