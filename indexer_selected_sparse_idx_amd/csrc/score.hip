@@ -308,7 +308,8 @@ __device__ __forceinline__ float reduce_scatter4(const float (&x)[4], int g) {
 // bucket of the K-th largest key seen so far, refreshed from the row's LDS
 // histogram every 1024 keys).  The K-th largest of a prefix never exceeds
 // the K-th largest of the row, so the list holds every key the selection can
-// take.  The row's complete histogram of the top 11 bits then fixes the
+// take.  The histogram counts the candidates only; its bins at or above the
+// bound, the only ones read, hold the counts of the whole row.  They fix the
 // threshold bucket d1; one pass over the list writes the positions above d1
 // and compacts the d1 keys in place (still in position order) while
 // histogramming their next 11 bits; a pass over those picks the 22-bit
@@ -683,11 +684,16 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
       const int sk = k * PF_KT + qd * 64 + 16 * g + c;  // this lane's key
       if (p.k_scale) keep *= ksc[k % PF_NBUF][qd * 64 + 16 * g + c];
       keep += 0.0f;  // -0 -> +0
+      // only candidates enter the histogram: every key at or above the
+      // bound is a candidate, so the counts of the bins at or above it (all
+      // that the bound refresh and the selection read) are the row's own
       const uint32_t key = score_key(keep);
-      const bool ok = sk <= t;
-      if (ok) atomicAdd(&my_hist[key >> (32 - SCORE_HIST_BITS)], 1u);
-      const uint64_t cm = __builtin_amdgcn_ballot_w64(ok && (key >> (32 - SCORE_HIST_BITS)) >= d1_run);
-      if ((cm >> lane) & 1ull) *(u32x2*)(cand + 2 * (ncand + __popcll(cm & below))) = u32x2{key, (uint32_t)sk};
+      const uint32_t bin = key >> (32 - SCORE_HIST_BITS);
+      const uint64_t cm = __builtin_amdgcn_ballot_w64(sk <= t && bin >= d1_run);
+      if ((cm >> lane) & 1ull) {
+        *(u32x2*)(cand + 2 * (ncand + __popcll(cm & below))) = u32x2{key, (uint32_t)sk};
+        atomicAdd(&my_hist[bin], 1u);
+      }
       ncand += __popcll(cm);
     }
     }
