@@ -45,7 +45,7 @@ namespace {
 
 constexpr int TOPK_THREADS = 1024;
 constexpr int TOPK_WAVES = TOPK_THREADS / WAVE;
-constexpr int CAP = 32768;   // LDS candidate capacity (one packed word each)
+constexpr int CAP = 24576;   // LDS candidate capacity (a packed word and a chunk byte each)
 constexpr int UNROLL = 4;   // 4-key vector accesses in flight per lane
 
 // Key source: candidate words in LDS (low key bits << 11 | offset in the
@@ -78,24 +78,16 @@ struct Keys {
 };
 
 // Position of list entry i: the entry itself (a whole score row), or, for
-// the candidate words, the chunk holding entry i (the last chunk whose first
-// candidate is at or before i, from the exclusive prefix sums of the
-// per-chunk counts) plus the word's offset.  Only entries that are written
-// out are looked up.
+// the candidate words, the entry's chunk (one byte per entry, stored beside
+// the words) plus the word's offset in it.
 struct RowPos {
   __device__ __forceinline__ int operator()(int i) const { return i; }
 };
 struct CandPos {
   const uint32_t* w;
-  const uint32_t* choff;
-  int nch;
+  const uint8_t* chunk;
   __device__ __forceinline__ int operator()(int i) const {
-    int lo = 0, hi = nch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (choff[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
-    }
-    return lo * TOPK_CHUNK + (int)(w[i] & (TOPK_CHUNK - 1));
+    return (int)chunk[i] * TOPK_CHUNK + (int)(w[i] & (TOPK_CHUNK - 1));
   }
 };
 
@@ -283,16 +275,15 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
 //           go to a per-chunk table.
 //   select  one workgroup per row: the positions above d1 go to the output,
 //           chunk after chunk; the packed d1 words go into LDS in position
-//           order (4 bytes each; a selected word's chunk is found from the
-//           per-chunk offsets) and the radix select above takes the
-//           remaining m - above1 of them.
+//           order (4 bytes each, with a byte for the chunk) and the radix
+//           select above takes the remaining m - above1 of them.
 // Rows with t + 1 <= K take every position.  Rows whose d1 bucket exceeds the
 // LDS capacity (massive ties), or with more chunks than the select tracks,
 // are left alone by emit and select over the whole score row.
 // ---------------------------------------------------------------------------
 constexpr int TKE_THREADS = 256;                     // 8 keys per thread
 constexpr int TKE_WAVES = TKE_THREADS / WAVE;
-constexpr int TK_MAXCH = 512;                        // chunks per row the select tracks
+constexpr int TK_MAXCH = 256;                        // chunks per row the select tracks (byte chunk ids)
 constexpr uint32_t TK_PARTIAL = 0, TK_ALL = 1, TK_WHOLE_ROW = 2;
 static_assert(TOPK_CHUNK == 2048 && TOPK_CHUNK == 8 * TKE_THREADS, "11-bit chunk offsets, 8 keys per thread");
 
@@ -412,6 +403,7 @@ __global__ __launch_bounds__(TKE_THREADS) void topk_emit_kernel(TopkParams p) {
 
 __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t cand_w[CAP];
+  __shared__ uint8_t cand_c[CAP];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t whist[TOPK_WAVES * 256];
   __shared__ uint32_t wcnt[2 * TOPK_WAVES];
@@ -475,11 +467,14 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select_kernel(TopkParams p)
     const uint32_t* seg = (const uint32_t*)(row + (int64_t)c * TOPK_CHUNK);
     const uint32_t ng = chcnt[0][c], ne = chcnt[1][c], og = choff[0][c], oe = choff[1][c];
     for (uint32_t j = lane; j < ng; j += WAVE) out[og + j] = (int32_t)seg[j];
-    for (uint32_t j = lane; j < ne; j += WAVE) cand_w[oe + j] = seg[ng + j];
+    for (uint32_t j = lane; j < ne; j += WAVE) {
+      cand_w[oe + j] = seg[ng + j];
+      cand_c[oe + j] = (uint8_t)c;
+    }
   }
   __syncthreads();
   select_row<true, SCORE_HIST_BITS>(Keys<true>{cand_w, nullptr, (int)r.cnt1, r.d1 << (32 - SCORE_HIST_BITS)},
-                                    (int)r.cnt1, m - (int)r.above1, out + r.above1, CandPos{cand_w, choff[1], nch},
+                                    (int)r.cnt1, m - (int)r.above1, out + r.above1, CandPos{cand_w, cand_c},
                                     hist, whist, wcnt, r.d1);
 }
 

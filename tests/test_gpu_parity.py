@@ -110,7 +110,7 @@ def test_all_equal_scores_take_lowest_positions():
 
 def test_decode_all_equal_scores_whole_row_select():
     # every score 0: the threshold bucket holds the whole row (40,000 and 33,000
-    # keys, more than the 32,768-entry candidate list), so decode selection
+    # keys, more than the 24,576-entry candidate list), so decode selection
     # runs over the whole row
     wl = Workload("zeros decode", [40000, 33000], [{"seqs": [0, 1], "q_len": None}], top_k=512, H=32, seed=30)
     inp = generate(wl, "cuda")
@@ -133,9 +133,9 @@ def _top11(scores):
 
 
 def test_decode_wide_threshold_bucket():
-    # Scores built so that 20,000 (request 0) and 25,000 (request 1) keys share
+    # Scores built so that 20,000 (request 0) and 24,000 (request 1) keys share
     # the histogram bucket of the K-th largest score, above the 12,288 keys of
-    # the older candidate list and within the 32,768 of the packed one; the
+    # the older candidate list and within the 24,576 of the packed one; the
     # bucket holds 32 distinct values, so the radix select and the tie rule
     # both take part.  Every head's query is the unit vector on dimension 0
     # and every head weight is 1, so S = 64 * ReLU(k[0]).
@@ -145,7 +145,7 @@ def test_decode_wide_threshold_bucket():
     inp.q_idx[:, :, 0] = 1.0
     inp.head_w.fill_(1.0)
     rng = np.random.default_rng(32)
-    for b, (n, n_mid) in enumerate([(131072, 20000), (70000, 25000)]):
+    for b, (n, n_mid) in enumerate([(131072, 20000), (70000, 24000)]):
         k0 = rng.integers(-4, 5, n).astype(np.float32)       # scores 0 .. 256
         perm = rng.permutation(n)
         k0[perm[:1000]] = 100.0                              # score 6400: above the bucket
@@ -158,13 +158,13 @@ def test_decode_wide_threshold_bucket():
     w_idx, w_out, w_lse = U.oracle_rows(inp, call, [0, 1])
     # the case is what it claims: the K-th largest score's bucket size
     import oracle
-    for b, n_mid in enumerate([20000, 25000]):
+    for b, n_mid in enumerate([20000, 24000]):
         keys = oracle.bf16_bits_to_f64(U.bits16(inp.k_idx[b * inp.seq_stride:b * inp.seq_stride + int(call.ctx_len[b])]))
         s = 64.0 * np.maximum(keys[:, 0], 0.0)
         kth = np.sort(s)[::-1][2047]
         cnt = int(np.sum(_top11(s) == _top11([kth])[0]))
         U.log("wide bucket request %d: %d keys in the threshold bucket" % (b, cnt))
-        assert cnt == n_mid and 12288 < cnt <= 32768
+        assert cnt == n_mid and 12288 < cnt <= 24576
     U.check_indices(idx.cpu().numpy(), w_idx, "wide bucket")
     U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), w_out, w_lse, U.TOL_BF16, "wide bucket")
 
