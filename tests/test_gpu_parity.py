@@ -83,6 +83,17 @@ def test_paged_mixed_scaled():
     _parity_all(inp, U.TOL_BF16, "mixed-paged/16")
 
 
+def test_multi_token_decode_rows_paged():
+    # speculative verification: every request scores and attends 2 to 8 new
+    # tokens at once (q_len > 1 through cu_q), over a paged cache, with
+    # contexts on both sides of K and of the 64-position page
+    ctx = [5000, 2100, 64, 130, 7777, 2049, 3000, 9000]
+    q_len = [4, 8, 2, 3, 5, 8, 2, 7]
+    wl = Workload("spec decode", ctx, [{"seqs": list(range(8)), "q_len": q_len}], top_k=2048, H=32,
+                  paged=True, page_size=64, seed=33)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "spec-decode")
+
+
 def test_key_scale_and_d64():
     wl = Workload("k_scale", [900, 333], [{"seqs": [0, 1], "q_len": [40, 7]}], top_k=96, d_I=64, H_I=33,
                   H=48, k_scale=True, seed=24)
