@@ -666,6 +666,53 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 rows, at most 32 heads, rows not split: one wave per workgroup and a
+// single tile buffer (about 40 KiB of LDS with MAXE <= 256), so several
+// tokens share a CU, one per SIMD, instead of one token holding the CU's
+// whole LDS for its ring.  Each tile is gathered, waited for and computed in
+// turn; the other tokens on the CU fill the gaps.  (Few heads make the
+// per-token work small, so the loads' latency, not the MFMAs, bounds it.)
+// ---------------------------------------------------------------------------
+template <int MAXE>
+__global__ __launch_bounds__(WAVE, 1) void attn_bf16_single_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[BUF_BYTES];
+  __shared__ int rows_sh[MAXE];
+  __shared__ int wsum[4];
+  typedef Bf16Rows<1> R;
+  const int lane = threadIdx.x;
+  const int h = lane >> 5;
+  Work w;
+  if (!map_work(p, w)) return;
+  const int head = lane & 31;
+  const bool head_ok = head < p.H;
+  const int n = resolve_rows<1, MAXE>(p, w, rows_sh, wsum, lane);
+  const int ntiles = cdiv(n, TILE);
+  WaveAcc a;
+  load_q(a, p, w.tok, head, head_ok, h);
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
+  TileAddr ad;
+  ad.init(lane);
+  float m_ref = -INFINITY;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    reset_acc(a, m_ref);
+    for (int k = 0; k < ntiles; ++k) {
+      // the previous tile's operand reads have all returned (their values
+      // fed its MFMAs), so the buffer can be overwritten
+      R::issue(p, rows_sh + k * TILE, smem_base, 0, lane);
+      wait_vmcnt<0>();
+      const f32x16 sc = s_phase(a, smem, ad, NoStep());
+      SoftmaxTile<true> sm(sc);
+      sm.run_all(a, min(TILE, n - k * TILE), p.scale_log2, h);
+      v_phase<true>(a, smem, ad, sm.op, NoStep());
+    }
+    o_fence(a);
+    if (!needs_redo<1>(a, wsum, 0, lane)) break;
+    m_ref = a.m_max;
+  }
+  write_result(a, p, w.tok, w.split, head, head_ok, h);
+}
+
+// ---------------------------------------------------------------------------
 // FP8 rows: gathers into a raw NRAW-deep ring, dequantised by the workgroup
 // into a double-buffered bf16 tile.
 // ---------------------------------------------------------------------------
@@ -783,6 +830,8 @@ hipError_t launch_grid(K kernel, const AttnParams& p, int waves, hipStream_t str
 template <int NW>
 hipError_t launch_nw(const AttnParams& p, bool fp8, hipStream_t stream, const TimerEvents& t) {
   if (fp8) return launch_grid(attn_fp8_kernel<NW, 3, 2048>, p, NW, stream, t);
+  if (NW == 1 && p.num_splits == 1 && p.split_len <= 256)
+    return launch_grid(attn_bf16_single_kernel<256>, p, 1, stream, t);
   if (p.split_len <= 1024) return launch_grid(attn_bf16_kernel<NW, 4, 1024, true>, p, NW, stream, t);
   return launch_grid(attn_bf16_kernel<NW, 4, 2048, true>, p, NW, stream, t);
 }
