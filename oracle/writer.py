@@ -1,0 +1,82 @@
+"""FP8 latent-row writer, written from its definition (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this
+module; only tests/, the smoke check and the bench's CPU-baseline leg do.
+
+The FP8 KV cache keeps every latent row as per-token tiles of 128 values,
+each with its own scale computed online from the row ("Hierarchical
+Quantization", KV cache bullet, in Day 0 Inference Support for New LLM
+Architectures; section 4 of Day 0 Inference Adaptation and Performance
+Optimization for New Models).  The pages give the tile size but not the
+scale rule or the rounding; the reading taken here:
+
+* scale_j = amax_j / 448 in fp32 (amax_j: the largest |value| of tile j, so
+  the largest value maps to the largest finite E4M3FN value, 448);
+* code = E4M3(clamp(value / scale_j, -448, 448)), the division in fp32 and
+  the E4M3 rounding to the nearest value, ties to the even code (last
+  mantissa bit 0), the sign kept (a negative value that rounds to zero gives
+  -0); an all-zero tile has scale 0 and codes 0;
+* the 64 rope values are stored unchanged as bf16.
+
+The packed row is the 656-byte layout decoded by formats.fp8_rows_to_f64.
+"""
+import numpy as np
+
+from .formats import E4M3_TABLE, FP8_ROW_BYTES, FP8_TILE, LATENT, ROPE, ROW
+
+E4M3_MAX = 448.0
+# finite non-negative codes 0x00 .. 0x7E in increasing value order
+_POS_CODES = np.arange(0x7F)
+_POS_VALUES = E4M3_TABLE[_POS_CODES]
+
+
+def e4m3_encode(x):
+    """Nearest E4M3FN code of a value with |x| <= 448, ties to the even
+    code, sign kept.  x: float (any float type; its exact value is used)."""
+    x = float(x)
+    if not (abs(x) <= E4M3_MAX):
+        raise ValueError("e4m3_encode: |x| must be <= 448 (clamp first): %r" % x)
+    neg = np.signbit(x)
+    a = abs(x)
+    # largest code whose value is <= a, and the next one up
+    lo = int(np.searchsorted(_POS_VALUES, a, side="right")) - 1
+    if _POS_VALUES[lo] == a or lo == len(_POS_VALUES) - 1:
+        code = lo
+    else:
+        hi = lo + 1
+        d_lo, d_hi = a - _POS_VALUES[lo], _POS_VALUES[hi] - a
+        if d_lo < d_hi:
+            code = lo
+        elif d_hi < d_lo:
+            code = hi
+        else:
+            code = lo if lo % 2 == 0 else hi
+    return (0x80 | code) if neg else code
+
+
+def fp8_rows_from_bf16(bits):
+    """bf16 latent rows (uint16 bit patterns [n, 576]) -> packed FP8 rows
+    (uint8 [n, 656])."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if bits.ndim != 2 or bits.shape[1] != ROW:
+        raise ValueError("rows must be [n, 576]")
+    n = bits.shape[0]
+    f32 = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    out = np.zeros((n, FP8_ROW_BYTES), dtype=np.uint8)
+    for r in range(n):
+        scales = np.zeros(LATENT // FP8_TILE, dtype=np.float32)
+        for j in range(LATENT // FP8_TILE):
+            tile = f32[r, j * FP8_TILE:(j + 1) * FP8_TILE]
+            amax = np.float32(np.max(np.abs(tile)))
+            scale = np.float32(amax / np.float32(E4M3_MAX))
+            scales[j] = scale
+            for i, v in enumerate(tile):
+                if scale > 0:
+                    q = np.float32(v / scale)
+                    q = np.float32(min(max(float(q), -E4M3_MAX), E4M3_MAX))
+                else:
+                    q = np.float32(0.0)
+                out[r, j * FP8_TILE + i] = e4m3_encode(q)
+        out[r, LATENT:LATENT + 16] = scales.view(np.uint8)
+        out[r, LATENT + 16:] = bits[r, LATENT:].view(np.uint8)
+    return out

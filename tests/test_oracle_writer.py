@@ -1,0 +1,100 @@
+"""Pins of the oracle's FP8 latent-row writer (CPU).
+
+The writer (oracle/writer.py) is pinned against what the definition fixes:
+every E4M3FN code round-trips, values halfway between two codes go to the
+even one and values just off halfway to the nearer one (the definition of
+round-to-nearest-even, checked at every pair of neighbouring codes), torch's
+own float8_e4m3fn conversion (a library routine) agrees on random values, a
+hand-built row with exactly representable tiles gives the codes written out
+by hand, and decoding any written row stays within half a code step of the
+input.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from oracle import writer as W
+
+
+def _finite_codes():
+    return [c for c in range(256) if c not in (0x7F, 0xFF)]
+
+
+def test_e4m3_encode_round_trips_every_code():
+    for c in _finite_codes():
+        assert W.e4m3_encode(F.E4M3_TABLE[c]) == c, hex(c)
+
+
+def test_e4m3_encode_halfway_goes_to_even_code():
+    for c in range(0x7E):
+        lo, hi = F.E4M3_TABLE[c], F.E4M3_TABLE[c + 1]
+        mid = (lo + hi) / 2.0                           # exact in float64
+        even = c if c % 2 == 0 else c + 1
+        assert W.e4m3_encode(mid) == even, (hex(c), mid)
+        assert W.e4m3_encode(-mid) == 0x80 | even
+        assert W.e4m3_encode(np.nextafter(mid, np.inf)) == c + 1
+        assert W.e4m3_encode(np.nextafter(mid, -np.inf)) == c
+
+
+def test_e4m3_encode_matches_torch_float8_e4m3fn():
+    rng = np.random.default_rng(7)
+    v = np.concatenate([rng.uniform(-448, 448, 3000), rng.normal(0, 1, 3000), rng.normal(0, 1e-2, 2000)])
+    v = v.astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([W.e4m3_encode(x) for x in v], dtype=np.uint8)
+    # torch keeps the sign of values that round to zero as well
+    assert np.array_equal(got, ref)
+
+
+def _bits(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_writer_hand_built_row():
+    row = np.zeros(576, dtype=np.float32)
+    # tile 0: amax 56 -> scale 56 / 448 = 0.125 exactly; value v -> v / 0.125
+    row[0], row[1], row[2], row[3] = 56.0, 1.5, -0.125, 0.0625
+    # tile 1: all zero -> scale 0, codes 0
+    # tile 2: amax 448 -> scale 1; a negative zero keeps its sign
+    row[256], row[257] = -448.0, -0.0
+    # tile 3: amax 2**-3 -> scale 2**-3 / 448 (not a power of two)
+    row[384] = 0.125
+    row[512:] = np.arange(64, dtype=np.float32) * 0.5 - 8.0   # rope
+    out = W.fp8_rows_from_bf16(_bits(row)[None, :])[0]
+    codes = out[:512]
+    scales = out[512:528].view(np.float32)
+    # 56 / 0.125 = 448 -> 0x7E; 1.5 / 0.125 = 12 = 1.5 * 2^3 -> 0 1010 100 = 0x54;
+    # -0.125 / 0.125 = -1 -> 1 0111 000 = 0xB8; 0.0625 / 0.125 = 0.5 -> 0 0110 000 = 0x30
+    assert list(codes[:4]) == [0x7E, 0x54, 0xB8, 0x30]
+    assert np.all(codes[4:128] == 0)
+    assert scales[0] == np.float32(0.125)
+    assert scales[1] == 0.0 and np.all(codes[128:256] == 0)
+    assert scales[2] == np.float32(1.0)
+    assert codes[256] == 0xFE and codes[257] == 0x80         # -448; -0 keeps its sign
+    assert scales[3] == np.float32(np.float32(0.125) / np.float32(448.0))
+    assert codes[384] == 0x7E                                # amax maps to 448
+    assert np.array_equal(out[528:].view(np.uint16), _bits(row[512:]))
+
+
+def test_writer_decodes_within_half_a_code_step():
+    rng = np.random.default_rng(11)
+    rows = np.concatenate([rng.normal(0, 1, (6, 576)), rng.normal(0, 1, (2, 576)) * 1e-3]).astype(np.float32)
+    rows[7, :128] = 0.0
+    bits = _bits(rows)
+    x = F.bf16_bits_to_f64(bits)
+    packed = W.fp8_rows_from_bf16(bits)
+    back = F.fp8_rows_to_f64(packed)
+    assert np.array_equal(back[:, 512:], x[:, 512:])         # rope unchanged
+    scales = packed[:, 512:528].view(np.float32).astype(np.float64)
+    for r in range(rows.shape[0]):
+        for j in range(4):
+            t = x[r, 128 * j:128 * (j + 1)]
+            d = back[r, 128 * j:128 * (j + 1)]
+            s = scales[r, j]
+            assert s == pytest.approx(np.max(np.abs(t)) / 448.0, rel=1e-7, abs=0)
+            # half a step: 2^-4 relative for normal codes, 2^-10 absolute
+            # (in units of the scale) for subnormal ones, plus the fp32
+            # division's own rounding
+            bound = np.maximum(np.abs(t) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 2.0 ** -20)
+            assert np.all(np.abs(d - t) <= bound)
