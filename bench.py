@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=0,
                     help="1..5: time another workload (all of its calls per step) and print per-kernel "
                          "figures instead of the headline JSON line")
+    ap.add_argument("--kv-write", action="store_true",
+                    help="time the FP8 latent-cache writer on 1,048,576 rows and print its own figures "
+                         "instead of the headline JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -213,6 +216,44 @@ def measure_workload(n, steps, warmup):
                       "per_call": per_call}), flush=True)
 
 
+KV_WRITE_ROWS = 1 << 20   # 8 sequences x 131,072 positions
+
+
+def measure_kv_write(steps, warmup):
+    """FP8 latent-cache writer: quantise 1,048,576 standard-normal bf16 latent
+    rows into a packed FP8 cache, as a paged cache's slots are written:
+    consecutive rows within pages of 64, the pages in a shuffled order.
+    Algorithmic bytes per row: 1152 read, 656 written, 4 of row index; the
+    kernel is HBM-bound."""
+    import torch
+    import indexer_selected_sparse_idx_amd as lib
+    dev = torch.device("cuda:0")
+    n = KV_WRITE_ROWS
+    g = torch.Generator(device=dev).manual_seed(6)
+    src = torch.randn((n, 576), generator=g, device=dev).to(torch.bfloat16)
+    pages = torch.randperm(n // 64, generator=g, device=dev).to(torch.int32)
+    perm = (pages[:, None] * 64 + torch.arange(64, dtype=torch.int32, device=dev)[None, :]).reshape(-1)
+    kv = torch.empty((n, 656), dtype=torch.uint8, device=dev)
+    for _ in range(max(1, warmup)):
+        lib.idx_kv_fp8_write(src, perm, kv)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(1, steps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        e1.record()   # (torch creates the HIP events on first record)
+        torch.cuda.synchronize()
+        lib.idx_timer_arm(lib.IDX_KERNEL_KV_WRITE, e0, e1)
+        lib.idx_kv_fp8_write(src, perm, kv)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    us = sorted(times)[len(times) // 2]
+    nbytes = n * (1152 + 656 + 4)
+    print(json.dumps({"kernel": "FP8 latent-cache writer", "rows": n, "median_us": us,
+                      "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / us / 1e3,
+                      "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "rows_per_s": n / us * 1e6}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -243,6 +284,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload:
         measure_workload(args.workload, args.steps, args.warmup)
+        return
+    if args.kv_write:
+        measure_kv_write(args.steps, args.warmup)
         return
     wl = config(2)
     inp = generate(wl, dev)

@@ -191,6 +191,31 @@ int idx_sparse_attn_decode(const idx_seqs *seqs,
                            float *out, float *lse, int32_t *out_idx,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------ *
+ * FP8 latent-cache writer: quantise latent rows into the packed 656-byte
+ * rows of an IDX_KV_FP8_656 cache (the producer side of that cache).
+ *
+ * Each latent row keeps per-token tiles of 128 values, each with its own
+ * scale computed online from the row ("Hierarchical Quantization", KV cache
+ * bullet, in Day 0 Inference Support...; section 4 of Day 0 Inference
+ * Adaptation and Performance Optimization for New Models).  Tile j of a row
+ * gets scale_j = amax_j / 448 (fp32; amax_j the largest |value| of the tile)
+ * and codes E4M3FN(clamp(value / scale_j, -448, 448)) (fp32 division,
+ * rounded to the nearest E4M3FN value, ties to even, the sign kept); an
+ * all-zero tile gets scale 0 and codes 0.  The 64 rope values are copied.
+ * (The scale rule and the rounding are this library's reading; the pages
+ * give the tile size.)
+ *
+ *   src      bf16 [n, 576] latent rows (512 latent values, then 64 rope)
+ *   n        rows, >= 0 (0: nothing is launched)
+ *   dst_row  device int32 [n]: the cache row each source row is written
+ *            to; entries < 0 are skipped.  Two entries naming the same row
+ *            race (undefined which is kept).
+ *   kv       the cache: rows of 656 bytes, 16-byte aligned; only the named
+ *            rows are written.
+ * ------------------------------------------------------------------------ */
+int idx_kv_fp8_write(const void *src, int n, const int32_t *dst_row, void *kv, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *idx_status_string(int status);
 
@@ -212,7 +237,8 @@ typedef enum {
   IDX_KERNEL_ATTN = 2,      /* sparse latent attention                        */
   IDX_KERNEL_COMBINE = 3,   /* split merge of the attention partials (only
                                launched when a call splits the index lists) */
-  IDX_KERNEL_COUNT = 4
+  IDX_KERNEL_KV_WRITE = 4,  /* FP8 latent-cache writer                      */
+  IDX_KERNEL_COUNT = 5
 } idx_kernel;
 int idx_timer_arm(int kernel, void *start_event, void *stop_event);
 

@@ -18,7 +18,7 @@ lib_path = os.environ.get("IDXSPARSE_LIB") or os.path.join(_HERE, "libidxsparse.
 
 IDX_OK = 0
 IDX_BF16, IDX_E4M3, IDX_KV_FP8_656 = 1, 2, 3
-IDX_KERNEL_SCORE, IDX_KERNEL_TOPK, IDX_KERNEL_ATTN, IDX_KERNEL_COMBINE = 0, 1, 2, 3
+IDX_KERNEL_SCORE, IDX_KERNEL_TOPK, IDX_KERNEL_ATTN, IDX_KERNEL_COMBINE, IDX_KERNEL_KV_WRITE = 0, 1, 2, 3, 4
 FP8_ROW_BYTES = 656
 
 
@@ -61,6 +61,7 @@ _SIGNATURES = {
                                      _P, _P, _P, _P, _SZ, _P]),
     "idx_sparse_attn_decode": (_I, [_SEQ, _P, _I, _P, _I, _P, _P, _I, _I, _I, _P, _I, _P, _I, _F,
                                     _P, _P, _P, _P, _SZ, _P]),
+    "idx_kv_fp8_write": (_I, [_P, _I, _P, _P, _P]),
     "idx_timer_arm": (_I, [_I, _P, _P]),
 }
 
@@ -227,6 +228,16 @@ def idx_sparse_attn_decode(seqs, q_idx, k_idx, head_w, top_k, q, kv, softmax_sca
     """Fused indexer + sparse attention, one token per sequence."""
     return _fused("idx_sparse_attn_decode", seqs, q_idx, k_idx, head_w, top_k, q, kv, softmax_scale,
                   k_scale, out, lse, out_idx, want_lse, ws)
+
+
+def idx_kv_fp8_write(src, dst_row, kv):
+    """Quantise bf16 latent rows src [n, 576] into the packed 656-byte FP8
+    rows dst_row[i] of kv (uint8 [rows, 656]); entries of dst_row < 0 are
+    skipped.  Returns kv."""
+    n = int(src.shape[0])
+    rc = lib().idx_kv_fp8_write(_ptr(src), n, _ptr(dst_row), _ptr(kv), _stream())
+    _check(rc, "idx_kv_fp8_write")
+    return kv
 
 
 def idx_timer_arm(kernel, start_event, stop_event):

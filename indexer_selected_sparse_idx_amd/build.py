@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libidxsparse.so")
-SOURCES = ["api.cpp", "score.hip", "topk.hip", "attn.hip"]
+SOURCES = ["api.cpp", "score.hip", "topk.hip", "attn.hip", "kvwrite.hip"]
 
 ARCH = os.environ.get("IDXSPARSE_ARCH", "gfx950")
 CFLAGS = [

@@ -300,6 +300,19 @@ int idx_sparse_attn_decode(const idx_seqs* seqs, const void* q_idx, int q_dtype,
                softmax_scale, out, lse, out_idx, ws, ws_bytes, stream);
 }
 
+int idx_kv_fp8_write(const void* src, int n, const int32_t* dst_row, void* kv, void* stream) {
+  if (n < 0) return IDX_ERR_INVALID_ARG;
+  if (n == 0) return IDX_OK;
+  if (!src || !dst_row || !kv) return IDX_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(kv) || !aligned4(dst_row)) return IDX_ERR_INVALID_ARG;
+  KvWriteParams p;
+  p.src = static_cast<const uint16_t*>(src);
+  p.n = n;
+  p.dst_row = dst_row;
+  p.kv = static_cast<uint8_t*>(kv);
+  return launch_kv_fp8_write(p, static_cast<hipStream_t>(stream)) == hipSuccess ? IDX_OK : IDX_ERR_HIP;
+}
+
 int idx_timer_arm(int kernel, void* start_event, void* stop_event) {
   if (kernel < 0 || kernel >= IDX_KERNEL_COUNT || !start_event || !stop_event) return IDX_ERR_INVALID_ARG;
   g_timers[kernel].start = static_cast<hipEvent_t>(start_event);

@@ -91,6 +91,13 @@ struct AttnParams {
   float* part_ls;          // [T, num_splits, H, 2]: (lse of the split, power-of-two scale of its stored O)
 };
 
+struct KvWriteParams {
+  const uint16_t* src;     // bf16 [n, 576] latent rows
+  int n;
+  const int32_t* dst_row;  // [n] destination cache row (< 0: skipped)
+  uint8_t* kv;             // packed FP8 latent rows of 656 bytes
+};
+
 // Kernel launchers (asynchronous, on `stream`).  Each records the armed
 // timing events of its kernel, if any.
 hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream);
@@ -98,6 +105,7 @@ hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream);
 bool score_selects(const SeqView& sv);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool kv_fp8, hipStream_t stream);
+hipError_t launch_kv_fp8_write(const KvWriteParams& p, hipStream_t stream);
 
 // Timing hook (api.cpp): the events armed for the next launch of `kernel`
 // (null when none), disarmed by the call.

@@ -1,0 +1,84 @@
+// FP8 latent-cache writer on gfx950.
+//
+// Quantises latent rows (576 bf16: 512 latent values, 64 rope values) into
+// the packed 656-byte FP8 row the sparse attention reads: per-token tiles of
+// 128 latent values, each with its own fp32 scale computed online from the
+// row ("Hierarchical Quantization", KV cache bullet, in Day 0 Inference
+// Support for New LLM Architectures; section 4 of Day 0 Inference Adaptation
+// and Performance Optimization for New Models).  Tile j of a row gets
+// scale = amax / 448 and codes E4M3FN(clamp(value / scale, -448, 448)),
+// rounded to the nearest value, ties to even (the gfx950 conversion); an
+// all-zero tile gets scale 0 and codes 0; the rope values are copied.
+//
+// Each wave takes KVW_RPW rows and issues all their loads before using any.
+// Per row, lane l holds latent values 8 l .. 8 l + 7 (one 16-byte load), so
+// the 16 lanes of a row of the wave cover one tile and a 16-lane max
+// reduction gives its amax; each lane stores its 8 codes (8 bytes), the
+// first lane of each tile its scale, and lanes 0..7 copy the rope.  The
+// kernel is HBM-bound: 1152 bytes read and 656 written per row.
+#include "common.h"
+#include "kernels.h"
+
+namespace idxs {
+
+namespace {
+
+constexpr int KVW_WAVES = 4;  // waves per workgroup
+constexpr int KVW_RPW = 4;    // rows per wave
+constexpr int KVW_ROWS = KVW_WAVES * KVW_RPW;
+constexpr float E4M3_MAX_F = 448.0f;
+
+__device__ __forceinline__ float clamp_e4m3(float q) { return fminf(fmaxf(q, -E4M3_MAX_F), E4M3_MAX_F); }
+
+__global__ __launch_bounds__(KVW_WAVES * WAVE) void kv_fp8_write_kernel(KvWriteParams p) {
+  const int lane = threadIdx.x & 63;
+  const int r0 = (blockIdx.x * KVW_WAVES + (threadIdx.x >> 6)) * KVW_RPW;
+  u32x4 w[KVW_RPW], rope[KVW_RPW];
+  int dst[KVW_RPW];
+#pragma unroll
+  for (int j = 0; j < KVW_RPW; ++j) {
+    const int r = min(r0 + j, p.n - 1);  // (rows past n: a valid row, not stored)
+    const uint16_t* src = p.src + (int64_t)r * ROW;
+    dst[j] = r0 + j < p.n ? p.dst_row[r] : -1;
+    w[j] = *(const u32x4*)(src + 8 * lane);
+    rope[j] = *(const u32x4*)(src + LATENT + 8 * (lane & 7));
+  }
+#pragma unroll
+  for (int j = 0; j < KVW_RPW; ++j) {
+    if (dst[j] < 0) continue;
+    uint8_t* out = p.kv + (int64_t)dst[j] * FP8_ROW_BYTES;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[j][e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[j][e] & 0xffff0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, shfl_xor(amax, off));
+    const float scale = amax / E4M3_MAX_F;  // (fp32 division, correctly rounded)
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = scale > 0.0f ? clamp_e4m3(x[i] / scale) : 0.0f;
+    // two codes per conversion: word_sel false fills bytes 0-1, true bytes 2-3
+    uint32_t c0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    c0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)c0, true);
+    uint32_t c1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+    c1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], (int)c1, true);
+    *(u32x2*)(out + 8 * lane) = u32x2{c0, c1};
+    if ((lane & 15) == 0) *(float*)(out + LATENT + 4 * (lane >> 4)) = scale;
+    if (lane < 8) *(u32x4*)(out + LATENT + 16 + 16 * lane) = rope[j];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_fp8_write(const KvWriteParams& p, hipStream_t stream) {
+  const TimerEvents t = timer_take(4);
+  return launch_kernel(kv_fp8_write_kernel, dim3(cdiv(p.n, KVW_ROWS)), dim3(KVW_WAVES * WAVE), stream, t.start,
+                       t.stop, p);
+}
+
+}  // namespace idxs

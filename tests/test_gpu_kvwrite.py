@@ -1,0 +1,125 @@
+"""GPU parity of the FP8 latent-cache writer (idx_kv_fp8_write) through the
+C ABI against the oracle's writer, byte for byte.
+
+Rows cover every rule of the format: an all-zero tile (scale 0), negative
+zeros, values halfway between two codes (tile scale 1, so the ties reach the
+rounding unchanged), values that round to subnormal codes, large
+magnitudes, and standard-normal rows; destination rows are a permutation
+with skipped (-1) entries, and rows not named must keep their bytes.  The
+written cache then goes through the FP8 sparse attention against the
+oracle on the same bytes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import indexer_selected_sparse_idx_amd as lib
+import oracle
+from oracle import writer as W
+
+import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lib.lib()
+
+
+def _rows(n, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    x = torch.randn((n, 576), generator=g, device="cuda")
+    x[0] = 0.0                                               # every tile zero
+    x[1, :128] = 0.0
+    x[1, 3] = -0.0                                           # zero tile holding -0
+    x[2, 128:256] = -0.0
+    x[2, 130] = 2.0                                          # -0 values in a live tile
+    x[3] *= 1e-3
+    x[4] *= 1e4
+    x[5, :128] = torch.linspace(-300.0, 300.0, 128, device="cuda")
+    # tile scale 1 (amax 448): halfway values between neighbouring codes
+    x[6, 256] = 448.0
+    x[6, 257:265] = torch.tensor([1.0625, 1.1875, -1.0625, 3.0 * 2 ** -10, 2 ** -10, 0.5625, 13.0, -26.0],
+                                 device="cuda")
+    # one large value and many tiny ones: subnormal codes
+    x[7, 384] = 100.0
+    x[7, 385:400] = torch.linspace(-0.02, 0.02, 15, device="cuda")
+    return x.to(torch.bfloat16)
+
+
+def _check_rows(kv_host, src_bits, dst, rows_to_check):
+    want = W.fp8_rows_from_bf16(src_bits[rows_to_check])
+    for k, r in enumerate(rows_to_check):
+        d = int(dst[r])
+        if d < 0:
+            continue
+        got = kv_host[d]
+        if not np.array_equal(got, want[k]):
+            diff = np.nonzero(got != want[k])[0]
+            raise AssertionError("source row %d -> cache row %d: %d bytes differ, first at %s (got %s want %s)"
+                                 % (r, d, diff.size, diff[:6], got[diff[:6]], want[k][diff[:6]]))
+
+
+def test_kv_fp8_write_bytes_match_oracle():
+    n, cache_rows = 96, 160
+    src = _rows(n, 41)
+    rng = np.random.default_rng(41)
+    dst = rng.permutation(cache_rows)[:n].astype(np.int32)
+    dst[[9, 40, 77]] = -1
+    kv = torch.full((cache_rows, 656), 0xAB, dtype=torch.uint8, device="cuda")
+    lib.idx_kv_fp8_write(src, torch.from_numpy(dst).cuda(), kv)
+    torch.cuda.synchronize()
+    kv_host = kv.cpu().numpy()
+    bits = U.bits16(src)
+    _check_rows(kv_host, bits, dst, list(range(n)))
+    untouched = sorted(set(range(cache_rows)) - set(int(d) for d in dst if d >= 0))
+    assert np.all(kv_host[untouched] == 0xAB)
+    U.log("kv write: %d rows exact, %d untouched rows kept" % (n - 3, len(untouched)))
+
+
+def test_kv_fp8_write_full_size_sampled_rows():
+    # the long-prefill latent cache: 65,536 rows; 64 sampled rows checked
+    n = 65536
+    src = _rows(n, 42)
+    dst = torch.arange(n, dtype=torch.int32, device="cuda").flip(0)
+    kv = torch.zeros((n, 656), dtype=torch.uint8, device="cuda")
+    lib.idx_kv_fp8_write(src, dst, kv)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(42)
+    rows = sorted(set(rng.integers(0, n, 56).tolist()) | set(range(8)) | {n - 1})
+    bits = U.bits16(src[rows])
+    want = W.fp8_rows_from_bf16(bits)
+    got = kv[[n - 1 - r for r in rows]].cpu().numpy()
+    assert np.array_equal(got, want)
+
+
+def test_kv_fp8_written_cache_through_attention():
+    # cache written by the writer, read by the FP8 sparse attention
+    B, ctx, H, K = 4, 3000, 32, 512
+    src = _rows(B * ctx, 43)
+    kv = torch.empty((B * ctx, 656), dtype=torch.uint8, device="cuda")
+    lib.idx_kv_fp8_write(src, torch.arange(B * ctx, dtype=torch.int32, device="cuda"), kv)
+    g = torch.Generator(device="cuda").manual_seed(44)
+    q = torch.randn((B, H, 576), generator=g, device="cuda").to(torch.bfloat16)
+    rng = np.random.default_rng(44)
+    idx = np.stack([np.concatenate([rng.choice(ctx, K - 8, replace=False), -np.ones(8)]) for _ in range(B)])
+    idx = idx.astype(np.int32)
+    ctx_t = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+    s = lib.Seqs(ctx_t, None, max_q_len=1, max_ctx_len=ctx, num_tokens=B, seq_stride=ctx)
+    out, lse = lib.sparse_mla_attn(s, q, kv, torch.from_numpy(idx).cuda(), U.SCALE)
+    torch.cuda.synchronize()
+    rows = oracle.fp8_rows_to_f64(kv.cpu().numpy())
+    qf = oracle.bf16_bits_to_f64(U.bits16(q))
+    w_out, w_lse = [], []
+    for b in range(B):
+        sel = idx[b][idx[b] >= 0].astype(np.int64) + b * ctx
+        o, l = oracle.sparse_attention(qf[b], rows[sel], U.SCALE)
+        w_out.append(o)
+        w_lse.append(l)
+    U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), np.stack(w_out), np.stack(w_lse), U.TOL_FP8,
+                      "written fp8 cache")
