@@ -19,6 +19,8 @@ scale rule or the rounding; the reading taken here:
 * the 64 rope values are stored unchanged as bf16.
 
 The packed row is the 656-byte layout decoded by formats.fp8_rows_to_f64.
+Index keys (e4m3_keys_from_bf16) follow the same rule with one scale per
+key row, or are stored with scale 1.0.
 """
 import numpy as np
 
@@ -80,3 +82,35 @@ def fp8_rows_from_bf16(bits):
         out[r, LATENT:LATENT + 16] = scales.view(np.uint8)
         out[r, LATENT + 16:] = bits[r, LATENT:].view(np.uint8)
     return out
+
+
+def e4m3_keys_from_bf16(bits, scaled):
+    """bf16 index-key rows (uint16 bit patterns [n, d]) -> (e4m3 codes uint8
+    [n, d], per-row fp32 scales [n] or None).
+
+    scaled=False: code = E4M3(clamp(k, -448, 448)) (keys stored with scale
+    1.0, as the FP8-key workloads hold them).  scaled=True: per row, scale =
+    amax / 448 in fp32 and code = E4M3(clamp(k / scale, -448, 448)) (fp32
+    division), an all-zero row getting scale 0 and codes 0; the indexer then
+    reads the scale as its per-row key scale."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if bits.ndim != 2:
+        raise ValueError("keys must be [n, d]")
+    f32 = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    n, d = f32.shape
+    codes = np.zeros((n, d), dtype=np.uint8)
+    scales = np.zeros(n, dtype=np.float32) if scaled else None
+    for r in range(n):
+        if scaled:
+            amax = np.float32(np.max(np.abs(f32[r])))
+            scale = np.float32(amax / np.float32(E4M3_MAX))
+            scales[r] = scale
+        for i in range(d):
+            v = f32[r, i]
+            if scaled:
+                q = np.float32(v / scale) if scale > 0 else np.float32(0.0)
+            else:
+                q = v
+            q = np.float32(min(max(float(q), -E4M3_MAX), E4M3_MAX))
+            codes[r, i] = e4m3_encode(q)
+    return codes, scales

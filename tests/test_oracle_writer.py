@@ -98,3 +98,34 @@ def test_writer_decodes_within_half_a_code_step():
             # division's own rounding
             bound = np.maximum(np.abs(t) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 2.0 ** -20)
             assert np.all(np.abs(d - t) <= bound)
+
+
+def test_key_writer_unscaled_integers_are_exact():
+    # integer keys in [-16, 16] are exact E4M3 values: scale 1.0 keeps them
+    k = np.arange(-16, 17, dtype=np.float32)
+    k = np.concatenate([k, np.zeros(128 - k.size, np.float32)])[None, :]
+    codes, scales = W.e4m3_keys_from_bf16(_bits(k), scaled=False)
+    assert scales is None
+    assert np.array_equal(F.e4m3_bytes_to_f64(codes), k.astype(np.float64))
+    # 500 clamps to 448; 17 lies halfway between 16 and 18 and goes to the even code (16)
+    c2, _ = W.e4m3_keys_from_bf16(_bits(np.array([[500.0, -500.0, 17.0, 19.0]], np.float32)), scaled=False)
+    assert list(F.e4m3_bytes_to_f64(c2[0])) == [448.0, -448.0, 16.0, 20.0]
+
+
+def test_key_writer_scaled_rows():
+    rng = np.random.default_rng(13)
+    k = rng.integers(-8, 9, (5, 64)).astype(np.float32)
+    k[2] = 0.0
+    k[3, 7] = 8.0
+    codes, scales = W.e4m3_keys_from_bf16(_bits(k), scaled=True)
+    for r in range(5):
+        amax = np.max(np.abs(k[r]))
+        assert scales[r] == np.float32(np.float32(amax) / np.float32(448.0))
+        if amax == 0:
+            assert np.all(codes[r] == 0)
+            continue
+        back = F.e4m3_bytes_to_f64(codes[r]) * scales[r]
+        # the largest key maps to the largest code; every key within half a code step
+        assert np.max(np.abs(F.e4m3_bytes_to_f64(codes[r]))) == 448.0
+        bound = np.maximum(np.abs(k[r]) * 2.0 ** -4, scales[r] * 2.0 ** -10) * (1 + 2.0 ** -20)
+        assert np.all(np.abs(back - k[r]) <= bound)
