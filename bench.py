@@ -46,8 +46,8 @@ def parse():
                     help="1..5: time another workload (all of its calls per step) and print per-kernel "
                          "figures instead of the headline JSON line")
     ap.add_argument("--kv-write", action="store_true",
-                    help="time the FP8 latent-cache writer on 1,048,576 rows and print its own figures "
-                         "instead of the headline JSON line")
+                    help="time the FP8 latent-cache and index-key writers on 1,048,576 rows each and print "
+                         "their own figures instead of the headline JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -250,6 +250,26 @@ def measure_kv_write(steps, warmup):
     us = sorted(times)[len(times) // 2]
     nbytes = n * (1152 + 656 + 4)
     print(json.dumps({"kernel": "FP8 latent-cache writer", "rows": n, "median_us": us,
+                      "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / us / 1e3,
+                      "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "rows_per_s": n / us * 1e6}), flush=True)
+    # index keys: 128 bf16 per row -> 128 e4m3 codes and one fp32 scale
+    keys = torch.randn((n, 128), generator=g, device=dev).to(torch.bfloat16)
+    kc = torch.empty((n, 128), dtype=torch.uint8, device=dev)
+    ks = torch.empty((n,), dtype=torch.float32, device=dev)
+    for _ in range(max(1, warmup)):
+        lib.idx_key_fp8_write(keys, perm, kc, ks)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(1, steps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        lib.idx_key_fp8_write(keys, perm, kc, ks)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    us = sorted(times)[len(times) // 2]
+    nbytes = n * (256 + 128 + 4 + 4)
+    print(json.dumps({"kernel": "FP8 index-key writer (per-row scales)", "rows": n, "median_us": us,
                       "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / us / 1e3,
                       "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "rows_per_s": n / us * 1e6}), flush=True)
 

@@ -216,6 +216,27 @@ int idx_sparse_attn_decode(const idx_seqs *seqs,
  * ------------------------------------------------------------------------ */
 int idx_kv_fp8_write(const void *src, int n, const int32_t *dst_row, void *kv, void *stream);
 
+/* ------------------------------------------------------------------------ *
+ * FP8 index-key writer: store bf16 index keys as E4M3FN codes in an
+ * IDX_E4M3 key cache (rows of d_I bytes), with one fp32 scale per row or
+ * with scale 1.0.  The indexer keys join the FP8 quantisation of "Hierarchical
+ * Quantization" (Day 0 Inference Support..., index-cache bullet); the
+ * per-row scale granularity is this library's reading (the pages quantise
+ * the index in groups of 32, which is not built here).
+ *
+ *   src      bf16 [n, d_I] keys;  d_I in {64, 128};  n >= 0
+ *   dst_row  device int32 [n]: destination cache row (entries < 0 skipped)
+ *   k_cache  E4M3FN key rows of d_I bytes, 16-byte aligned
+ *   k_scale  fp32 per cache row, or NULL.  Non-NULL: row scale = amax / 448
+ *            (fp32), codes E4M3FN(clamp(k / scale, -448, 448)) (an all-zero
+ *            row gets scale 0 and codes 0), and the scale is written to
+ *            k_scale[dst_row[i]] -- the per-row key scale the indexer reads.
+ *            NULL: codes E4M3FN(clamp(k, -448, 448)), scale 1.0.
+ * Rounding: to the nearest E4M3FN value, ties to even, the sign kept.
+ * ------------------------------------------------------------------------ */
+int idx_key_fp8_write(const void *src, int n, int d_I, const int32_t *dst_row, void *k_cache, float *k_scale,
+                      void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *idx_status_string(int status);
 

@@ -62,6 +62,7 @@ _SIGNATURES = {
     "idx_sparse_attn_decode": (_I, [_SEQ, _P, _I, _P, _I, _P, _P, _I, _I, _I, _P, _I, _P, _I, _F,
                                     _P, _P, _P, _P, _SZ, _P]),
     "idx_kv_fp8_write": (_I, [_P, _I, _P, _P, _P]),
+    "idx_key_fp8_write": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "idx_timer_arm": (_I, [_I, _P, _P]),
 }
 
@@ -238,6 +239,17 @@ def idx_kv_fp8_write(src, dst_row, kv):
     rc = lib().idx_kv_fp8_write(_ptr(src), n, _ptr(dst_row), _ptr(kv), _stream())
     _check(rc, "idx_kv_fp8_write")
     return kv
+
+
+def idx_key_fp8_write(src, dst_row, k_cache, k_scale=None):
+    """Store bf16 index keys src [n, d_I] as E4M3FN codes in rows dst_row[i]
+    of k_cache (uint8 [rows, d_I]); with k_scale (fp32 [rows]) each row gets
+    an amax/448 scale written to k_scale, without it the scale is 1.0.
+    Returns k_cache."""
+    n, d = int(src.shape[0]), int(src.shape[1])
+    rc = lib().idx_key_fp8_write(_ptr(src), n, d, _ptr(dst_row), _ptr(k_cache), _ptr(k_scale), _stream())
+    _check(rc, "idx_key_fp8_write")
+    return k_cache
 
 
 def idx_timer_arm(kernel, start_event, stop_event):

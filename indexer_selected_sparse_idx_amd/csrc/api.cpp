@@ -313,6 +313,23 @@ int idx_kv_fp8_write(const void* src, int n, const int32_t* dst_row, void* kv, v
   return launch_kv_fp8_write(p, static_cast<hipStream_t>(stream)) == hipSuccess ? IDX_OK : IDX_ERR_HIP;
 }
 
+int idx_key_fp8_write(const void* src, int n, int d_I, const int32_t* dst_row, void* k_cache, float* k_scale,
+                      void* stream) {
+  if (n < 0 || (d_I != 64 && d_I != 128)) return IDX_ERR_INVALID_ARG;
+  if (n == 0) return IDX_OK;
+  if (!src || !dst_row || !k_cache) return IDX_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(k_cache) || !aligned4(dst_row)) return IDX_ERR_INVALID_ARG;
+  if (k_scale && !aligned4(k_scale)) return IDX_ERR_INVALID_ARG;
+  KeyWriteParams p;
+  p.src = static_cast<const uint16_t*>(src);
+  p.n = n;
+  p.d = d_I;
+  p.dst_row = dst_row;
+  p.k = static_cast<uint8_t*>(k_cache);
+  p.scale = k_scale;
+  return launch_key_fp8_write(p, static_cast<hipStream_t>(stream)) == hipSuccess ? IDX_OK : IDX_ERR_HIP;
+}
+
 int idx_timer_arm(int kernel, void* start_event, void* stop_event) {
   if (kernel < 0 || kernel >= IDX_KERNEL_COUNT || !start_event || !stop_event) return IDX_ERR_INVALID_ARG;
   g_timers[kernel].start = static_cast<hipEvent_t>(start_event);

@@ -98,6 +98,15 @@ struct KvWriteParams {
   uint8_t* kv;             // packed FP8 latent rows of 656 bytes
 };
 
+struct KeyWriteParams {
+  const uint16_t* src;     // bf16 [n, d] index keys
+  int n;
+  int d;                   // 64 or 128
+  const int32_t* dst_row;  // [n] destination cache row (< 0: skipped)
+  uint8_t* k;              // e4m3 key rows of d bytes
+  float* scale;            // per-row fp32 scale, or null (keys stored with scale 1.0)
+};
+
 // Kernel launchers (asynchronous, on `stream`).  Each records the armed
 // timing events of its kernel, if any.
 hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream);
@@ -106,6 +115,7 @@ bool score_selects(const SeqView& sv);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 hipError_t launch_attn(const AttnParams& p, bool kv_fp8, hipStream_t stream);
 hipError_t launch_kv_fp8_write(const KvWriteParams& p, hipStream_t stream);
+hipError_t launch_key_fp8_write(const KeyWriteParams& p, hipStream_t stream);
 
 // Timing hook (api.cpp): the events armed for the next launch of `kernel`
 // (null when none), disarmed by the call.

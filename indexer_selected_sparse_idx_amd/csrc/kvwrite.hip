@@ -1,5 +1,7 @@
 // FP8 latent-cache writer on gfx950.
 //
+// Also writes FP8 index keys (key_fp8_write_kernel, below).
+//
 // Quantises latent rows (576 bf16: 512 latent values, 64 rope values) into
 // the packed 656-byte FP8 row the sparse attention reads: per-token tiles of
 // 128 latent values, each with its own fp32 scale computed online from the
@@ -73,7 +75,71 @@ __global__ __launch_bounds__(KVW_WAVES * WAVE) void kv_fp8_write_kernel(KvWriteP
   }
 }
 
+// Index keys: a row of D bf16 keys spans D / 8 lanes (8 keys each), so a
+// wave step covers 64 / (D / 8) rows; a wave takes KW_STEPS steps, all loads
+// first.  With a scale array, each row's amax comes from a max reduction over
+// its lanes and the row's scale goes to scale[dst]; without, the keys are
+// stored with scale 1.0.
+template <int D>
+__global__ __launch_bounds__(KVW_WAVES * WAVE) void key_fp8_write_kernel(KeyWriteParams p) {
+  constexpr int G = D / 8;        // lanes per row
+  constexpr int RPS = WAVE / G;   // rows per wave step
+  constexpr int KW_STEPS = 4;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / G, gl = lane % G;
+  const int base = (blockIdx.x * KVW_WAVES + (threadIdx.x >> 6)) * RPS * KW_STEPS;
+  u32x4 w[KW_STEPS];
+  int dst[KW_STEPS];
+#pragma unroll
+  for (int j = 0; j < KW_STEPS; ++j) {
+    const int r = base + j * RPS + sub;
+    const int rr = min(r, p.n - 1);  // (rows past n: a valid row, not stored)
+    dst[j] = r < p.n ? p.dst_row[rr] : -1;
+    w[j] = *(const u32x4*)(p.src + (int64_t)rr * D + 8 * gl);
+  }
+#pragma unroll
+  for (int j = 0; j < KW_STEPS; ++j) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[j][e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[j][e] & 0xffff0000u);
+    }
+    float q[8];
+    float scale = 1.0f;
+    if (p.scale) {  // (uniform: every lane reduces)
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+      for (int off = 1; off < G; off <<= 1) amax = fmaxf(amax, shfl_xor(amax, off));
+      scale = amax / E4M3_MAX_F;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = scale > 0.0f ? clamp_e4m3(x[i] / scale) : 0.0f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = clamp_e4m3(x[i]);
+    }
+    if (dst[j] < 0) continue;
+    uint32_t c0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    c0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)c0, true);
+    uint32_t c1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+    c1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], (int)c1, true);
+    *(u32x2*)(p.k + (int64_t)dst[j] * D + 8 * gl) = u32x2{c0, c1};
+    if (p.scale && gl == 0) p.scale[dst[j]] = scale;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_key_fp8_write(const KeyWriteParams& p, hipStream_t stream) {
+  constexpr int KW_STEPS = 4;
+  const int rows_per_wg = KVW_WAVES * KW_STEPS * (WAVE / (p.d == 64 ? 8 : 16));
+  const dim3 grid(cdiv(p.n, rows_per_wg)), block(KVW_WAVES * WAVE);
+  if (p.d == 64) hipLaunchKernelGGL(key_fp8_write_kernel<64>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(key_fp8_write_kernel<128>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_fp8_write(const KvWriteParams& p, hipStream_t stream) {
   const TimerEvents t = timer_take(4);

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
     for want in ["idx_score_topk", "sparse_mla_attn", "idx_sparse_attn_prefill",
                  "idx_sparse_attn_decode", "idx_score_topk_workspace",
                  "sparse_mla_attn_workspace", "idx_sparse_attn_workspace",
-                 "idx_status_string", "idx_timer_arm", "idx_kv_fp8_write"]:
+                 "idx_status_string", "idx_timer_arm", "idx_kv_fp8_write", "idx_key_fp8_write"]:
         assert want in names
 
 
@@ -169,6 +169,18 @@ def test_kv_fp8_write_rejects(L):
     assert L.idx_kv_fp8_write(FAKE, 4, FAKE, FAKE + 8, None) == -1      # misaligned cache
     assert L.idx_kv_fp8_write(FAKE, 4, FAKE + 2, FAKE, None) == -1      # misaligned row map
     assert L.idx_kv_fp8_write(None, 0, None, None, None) == 0           # no rows: no-op
+
+
+def test_key_fp8_write_rejects(L):
+    assert L.idx_key_fp8_write(FAKE, 4, 96, FAKE, FAKE, None, None) == -1     # d_I not 64 or 128
+    assert L.idx_key_fp8_write(FAKE, -1, 128, FAKE, FAKE, None, None) == -1   # negative row count
+    assert L.idx_key_fp8_write(None, 4, 128, FAKE, FAKE, None, None) == -1    # null source
+    assert L.idx_key_fp8_write(FAKE, 4, 128, None, FAKE, None, None) == -1    # null row map
+    assert L.idx_key_fp8_write(FAKE, 4, 128, FAKE, None, None, None) == -1    # null cache
+    assert L.idx_key_fp8_write(FAKE + 8, 4, 128, FAKE, FAKE, None, None) == -1
+    assert L.idx_key_fp8_write(FAKE, 4, 128, FAKE, FAKE + 4, None, None) == -1
+    assert L.idx_key_fp8_write(FAKE, 4, 128, FAKE, FAKE, FAKE + 2, None) == -1  # misaligned scales
+    assert L.idx_key_fp8_write(None, 0, 64, None, None, None, None) == 0      # no rows: no-op
 
 
 def test_empty_batch_is_a_no_op(L):

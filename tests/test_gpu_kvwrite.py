@@ -123,3 +123,61 @@ def test_kv_fp8_written_cache_through_attention():
         w_lse.append(l)
     U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), np.stack(w_out), np.stack(w_lse), U.TOL_FP8,
                       "written fp8 cache")
+
+
+def _keys(n, d, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    k = torch.randn((n, d), generator=g, device="cuda")
+    k[0] = 0.0
+    k[1] = -0.0
+    k[2] *= 1e3                                             # clamps when unscaled
+    k[3, :8] = torch.tensor([1.0625, 17.0, 19.0, -26.0, 2 ** -10, 3 * 2 ** -10, 448.0, 0.5], device="cuda")
+    k[4] = torch.randint(-8, 9, (d,), generator=g, device="cuda").float()
+    return k.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scaled", [False, True])
+def test_key_fp8_write_bytes_match_oracle(d, scaled):
+    n, rows = 200, 300
+    src = _keys(n, d, 50 + d + scaled)
+    rng = np.random.default_rng(d)
+    dst = rng.permutation(rows)[:n].astype(np.int32)
+    dst[[3, 99]] = -1
+    kc = torch.full((rows, d), 0xCD, dtype=torch.uint8, device="cuda")
+    ks = torch.full((rows,), -7.0, dtype=torch.float32, device="cuda") if scaled else None
+    lib.idx_key_fp8_write(src, torch.from_numpy(dst).cuda(), kc, ks)
+    torch.cuda.synchronize()
+    want_c, want_s = W.e4m3_keys_from_bf16(U.bits16(src), scaled)
+    got_c = kc.cpu().numpy()
+    live = dst >= 0
+    assert np.array_equal(got_c[dst[live]], want_c[live])
+    untouched = sorted(set(range(rows)) - set(dst[live].tolist()))
+    assert np.all(got_c[untouched] == 0xCD)
+    if scaled:
+        got_s = ks.cpu().numpy()
+        assert np.array_equal(got_s[dst[live]], want_s[live])
+        assert np.all(got_s[untouched] == -7.0)
+
+
+def test_written_fp8_keys_through_the_indexer():
+    # integer keys stored with scale 1.0 by the writer, scored by the FP8
+    # indexer: the Top-K sets must match the oracle's exactly
+    B, ctx, H_I, d, K = 4, 5000, 64, 128, 512
+    g = torch.Generator(device="cuda").manual_seed(60)
+    keys = torch.randint(-8, 9, (B * ctx, d), generator=g, device="cuda").to(torch.bfloat16)
+    kc = torch.empty((B * ctx, d), dtype=torch.uint8, device="cuda")
+    lib.idx_key_fp8_write(keys, torch.arange(B * ctx, dtype=torch.int32, device="cuda"), kc)
+    q_idx = torch.randint(-4, 5, (B, H_I, d), generator=g, device="cuda").to(torch.bfloat16)
+    head_w = torch.pow(2.0, -torch.randint(0, 4, (B, H_I), generator=g, device="cuda").float())
+    ctx_t = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+    s = lib.Seqs(ctx_t, None, max_q_len=1, max_ctx_len=ctx, num_tokens=B, seq_stride=ctx)
+    idx = lib.idx_score_topk(s, q_idx, kc.view(torch.float8_e4m3fn), head_w, K)
+    torch.cuda.synchronize()
+    kf = oracle.e4m3_bytes_to_f64(kc.cpu().numpy())
+    assert np.array_equal(kf, keys.float().cpu().numpy().astype(np.float64))
+    qf = oracle.bf16_bits_to_f64(U.bits16(q_idx))
+    w = head_w.cpu().numpy().astype(np.float64)
+    want = np.stack([oracle.topk_select(oracle.indexer_scores(qf[b], kf[b * ctx:(b + 1) * ctx], w[b]), K)
+                     for b in range(B)])
+    U.check_indices(idx.cpu().numpy(), want, "written fp8 keys")
