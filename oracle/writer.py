@@ -114,3 +114,32 @@ def e4m3_keys_from_bf16(bits, scaled):
             q = np.float32(min(max(float(q), -E4M3_MAX), E4M3_MAX))
             codes[r, i] = e4m3_encode(q)
     return codes, scales
+
+
+def mx_block_quantize(values):
+    """One MXFP8 block, from the OCP MX definition for E4M3 elements: shared
+    exponent e = floor(log2(amax)) - 8 (8: the exponent of E4M3's largest
+    normal), clamped to [-127, 127], and e = -127 (byte 0) for an all-zero
+    block; codes E4M3(clamp(v / 2^e, -448, 448)).  values: exact floats
+    (32 of them).  Returns (codes uint8 [32], E8M0 byte = e + 127)."""
+    v = np.asarray(values, dtype=np.float64)
+    amax = float(np.max(np.abs(v)))
+    if amax == 0.0:
+        return np.zeros(v.shape, dtype=np.uint8), 0
+    e = int(np.frexp(amax)[1]) - 1 - 8   # frexp: amax = m 2^E, m in [0.5, 1), so floor(log2) = E - 1
+    e = min(max(e, -127), 127)
+    q = np.clip(v / 2.0 ** e, -E4M3_MAX, E4M3_MAX)   # exact: division by a power of two
+    return np.array([e4m3_encode(x) for x in q], dtype=np.uint8), e + 127
+
+
+def mxfp8_rows_from_values(values):
+    """float rows [n, 128] -> packed MXFP8 rows (uint8 [n, 132])."""
+    from .formats import MX_BLOCK, MX_D, MX_ROW_BYTES
+    v = np.asarray(values, dtype=np.float64)
+    out = np.zeros((v.shape[0], MX_ROW_BYTES), dtype=np.uint8)
+    for r in range(v.shape[0]):
+        for b in range(MX_D // MX_BLOCK):
+            codes, e8 = mx_block_quantize(v[r, b * MX_BLOCK:(b + 1) * MX_BLOCK])
+            out[r, b * MX_BLOCK:(b + 1) * MX_BLOCK] = codes
+            out[r, MX_D + b] = e8
+    return out

@@ -129,3 +129,33 @@ def test_key_writer_scaled_rows():
         assert np.max(np.abs(F.e4m3_bytes_to_f64(codes[r]))) == 448.0
         bound = np.maximum(np.abs(k[r]) * 2.0 ** -4, scales[r] * 2.0 ** -10) * (1 + 2.0 ** -20)
         assert np.all(np.abs(back - k[r]) <= bound)
+
+
+def test_mx_block_follows_the_shared_exponent_rule():
+    # amax 4 -> e = floor(log2 4) - 8 = -6: 4 -> 256 (0x78), -3 -> -192 (0xF4), 1 -> 64 (0x68)
+    codes, e8 = W.mx_block_quantize([4.0, -3.0, 1.0, 0.0] + [0.0] * 28)
+    assert e8 == 127 - 6 and list(codes[:4]) == [0x78, 0xF4, 0x68, 0x00]
+    # the largest element lands in [256, 448] (or saturates to 448 above it)
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        v = rng.normal(0, 10.0 ** rng.uniform(-6, 6), 32)
+        c, e8 = W.mx_block_quantize(v)
+        top = np.max(np.abs(F.E4M3_TABLE[c]))
+        assert 256.0 <= top <= 448.0
+        back = F.E4M3_TABLE[c] * 2.0 ** (e8 - 127)
+        # within half a code step, or saturated at 448 (|v| / 2^e in (448, 512))
+        step = np.maximum(np.abs(v) * 2.0 ** -4, 2.0 ** (e8 - 127 - 9))
+        ok = (np.abs(back - v) <= step) | (np.abs(v) / 2.0 ** (e8 - 127) > 448.0)
+        assert np.all(ok)
+    z, e8 = W.mx_block_quantize(np.zeros(32))
+    assert e8 == 0 and np.all(z == 0)
+
+
+def test_mxfp8_rows_round_trip_integer_keys():
+    rng = np.random.default_rng(5)
+    k = rng.integers(-8, 9, (6, 128)).astype(np.float64)
+    k[2, :32] = 0.0
+    packed = W.mxfp8_rows_from_values(k)
+    assert packed.shape == (6, F.MX_ROW_BYTES)
+    assert np.array_equal(F.mxfp8_rows_to_f64(packed), k)
+    assert packed[2, 128] == 0                               # all-zero block: exponent byte 0
