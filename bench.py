@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--kv-write", action="store_true",
                     help="time the FP8 latent-cache and index-key writers on 1,048,576 rows each and print "
                          "their own figures instead of the headline JSON line")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="time the decode indexer (scores + Top-K) on the 64 x 32768 decode batch with MXFP8 "
+                         "key rows and with bf16 keys, and print their own figures instead of the headline line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -274,6 +277,60 @@ def measure_kv_write(steps, warmup):
                       "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "rows_per_s": n / us * 1e6}), flush=True)
 
 
+def measure_mxfp8(steps, warmup):
+    """Decode indexer (scores + Top-K) on the decode batch (64 requests x
+    32768 positions, 64 index heads of 128, Top-K 2048) with MXFP8 key rows
+    (128 E4M3 codes + 4 E8M0 block exponents, 132 bytes per position) and,
+    for comparison, with the workload's bf16 keys (256 bytes per position).
+    The score kernel streams the keys once: algorithmic bytes per launch are
+    the key rows plus the queries and head weights, HBM-bound."""
+    import numpy as np
+    import torch
+    import indexer_selected_sparse_idx_amd as lib
+    from workloads import config, generate, gen
+    dev = torch.device("cuda:0")
+    wl = config(2)
+    inp = generate(wl, dev)
+    call = inp.calls[0]
+    T = call.num_tokens
+    g = torch.Generator(device=dev).manual_seed(8)
+    keys_mx = gen.mxfp8_key_rows(g, inp.k_idx.shape[0], dev)
+    ctx_t = torch.from_numpy(call.ctx_len.astype(np.int32)).to(dev)
+    seqs = lib.Seqs(ctx_t, None, max_q_len=1, max_ctx_len=int(call.ctx_len.max()), seq_stride=inp.seq_stride)
+    idx = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
+    ws = torch.empty(lib.idx_score_topk_workspace(seqs, wl.H_I, wl.d_I, wl.top_k), dtype=torch.uint8, device=dev)
+    positions = int(call.ctx_len.sum())
+    for label, keys, row_bytes in (("MXFP8 keys", keys_mx, 132), ("bf16 keys", inp.k_idx, 256)):
+        def run():
+            lib.idx_score_topk(seqs, inp.q_idx, keys, inp.head_w, wl.top_k, out_idx=idx, ws=ws)
+        for _ in range(max(1, warmup)):
+            run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(max(1, steps)):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        call_us = a.elapsed_time(b) * 1e3 / max(1, steps)
+        times = []
+        for _ in range(max(1, steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            e1.record()
+            torch.cuda.synchronize()
+            lib.idx_timer_arm(lib.IDX_KERNEL_SCORE, e0, e1)
+            run()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        us = sorted(times)[len(times) // 2]
+        nbytes = positions * row_bytes + T * wl.H_I * (wl.d_I * 2 + 4)
+        print(json.dumps({"kernel": "decode indexer score, " + label, "tokens": T, "positions": positions,
+                          "score_median_us": us, "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / us / 1e3,
+                          "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "score_topk_call_us": call_us}),
+              flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -307,6 +364,9 @@ def main():
         return
     if args.kv_write:
         measure_kv_write(args.steps, args.warmup)
+        return
+    if args.mxfp8:
+        measure_mxfp8(args.steps, args.warmup)
         return
     wl = config(2)
     inp = generate(wl, dev)

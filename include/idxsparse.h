@@ -65,7 +65,7 @@ typedef enum {
 typedef enum {
   IDX_BF16 = 1,        /* bfloat16                                               */
   IDX_E4M3 = 2,        /* OCP FP8 E4M3FN codes, one byte per value               */
-  IDX_KV_FP8_656 = 3   /* packed FP8 latent row of 656 bytes: 512 e4m3 latent
+  IDX_KV_FP8_656 = 3,  /* packed FP8 latent row of 656 bytes: 512 e4m3 latent
                           codes, 4 little-endian fp32 scales (one per
                           128-value tile; value j = code[j] * scale[j / 128]),
                           64 bf16 rope values.  The per-token tile of 128 with
@@ -73,6 +73,15 @@ typedef enum {
                           (Day 0 Inference Support..., KV cache bullet) and
                           section 4 of Day 0 Inference Adaptation and
                           Performance Optimization for New Models.           */
+  IDX_MXFP8 = 4        /* MXFP8 index-key row of 132 bytes (d_I = 128): 128
+                          E4M3FN codes, then 4 E8M0 bytes, one per block of 32
+                          codes (value j = code[j] * 2^(byte[j / 32] - 127)).
+                          The index quantised in blocks of 32 ("Hierarchical
+                          Quantization", index-cache bullet, Day 0 Inference
+                          Support...).  Rows are 4-byte aligned; decode calls
+                          only; the query is quantised on the fly per head and
+                          block of 32 (shared exponent floor(log2 amax) - 8,
+                          codes E4M3(clamp(q / 2^e, +-448))).                */
 } idx_dtype;
 
 typedef struct idx_seqs {
@@ -106,7 +115,8 @@ typedef struct idx_seqs {
  * fp32 from bf16 (or e4m3) products.
  *
  *   q_idx    [T, H_I, d_I], dtype q_dtype (IDX_BF16)
- *   k_idx    cache rows of d_I values, dtype k_dtype (IDX_BF16 or IDX_E4M3)
+ *   k_idx    cache rows of d_I values, dtype k_dtype (IDX_BF16, IDX_E4M3, or
+ *            IDX_MXFP8: 132-byte rows, d_I = 128, decode calls, k_scale NULL)
  *   k_scale  fp32 per cache row, or NULL for 1.0.  A quantisation scale, so it
  *            must be >= 0: ReLU(k * x) = k * ReLU(x) then holds, and prefill
  *            calls apply it to the head-weighted sum (one multiply per key)

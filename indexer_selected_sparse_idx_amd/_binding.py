@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.environ.get("IDXSPARSE_LIB") or os.path.join(_HERE, "libidxsparse.so")
 
 IDX_OK = 0
-IDX_BF16, IDX_E4M3, IDX_KV_FP8_656 = 1, 2, 3
+IDX_BF16, IDX_E4M3, IDX_KV_FP8_656, IDX_MXFP8 = 1, 2, 3, 4
+MX_ROW_BYTES = 132   # MXFP8 index-key row: 128 e4m3 codes, 4 E8M0 bytes
 IDX_KERNEL_SCORE, IDX_KERNEL_TOPK, IDX_KERNEL_ATTN, IDX_KERNEL_COMBINE, IDX_KERNEL_KV_WRITE = 0, 1, 2, 3, 4
 FP8_ROW_BYTES = 656
 
@@ -133,6 +134,8 @@ class Seqs:
 def _kdtype(t):
     if t.dtype == torch.bfloat16:
         return IDX_BF16
+    if t.dtype == torch.uint8 and t.dim() == 2 and t.shape[1] == MX_ROW_BYTES:
+        return IDX_MXFP8
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return IDX_E4M3
     raise ValueError("unsupported index-key dtype %s" % t.dtype)

@@ -69,12 +69,18 @@ int check_indexer(const idx_seqs* seqs, const void* q_idx, int q_dtype, const vo
   int rc = check_seqs(seqs);
   if (rc) return rc;
   if (!q_idx || !k_idx || !head_w) return IDX_ERR_INVALID_ARG;
-  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned4(head_w)) return IDX_ERR_INVALID_ARG;
+  if (!aligned16(q_idx) || !aligned4(head_w)) return IDX_ERR_INVALID_ARG;
+  if (k_dtype != IDX_MXFP8 && !aligned16(k_idx)) return IDX_ERR_INVALID_ARG;
   if (k_scale && !aligned4(k_scale)) return IDX_ERR_INVALID_ARG;
   if (H_I < 1 || top_k < 1) return IDX_ERR_INVALID_ARG;
   if (q_dtype != IDX_BF16) return IDX_ERR_UNSUPPORTED;
-  if (k_dtype != IDX_BF16 && k_dtype != IDX_E4M3) return IDX_ERR_UNSUPPORTED;
+  if (k_dtype != IDX_BF16 && k_dtype != IDX_E4M3 && k_dtype != IDX_MXFP8) return IDX_ERR_UNSUPPORTED;
   if (H_I > 64 || (d_I != 64 && d_I != 128) || top_k > 2048) return IDX_ERR_UNSUPPORTED;
+  if (k_dtype == IDX_MXFP8) {
+    // 4-byte aligned 132-byte rows; decode calls only; no per-row key scale
+    if (!aligned4(k_idx) || k_scale) return IDX_ERR_INVALID_ARG;
+    if (d_I != 128 || seqs->max_q_len != 1) return IDX_ERR_UNSUPPORTED;
+  }
   return IDX_OK;
 }
 
@@ -145,7 +151,8 @@ int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int 
   sp.hist = reinterpret_cast<uint32_t*>(base + hist_off);
   sp.top_k = top_k;
   sp.out_idx = out_idx;
-  if (launch_score(sp, k_dtype == IDX_E4M3, stream) != hipSuccess) return IDX_ERR_HIP;
+  const int k_format = k_dtype == IDX_E4M3 ? 1 : k_dtype == IDX_MXFP8 ? 2 : 0;
+  if (launch_score(sp, k_format, stream) != hipSuccess) return IDX_ERR_HIP;
   if (score_selects(sp.sv)) {
     // the score kernel has selected: an armed Top-K timer measures nothing
     const TimerEvents t = timer_take(IDX_KERNEL_TOPK);

@@ -109,7 +109,8 @@ struct KeyWriteParams {
 
 // Kernel launchers (asynchronous, on `stream`).  Each records the armed
 // timing events of its kernel, if any.
-hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream);
+// k_format: 0 bf16 keys, 1 e4m3 keys, 2 MXFP8 key rows (decode only)
+hipError_t launch_score(const ScoreParams& p, int k_format, hipStream_t stream);
 // true when launch_score also runs the Top-K selection (out_idx is then final)
 bool score_selects(const SeqView& sv);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);

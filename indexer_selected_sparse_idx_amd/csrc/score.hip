@@ -229,6 +229,182 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode indexer over MXFP8 keys (d_I = 128): the index quantised in blocks
+// of 32 values sharing a power-of-two scale ("Hierarchical Quantization",
+// index-cache bullet, in Day 0 Inference Support for New LLM Architectures;
+// section 4 of Day 0 Inference Adaptation and Performance Optimization for
+// New Models).  A key row is 128 E4M3FN codes and 4 E8M0 bytes (132 bytes,
+// read with dword loads: rows are 4-byte aligned).  The query is quantised
+// on the fly, per head and block of 32, with the same rule as the keys'
+// writer: shared exponent floor(log2(amax)) - 8, codes E4M3(clamp(q / 2^e,
+// +-448)).  One v_mfma_scale_f32_16x16x128_f8f6f4 covers 16 heads x 16 keys
+// x all 128 dims: lane (c, g) holds head / key c of its tile and dims
+// 32 g .. 32 g + 31 - one MX block - with that block's E8M0 byte as its scale
+// operand.  The rest (pipeline, epilogue, histogram) is the decode kernel's.
+// ---------------------------------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+template <int MT>
+__global__ __launch_bounds__(256) void score_mx_kernel(ScoreParams p, int keys_per_wg) {
+  constexpr int MX_ROW = 132;
+  __shared__ uint32_t lhist[SCORE_HIST_BINS];
+  __shared__ int pages[SCORE_MAX_KPW];
+  __shared__ float sbuf[SCORE_WAVES][SCORE_WAVE_KEYS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const SeqView& sv = p.sv;
+  for (int i = threadIdx.x; i < SCORE_HIST_BINS; i += 256) lhist[i] = 0;
+  const int b = blockIdx.y;
+  const int tok = first_token(sv, b);
+  const int t = sv.ctx_len[b] - 1;
+  const int wg_lo = blockIdx.x * keys_per_wg;
+  const int per_wave = keys_per_wg / SCORE_WAVES;
+  const int key_lo = wg_lo + wave * per_wave;
+  const int key_hi = min(t, key_lo + per_wave - 1);
+  const bool active = key_lo <= key_hi;
+  const int page0 = wg_lo >> sv.page_shift;
+  if (sv.block_table) {
+    const int last = min(sv.ctx_len[b], wg_lo + keys_per_wg) - 1;
+    const int np = last >= wg_lo ? (last >> sv.page_shift) - page0 + 1 : 0;
+    for (int i = threadIdx.x; i < np; i += 256) pages[i] = sv.block_table[(int64_t)b * sv.bt_stride + page0 + i];
+  }
+  __syncthreads();
+
+  if (active) {
+    // ---- query operand ------------------------------------------------------
+    // The scaled MFMA reads, in lane group g, the values k = 16 g .. +15 from
+    // bytes 0..15 and k = 64 + 16 g .. +15 from bytes 16..31, and takes the
+    // exponent of the 32-value block s of row m from lane m + 16 s.  So lane
+    // (c, g) finds the exponent of block g of head 16 mt + c, passes it as its
+    // scale operand, and quantises its two 16-value halves with the exponents
+    // of blocks g >> 1 and 2 + (g >> 1), fetched from the lanes that own them.
+    i32x8 qa[MT];
+    int qe[MT];
+    float w[MT][4];
+    const uint16_t* qrow = p.q_idx + (int64_t)tok * p.H_I * 128;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = mt * 16 + c;
+      const uint16_t* qh = qrow + (int64_t)h * 128;
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (h < p.H_I) raw = *(const u32x4*)(qh + 32 * g + 8 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[e] << 16)), fabsf(__uint_as_float(raw[e] & 0xffff0000u))));
+      }
+      // shared exponent floor(log2 amax) - 8 (frexp: amax = m 2^E, m in [0.5, 1))
+      const int e = amax > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(amax) - 9, -127), 127) : -127;
+      qe[mt] = e + 127;
+      const int e_lo = __shfl(e, c + 16 * (g >> 1));
+      const int e_hi = __shfl(e, c + 16 * (2 + (g >> 1)));
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int eh = half ? e_hi : e_lo;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          u32x4 raw = {0u, 0u, 0u, 0u};
+          if (h < p.H_I) raw = *(const u32x4*)(qh + 64 * half + 16 * g + 8 * j);
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            float x[4];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              const uint32_t r = raw[2 * e2 + k];
+              x[2 * k] = fminf(fmaxf(__builtin_amdgcn_ldexpf(__uint_as_float(r << 16), -eh), -448.0f), 448.0f);
+              x[2 * k + 1] = fminf(fmaxf(__builtin_amdgcn_ldexpf(__uint_as_float(r & 0xffff0000u), -eh), -448.0f), 448.0f);
+            }
+            qa[mt][4 * half + 2 * j + e2] = (int)fp8x4(x[0], x[1], x[2], x[3]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hr = mt * 16 + g * 4 + r;
+        w[mt][r] = hr < p.H_I ? p.head_w[(int64_t)tok * p.H_I + hr] : 0.0f;
+      }
+    }
+
+    float* srow = p.scores + (int64_t)tok * p.score_stride;
+    const int pmask = (1 << sv.page_shift) - 1;
+    const int64_t seq_base = (int64_t)b * sv.seq_stride;
+
+    // key s0 + 16 nt + c (clamped to key_hi: rows past it are masked at the
+    // store): its codes 16 g .. +15 and 64 + 16 g .. +15, and block g's
+    // exponent byte (rows are 132 bytes, so only 4-byte aligned)
+    auto load = [&](int s0, i32x8 (&kb)[NT], int (&ke)[NT]) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int s = min(s0 + nt * 16 + c, key_hi);
+        const int64_t row = sv.block_table ? ((int64_t)pages[(s >> sv.page_shift) - page0] << sv.page_shift) + (s & pmask)
+                                           : seq_base + s;
+        const uint8_t* krow = p.k_idx + row * MX_ROW;
+        const uint32_t* kw = (const uint32_t*)(krow + 16 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kb[nt][j] = (int)kw[j];
+          kb[nt][4 + j] = (int)kw[16 + j];
+        }
+        ke[nt] = krow[128 + g];
+      }
+    };
+    auto compute = [&](int s0, const i32x8 (&kb)[NT], const int (&ke)[NT]) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float v = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], kb[nt], f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                            0, 0, 0, qe[mt], 0, ke[nt]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v += w[mt][r] * relu(acc[r]);
+        }
+        v += shfl_xor(v, 16);
+        v += shfl_xor(v, 32);
+        const int s = s0 + nt * 16 + c;
+        if (g == 0 && s <= key_hi) {
+          sbuf[wave][s - key_lo] = v;
+          atomicAdd(&lhist[score_key(v) >> (32 - SCORE_HIST_BITS)], 1u);
+        }
+      }
+    };
+
+    // stage pairs in a loop with its one exit at the bottom, odd stage after it
+    i32x8 ra[NT], rb[NT];
+    int ea[NT], eb[NT];
+    const int stages = (key_hi - key_lo) / (16 * NT) + 1;
+    int s0 = key_lo;
+    load(s0, ra, ea);
+    for (int i = 0; i + 2 <= stages; i += 2) {
+      load(s0 + 16 * NT, rb, eb);
+      compute(s0, ra, ea);
+      load(s0 + 32 * NT, ra, ea);
+      compute(s0 + 16 * NT, rb, eb);
+      s0 += 32 * NT;
+    }
+    if (stages & 1) compute(s0, ra, ea);
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i <= key_hi - key_lo; i += WAVE) srow[key_lo + i] = sbuf[wave][i];
+  }
+
+  __syncthreads();
+  uint32_t* gh = p.hist + (int64_t)tok * SCORE_HIST_BINS;
+  for (int i = threadIdx.x; i < SCORE_HIST_BINS; i += 256) {
+    const uint32_t v = lhist[i];
+    if (v) atomicAdd(&gh[i], v);
+  }
+}
+
 __global__ void zero_kernel(uint32_t* p, int64_t n4) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
     ((u32x4*)p)[i] = u32x4{0u, 0u, 0u, 0u};
@@ -768,7 +944,8 @@ hipError_t launch_dt(const ScoreParams& p, hipStream_t stream, const TimerEvents
 
 }  // namespace
 
-hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream) {
+hipError_t launch_score(const ScoreParams& p, int k_format, hipStream_t stream) {
+  const bool k_fp8 = k_format == 1;
   // the decode kernel accumulates the row histograms with atomics: clear
   // them first (a kernel, not a memset, so the call stays safe to capture in
   // a graph); the prefill kernel keeps its histograms in LDS
@@ -779,6 +956,16 @@ hipError_t launch_score(const ScoreParams& p, bool k_fp8, hipStream_t stream) {
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   const TimerEvents t = timer_take(0);
+  if (k_format == 2) {  // MXFP8 keys, decode only, d_I = 128 (checked by the caller)
+    const int kpw = 1024;
+    const dim3 grid(cdiv(p.sv.max_ctx_len, kpw), p.sv.num_seqs);
+    switch (cdiv(p.H_I, 16)) {
+      case 1: return launch_kernel(score_mx_kernel<1>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
+      case 2: return launch_kernel(score_mx_kernel<2>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
+      case 3: return launch_kernel(score_mx_kernel<3>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
+      default: return launch_kernel(score_mx_kernel<4>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
+    }
+  }
   return k_fp8 ? launch_dt<true>(p, stream, t) : launch_dt<false>(p, stream, t);
 }
 

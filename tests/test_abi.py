@@ -159,6 +159,20 @@ def test_timer_arm_rejects_bad_kernel(L):
     assert L.idx_timer_arm(0, None, FAKE) == -1
 
 
+def test_mxfp8_keys_checks(L):
+    s = seqs()
+    # a bad workspace comes last: every MXFP8 case that passes the argument
+    # checks reaches the workspace check (-3), so nothing is launched
+    assert score(L, s, kdt=4, ws=None, wsb=0) == -3                    # accepted: decode, d_I 128
+    assert score(L, s, kdt=4, k=FAKE + 4, ws=None, wsb=0) == -3        # 132-byte rows: 4-byte alignment suffices
+    assert score(L, s, kdt=4, k=FAKE + 2) == -1                         # not 4-byte aligned
+    assert score(L, s, kdt=4, ks=FAKE) == -1                            # no per-row key scale
+    assert score(L, s, kdt=4, d_I=64) == -2                             # d_I 128 only
+    assert score(L, s, kdt=1, k=FAKE + 4) == -1                         # other key types: 16-byte aligned
+    sp = seqs(cu_q=FAKE, num_seqs=1, num_tokens=8, max_q_len=8)
+    assert score(L, sp, kdt=4) == -2                                    # decode calls only
+
+
 def test_kv_fp8_write_rejects(L):
     # host-side checks only: nothing is launched for any of these
     assert L.idx_kv_fp8_write(FAKE, -1, FAKE, FAKE, None) == -1         # negative row count

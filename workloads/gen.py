@@ -181,6 +181,23 @@ def _fp8_rows(gen, n, device):
     return out
 
 
+MX_ROW_BYTES = 132   # MXFP8 index-key row: 128 e4m3 codes, 4 E8M0 block exponents
+
+
+def mxfp8_key_rows(gen, n, device, k_range=8, e8_lo=121, e8_hi=123):
+    """Packed MXFP8 index-key rows for n positions: the codes hold 32 k for
+    integers k uniform in [-k_range, k_range] (exact E4M3 values for
+    k_range <= 14), and each block of 32 takes an E8M0 byte uniform in
+    [e8_lo, e8_hi], so a key decodes to k * 2^(byte - 122).  With the default
+    ranges, integer queries in [-4, 4] and head weights 2^-3 .. 1, every
+    partial sum of the indexer score fits fp32's 24 bits (at most 2^19 in
+    steps of 2^-4), so the scores are exact."""
+    k = torch.randint(-k_range, k_range + 1, (n, 128), generator=gen, device=device)
+    codes = (k.float() * 32.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    e8 = torch.randint(e8_lo, e8_hi + 1, (n, 4), generator=gen, device=device).to(torch.uint8)
+    return torch.cat([codes, e8], dim=1).contiguous()
+
+
 def generate(wl, device="cpu", chunk_rows=1 << 20):
     """Draw every tensor of workload `wl` on `device` (seeded by wl.seed)."""
     device = torch.device(device)
