@@ -280,7 +280,7 @@ def measure_kv_write(steps, warmup):
 def measure_mxfp8(steps, warmup):
     """Decode indexer (scores + Top-K) on the decode batch (64 requests x
     32768 positions, 64 index heads of 128, Top-K 2048) with MXFP8 key rows
-    (128 E4M3 codes + 4 E8M0 block exponents, 132 bytes per position) and,
+    (128 E4M3 codes and 4 E8M0 block exponents, 132 bytes per position) and,
     for comparison, with the workload's bf16 keys (256 bytes per position).
     The score kernel streams the keys once: algorithmic bytes per launch are
     the key rows plus the queries and head weights, HBM-bound."""
@@ -294,15 +294,15 @@ def measure_mxfp8(steps, warmup):
     call = inp.calls[0]
     T = call.num_tokens
     g = torch.Generator(device=dev).manual_seed(8)
-    keys_mx = gen.mxfp8_key_rows(g, inp.k_idx.shape[0], dev)
+    codes_mx, exps_mx = gen.mxfp8_keys(g, inp.k_idx.shape[0], dev)
     ctx_t = torch.from_numpy(call.ctx_len.astype(np.int32)).to(dev)
     seqs = lib.Seqs(ctx_t, None, max_q_len=1, max_ctx_len=int(call.ctx_len.max()), seq_stride=inp.seq_stride)
     idx = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
     ws = torch.empty(lib.idx_score_topk_workspace(seqs, wl.H_I, wl.d_I, wl.top_k), dtype=torch.uint8, device=dev)
     positions = int(call.ctx_len.sum())
-    for label, keys, row_bytes in (("MXFP8 keys", keys_mx, 132), ("bf16 keys", inp.k_idx, 256)):
+    for label, keys, exps, row_bytes in (("MXFP8 keys", codes_mx, exps_mx, 132), ("bf16 keys", inp.k_idx, None, 256)):
         def run():
-            lib.idx_score_topk(seqs, inp.q_idx, keys, inp.head_w, wl.top_k, out_idx=idx, ws=ws)
+            lib.idx_score_topk(seqs, inp.q_idx, keys, inp.head_w, wl.top_k, k_scale=exps, out_idx=idx, ws=ws)
         for _ in range(max(1, warmup)):
             run()
         torch.cuda.synchronize()

@@ -73,15 +73,16 @@ typedef enum {
                           (Day 0 Inference Support..., KV cache bullet) and
                           section 4 of Day 0 Inference Adaptation and
                           Performance Optimization for New Models.           */
-  IDX_MXFP8 = 4        /* MXFP8 index-key row of 132 bytes (d_I = 128): 128
-                          E4M3FN codes, then 4 E8M0 bytes, one per block of 32
-                          codes (value j = code[j] * 2^(byte[j / 32] - 127)).
-                          The index quantised in blocks of 32 ("Hierarchical
-                          Quantization", index-cache bullet, Day 0 Inference
-                          Support...).  Rows are 4-byte aligned; decode calls
-                          only; the query is quantised on the fly per head and
-                          block of 32 (shared exponent floor(log2 amax) - 8,
-                          codes E4M3(clamp(q / 2^e, +-448))).                */
+  IDX_MXFP8 = 4        /* MXFP8 index keys (d_I = 128): rows of 128 E4M3FN
+                          codes in k_idx, and in k_scale 4 E8M0 bytes per row,
+                          one per block of 32 codes (value j = code[j] *
+                          2^(byte[j / 32] - 127)).  The index quantised in
+                          blocks of 32 ("Hierarchical Quantization",
+                          index-cache bullet, Day 0 Inference Support...).
+                          Decode calls only; the query is quantised on the fly
+                          per head and block of 32 (shared exponent
+                          floor(log2 amax) - 8, codes E4M3(clamp(q / 2^e,
+                          +-448))).                                            */
 } idx_dtype;
 
 typedef struct idx_seqs {
@@ -116,10 +117,13 @@ typedef struct idx_seqs {
  *
  *   q_idx    [T, H_I, d_I], dtype q_dtype (IDX_BF16)
  *   k_idx    cache rows of d_I values, dtype k_dtype (IDX_BF16, IDX_E4M3, or
- *            IDX_MXFP8: 132-byte rows, d_I = 128, decode calls, k_scale NULL)
- *   k_scale  fp32 per cache row, or NULL for 1.0.  A quantisation scale, so it
- *            must be >= 0: ReLU(k * x) = k * ReLU(x) then holds, and prefill
- *            calls apply it to the head-weighted sum (one multiply per key)
+ *            IDX_MXFP8: E4M3 codes, d_I = 128, decode calls); 16-byte aligned
+ *   k_scale  bf16 / e4m3 keys: fp32 per cache row, or NULL for 1.0.  A
+ *            quantisation scale, so it must be >= 0: ReLU(k * x) = k * ReLU(x)
+ *            then holds, and prefill calls apply it to the head-weighted sum
+ *            (one multiply per key).
+ *            IDX_MXFP8: required, uint8 [rows, 4] E8M0 block exponents (row r
+ *            at byte 4 r), 4-byte aligned
  *   head_w   fp32 [T, H_I]
  *   H_I      1..64 indexer heads;  d_I in {64, 128};  top_k 1..2048
  *   out_idx  int32 [T, top_k]
@@ -129,7 +133,7 @@ size_t idx_score_topk_workspace(const idx_seqs *seqs, int H_I, int d_I, int top_
 int idx_score_topk(const idx_seqs *seqs,
                    const void *q_idx, int q_dtype,
                    const void *k_idx, int k_dtype,
-                   const float *k_scale,
+                   const void *k_scale,
                    const float *head_w,
                    int H_I, int d_I, int top_k,
                    int32_t *out_idx,
@@ -183,7 +187,7 @@ size_t idx_sparse_attn_workspace(const idx_seqs *seqs, int H_I, int d_I, int H, 
 int idx_sparse_attn_prefill(const idx_seqs *seqs,
                             const void *q_idx, int q_dtype,
                             const void *k_idx, int k_dtype,
-                            const float *k_scale, const float *head_w,
+                            const void *k_scale, const float *head_w,
                             int H_I, int d_I, int top_k,
                             const void *q, int H,
                             const void *kv, int kv_dtype,
@@ -193,7 +197,7 @@ int idx_sparse_attn_prefill(const idx_seqs *seqs,
 int idx_sparse_attn_decode(const idx_seqs *seqs,
                            const void *q_idx, int q_dtype,
                            const void *k_idx, int k_dtype,
-                           const float *k_scale, const float *head_w,
+                           const void *k_scale, const float *head_w,
                            int H_I, int d_I, int top_k,
                            const void *q, int H,
                            const void *kv, int kv_dtype,

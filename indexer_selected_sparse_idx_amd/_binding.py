@@ -18,7 +18,6 @@ lib_path = os.environ.get("IDXSPARSE_LIB") or os.path.join(_HERE, "libidxsparse.
 
 IDX_OK = 0
 IDX_BF16, IDX_E4M3, IDX_KV_FP8_656, IDX_MXFP8 = 1, 2, 3, 4
-MX_ROW_BYTES = 132   # MXFP8 index-key row: 128 e4m3 codes, 4 E8M0 bytes
 IDX_KERNEL_SCORE, IDX_KERNEL_TOPK, IDX_KERNEL_ATTN, IDX_KERNEL_COMBINE, IDX_KERNEL_KV_WRITE = 0, 1, 2, 3, 4
 FP8_ROW_BYTES = 656
 
@@ -131,10 +130,14 @@ class Seqs:
         return ctypes.byref(self._c)
 
 
-def _kdtype(t):
+def _kdtype(t, k_scale=None):
+    """Key format: bf16, E4M3 (uint8 / float8_e4m3fn codes), or MXFP8 when the
+    scale argument holds uint8 E8M0 block exponents [rows, 4]."""
     if t.dtype == torch.bfloat16:
         return IDX_BF16
-    if t.dtype == torch.uint8 and t.dim() == 2 and t.shape[1] == MX_ROW_BYTES:
+    if k_scale is not None and k_scale.dtype == torch.uint8:
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError("MXFP8 keys must be E4M3 codes")
         return IDX_MXFP8
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return IDX_E4M3
@@ -182,7 +185,7 @@ def idx_score_topk(seqs, q_idx, k_idx, head_w, top_k, k_scale=None, out_idx=None
         out_idx = torch.empty((T, top_k), dtype=torch.int32, device=q_idx.device)
     ws, nbytes = _workspace(idx_score_topk_workspace(seqs, H_I, d_I, top_k), q_idx.device, ws)
     rc = lib().idx_score_topk(seqs.ref, _ptr(q_idx), IDX_BF16 if q_idx.dtype == torch.bfloat16 else -1,
-                              _ptr(k_idx), _kdtype(k_idx), _ptr(k_scale), _ptr(head_w),
+                              _ptr(k_idx), _kdtype(k_idx, k_scale), _ptr(k_scale), _ptr(head_w),
                               H_I, d_I, top_k, _ptr(out_idx), _ptr(ws), nbytes, _stream())
     _check(rc, "idx_score_topk")
     return out_idx
@@ -213,7 +216,7 @@ def _fused(name, seqs, q_idx, k_idx, head_w, top_k, q, kv, softmax_scale, k_scal
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     ws, nbytes = _workspace(idx_sparse_attn_workspace(seqs, H_I, d_I, H, top_k), q.device, ws)
     rc = getattr(lib(), name)(seqs.ref, _ptr(q_idx), IDX_BF16 if q_idx.dtype == torch.bfloat16 else -1,
-                              _ptr(k_idx), _kdtype(k_idx), _ptr(k_scale), _ptr(head_w), H_I, d_I, top_k,
+                              _ptr(k_idx), _kdtype(k_idx, k_scale), _ptr(k_scale), _ptr(head_w), H_I, d_I, top_k,
                               _ptr(q), H, _ptr(kv), _kvdtype(kv), float(softmax_scale),
                               _ptr(out), _ptr(lse), _ptr(out_idx), _ptr(ws), nbytes, _stream())
     _check(rc, name)

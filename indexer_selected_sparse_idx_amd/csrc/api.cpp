@@ -65,20 +65,20 @@ SeqView make_view(const idx_seqs* s) {
 }
 
 int check_indexer(const idx_seqs* seqs, const void* q_idx, int q_dtype, const void* k_idx, int k_dtype,
-                  const float* k_scale, const float* head_w, int H_I, int d_I, int top_k) {
+                  const void* k_scale, const float* head_w, int H_I, int d_I, int top_k) {
   int rc = check_seqs(seqs);
   if (rc) return rc;
   if (!q_idx || !k_idx || !head_w) return IDX_ERR_INVALID_ARG;
   if (!aligned16(q_idx) || !aligned4(head_w)) return IDX_ERR_INVALID_ARG;
-  if (k_dtype != IDX_MXFP8 && !aligned16(k_idx)) return IDX_ERR_INVALID_ARG;
+  if (!aligned16(k_idx)) return IDX_ERR_INVALID_ARG;
   if (k_scale && !aligned4(k_scale)) return IDX_ERR_INVALID_ARG;
   if (H_I < 1 || top_k < 1) return IDX_ERR_INVALID_ARG;
   if (q_dtype != IDX_BF16) return IDX_ERR_UNSUPPORTED;
   if (k_dtype != IDX_BF16 && k_dtype != IDX_E4M3 && k_dtype != IDX_MXFP8) return IDX_ERR_UNSUPPORTED;
   if (H_I > 64 || (d_I != 64 && d_I != 128) || top_k > 2048) return IDX_ERR_UNSUPPORTED;
   if (k_dtype == IDX_MXFP8) {
-    // 4-byte aligned 132-byte rows; decode calls only; no per-row key scale
-    if (!aligned4(k_idx) || k_scale) return IDX_ERR_INVALID_ARG;
+    // the block exponents are required; decode calls only
+    if (!k_scale) return IDX_ERR_INVALID_ARG;
     if (d_I != 128 || seqs->max_q_len != 1) return IDX_ERR_UNSUPPORTED;
   }
   return IDX_OK;
@@ -132,14 +132,15 @@ size_t idx_buf_bytes(const idx_seqs* s, int top_k) {
   return align_up((size_t)std::max(s->num_tokens, 0) * top_k * sizeof(int32_t));
 }
 
-int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int k_dtype, const float* k_scale,
+int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int k_dtype, const void* k_scale,
                 const float* head_w, int H_I, int d_I, int top_k, int32_t* out_idx, void* ws,
                 hipStream_t stream) {
   ScoreParams sp;
   sp.sv = make_view(seqs);
   sp.q_idx = static_cast<const uint16_t*>(q_idx);
   sp.k_idx = static_cast<const uint8_t*>(k_idx);
-  sp.k_scale = k_scale;
+  sp.k_scale = k_dtype == IDX_MXFP8 ? nullptr : static_cast<const float*>(k_scale);
+  sp.k_exp = k_dtype == IDX_MXFP8 ? static_cast<const uint8_t*>(k_scale) : nullptr;
   sp.head_w = head_w;
   sp.H_I = H_I;
   sp.d_I = d_I;
@@ -244,7 +245,7 @@ size_t idx_sparse_attn_workspace(const idx_seqs* seqs, int H_I, int d_I, int H, 
 }
 
 int idx_score_topk(const idx_seqs* seqs, const void* q_idx, int q_dtype, const void* k_idx, int k_dtype,
-                   const float* k_scale, const float* head_w, int H_I, int d_I, int top_k, int32_t* out_idx,
+                   const void* k_scale, const float* head_w, int H_I, int d_I, int top_k, int32_t* out_idx,
                    void* ws, size_t ws_bytes, void* stream) {
   int rc = check_indexer(seqs, q_idx, q_dtype, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k);
   if (rc) return rc;
@@ -269,7 +270,7 @@ int sparse_mla_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, 
 }
 
 static int fused(const idx_seqs* seqs, const void* q_idx, int q_dtype, const void* k_idx, int k_dtype,
-                 const float* k_scale, const float* head_w, int H_I, int d_I, int top_k, const void* q, int H,
+                 const void* k_scale, const float* head_w, int H_I, int d_I, int top_k, const void* q, int H,
                  const void* kv, int kv_dtype, float softmax_scale, float* out, float* lse, int32_t* out_idx,
                  void* ws, size_t ws_bytes, void* stream) {
   int rc = check_indexer(seqs, q_idx, q_dtype, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k);
@@ -291,7 +292,7 @@ static int fused(const idx_seqs* seqs, const void* q_idx, int q_dtype, const voi
 }
 
 int idx_sparse_attn_prefill(const idx_seqs* seqs, const void* q_idx, int q_dtype, const void* k_idx, int k_dtype,
-                            const float* k_scale, const float* head_w, int H_I, int d_I, int top_k, const void* q,
+                            const void* k_scale, const float* head_w, int H_I, int d_I, int top_k, const void* q,
                             int H, const void* kv, int kv_dtype, float softmax_scale, float* out, float* lse,
                             int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
   return fused(seqs, q_idx, q_dtype, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k, q, H, kv, kv_dtype,
@@ -299,7 +300,7 @@ int idx_sparse_attn_prefill(const idx_seqs* seqs, const void* q_idx, int q_dtype
 }
 
 int idx_sparse_attn_decode(const idx_seqs* seqs, const void* q_idx, int q_dtype, const void* k_idx, int k_dtype,
-                           const float* k_scale, const float* head_w, int H_I, int d_I, int top_k, const void* q,
+                           const void* k_scale, const float* head_w, int H_I, int d_I, int top_k, const void* q,
                            int H, const void* kv, int kv_dtype, float softmax_scale, float* out, float* lse,
                            int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
   if (seqs && seqs->cu_q != nullptr) return IDX_ERR_INVALID_ARG;

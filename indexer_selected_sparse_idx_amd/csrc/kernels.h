@@ -46,6 +46,7 @@ struct ScoreParams {
   const uint16_t* q_idx;   // bf16 [T, H_I, d_I]
   const uint8_t* k_idx;    // rows of d_I bf16 (2 bytes) or e4m3 (1 byte)
   const float* k_scale;    // nullable, per row
+  const uint8_t* k_exp;    // MXFP8 keys: 4 E8M0 block exponents per row
   const float* head_w;     // [T, H_I]
   int H_I;
   int d_I;

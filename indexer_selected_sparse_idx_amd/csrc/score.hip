@@ -35,8 +35,11 @@ namespace {
 
 constexpr int SCORE_WAVES = 4;
 constexpr int NT = 2;            // key tiles (16 keys each) per pipeline stage
-constexpr int SCORE_MAX_KPW = 1024;  // keys per workgroup the LDS page table covers
-constexpr int SCORE_WAVE_KEYS = 256;  // keys per wave: decode 1024 / 4 waves, prefill 256 (all waves)
+// keys per workgroup of the decode kernel: each wave loads its token's whole
+// query first, so FP8 keys (half the bytes per key) take longer runs to keep
+// that prologue small against the key stream
+template <bool FP8>
+constexpr int decode_kpw() { return FP8 ? 2048 : 1024; }
 
 // max(x, 0) as one integer max on the bit pattern: negative floats (-0
 // included) are negative integers (fmaxf costs a second instruction that
@@ -72,8 +75,11 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_
   // decode: one histogram shared by the 4 waves (one token);
   // prefill: one histogram per wave (one token each)
   __shared__ uint32_t lhist[DECODE ? 1 : SCORE_WAVES][SCORE_HIST_BINS];
-  __shared__ int pages[SCORE_MAX_KPW];
-  __shared__ float sbuf[SCORE_WAVES][SCORE_WAVE_KEYS];
+  // LDS page table and score staging: a workgroup's keys (decode), or 256
+  // keys for every wave (the multi-token kernel)
+  constexpr int MAXK = DECODE ? decode_kpw<FP8>() : 256 * SCORE_WAVES;
+  __shared__ int pages[MAXK];
+  __shared__ float sbuf[SCORE_WAVES][MAXK / SCORE_WAVES];
   const int lane = threadIdx.x & 63;
   // wave-uniform (scalar) so that the key loop is a uniform loop: a divergent
   // one merges its exit paths and waits for every load at the loop head
@@ -250,12 +256,17 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
+// keys per workgroup of the MXFP8 kernel (the LDS page table and score
+// staging are sized for it): every wave quantises its token's whole query
+// before its keys, so long runs keep that prologue small (1024 keys per
+// workgroup measured 73 us on 64 x 32768 positions, 4096 keys 59 us)
+constexpr int MX_KPW = 4096;
+
 template <int MT>
 __global__ __launch_bounds__(256) void score_mx_kernel(ScoreParams p, int keys_per_wg) {
-  constexpr int MX_ROW = 132;
   __shared__ uint32_t lhist[SCORE_HIST_BINS];
-  __shared__ int pages[SCORE_MAX_KPW];
-  __shared__ float sbuf[SCORE_WAVES][SCORE_WAVE_KEYS];
+  __shared__ int pages[MX_KPW];
+  __shared__ float sbuf[SCORE_WAVES][MX_KPW / SCORE_WAVES];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
@@ -341,21 +352,21 @@ __global__ __launch_bounds__(256) void score_mx_kernel(ScoreParams p, int keys_p
 
     // key s0 + 16 nt + c (clamped to key_hi: rows past it are masked at the
     // store): its codes 16 g .. +15 and 64 + 16 g .. +15, and block g's
-    // exponent byte (rows are 132 bytes, so only 4-byte aligned)
+    // exponent byte
     auto load = [&](int s0, i32x8 (&kb)[NT], int (&ke)[NT]) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int s = min(s0 + nt * 16 + c, key_hi);
         const int64_t row = sv.block_table ? ((int64_t)pages[(s >> sv.page_shift) - page0] << sv.page_shift) + (s & pmask)
                                            : seq_base + s;
-        const uint8_t* krow = p.k_idx + row * MX_ROW;
-        const uint32_t* kw = (const uint32_t*)(krow + 16 * g);
+        const u32x4* kw = (const u32x4*)(p.k_idx + row * 128 + 16 * g);
+        const u32x4 lo = kw[0], hi = kw[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          kb[nt][j] = (int)kw[j];
-          kb[nt][4 + j] = (int)kw[16 + j];
+          kb[nt][j] = (int)lo[j];
+          kb[nt][4 + j] = (int)hi[j];
         }
-        ke[nt] = krow[128 + g];
+        ke[nt] = p.k_exp[row * 4 + g];
       }
     };
     auto compute = [&](int s0, const i32x8 (&kb)[NT], const int (&ke)[NT]) {
@@ -911,10 +922,8 @@ hipError_t launch_mt(const ScoreParams& p, hipStream_t stream, const TimerEvents
     dim3 grid(cdiv(sv.max_q_len, PF_TOKS), sv.num_seqs);
     return launch_kernel(score_prefill_kernel<MT, KS, FP8>, grid, dim3(PF_TOKS * WAVE), stream, t.start, t.stop, p);
   }
-  static_assert(SCORE_MAX_KPW >= 1024 && SCORE_WAVE_KEYS * SCORE_WAVES >= 1024 && SCORE_WAVE_KEYS >= 256,
-                "the LDS page table and score buffers must cover a workgroup's keys");
   if (decode) {
-    const int kpw = 1024;
+    const int kpw = decode_kpw<FP8>();
     dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs);
     return launch_kernel(score_kernel<MT, KS, FP8, true>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
   }
@@ -957,7 +966,7 @@ hipError_t launch_score(const ScoreParams& p, int k_format, hipStream_t stream) 
   }
   const TimerEvents t = timer_take(0);
   if (k_format == 2) {  // MXFP8 keys, decode only, d_I = 128 (checked by the caller)
-    const int kpw = 1024;
+    const int kpw = MX_KPW;
     const dim3 grid(cdiv(p.sv.max_ctx_len, kpw), p.sv.num_seqs);
     switch (cdiv(p.H_I, 16)) {
       case 1: return launch_kernel(score_mx_kernel<1>, grid, dim3(256), stream, t.start, t.stop, p, kpw);

@@ -72,20 +72,20 @@ def fp8_rows_to_f64(rows):
     return out
 
 
-# MXFP8 index keys: rows of 128 e4m3 codes followed by 4 E8M0 scale bytes
-# (one per block of 32 values; the scale of a block is 2^(byte - 127)).  The
-# pages quantise the index to MXFP8 with groups of 32 ("Hierarchical
-# Quantization", index-cache bullet, in Day 0 Inference Support for New LLM
-# Architectures; section 4 of Day 0 Inference Adaptation and Performance
-# Optimization for New Models); the row layout is this library's.
+# MXFP8 index keys: rows of 128 e4m3 codes, and per row 4 E8M0 scale bytes
+# (one per block of 32 values; the scale of a block is 2^(byte - 127)), kept
+# in an array of their own.  The pages quantise the index to MXFP8 with
+# groups of 32 ("Hierarchical Quantization", index-cache bullet, in Day 0
+# Inference Support for New LLM Architectures; section 4 of Day 0 Inference
+# Adaptation and Performance Optimization for New Models); the storage
+# layout is this library's.
 MX_BLOCK = 32
 MX_D = 128
-MX_ROW_BYTES = MX_D + MX_D // MX_BLOCK  # 132
 
 
-def mxfp8_rows_to_f64(rows):
-    """Packed MXFP8 key rows (uint8 [n, 132]) -> float64 [n, 128], exactly."""
-    rows = np.asarray(rows, dtype=np.uint8)
-    codes = E4M3_TABLE[rows[:, :MX_D]]
-    exps = rows[:, MX_D:].astype(np.int64) - 127
-    return codes * np.repeat(np.ldexp(1.0, exps), MX_BLOCK, axis=1)
+def mxfp8_to_f64(codes, exps):
+    """MXFP8 keys (codes uint8 [n, 128], E8M0 bytes uint8 [n, 4]) -> float64
+    [n, 128], exactly."""
+    codes = E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+    e = np.asarray(exps, dtype=np.uint8).astype(np.int64) - 127
+    return codes * np.repeat(np.ldexp(1.0, e), MX_BLOCK, axis=1)

@@ -132,14 +132,16 @@ def mx_block_quantize(values):
     return np.array([e4m3_encode(x) for x in q], dtype=np.uint8), e + 127
 
 
-def mxfp8_rows_from_values(values):
-    """float rows [n, 128] -> packed MXFP8 rows (uint8 [n, 132])."""
-    from .formats import MX_BLOCK, MX_D, MX_ROW_BYTES
+def mxfp8_from_values(values):
+    """float rows [n, 128] -> MXFP8 keys: codes uint8 [n, 128] and E8M0
+    block exponents uint8 [n, 4]."""
+    from .formats import MX_BLOCK, MX_D
     v = np.asarray(values, dtype=np.float64)
-    out = np.zeros((v.shape[0], MX_ROW_BYTES), dtype=np.uint8)
+    codes = np.zeros((v.shape[0], MX_D), dtype=np.uint8)
+    exps = np.zeros((v.shape[0], MX_D // MX_BLOCK), dtype=np.uint8)
     for r in range(v.shape[0]):
         for b in range(MX_D // MX_BLOCK):
-            codes, e8 = mx_block_quantize(v[r, b * MX_BLOCK:(b + 1) * MX_BLOCK])
-            out[r, b * MX_BLOCK:(b + 1) * MX_BLOCK] = codes
-            out[r, MX_D + b] = e8
-    return out
+            c, e8 = mx_block_quantize(v[r, b * MX_BLOCK:(b + 1) * MX_BLOCK])
+            codes[r, b * MX_BLOCK:(b + 1) * MX_BLOCK] = c
+            exps[r, b] = e8
+    return codes, exps

@@ -163,14 +163,14 @@ def test_mxfp8_keys_checks(L):
     s = seqs()
     # a bad workspace comes last: every MXFP8 case that passes the argument
     # checks reaches the workspace check (-3), so nothing is launched
-    assert score(L, s, kdt=4, ws=None, wsb=0) == -3                    # accepted: decode, d_I 128
-    assert score(L, s, kdt=4, k=FAKE + 4, ws=None, wsb=0) == -3        # 132-byte rows: 4-byte alignment suffices
-    assert score(L, s, kdt=4, k=FAKE + 2) == -1                         # not 4-byte aligned
-    assert score(L, s, kdt=4, ks=FAKE) == -1                            # no per-row key scale
-    assert score(L, s, kdt=4, d_I=64) == -2                             # d_I 128 only
-    assert score(L, s, kdt=1, k=FAKE + 4) == -1                         # other key types: 16-byte aligned
+    assert score(L, s, kdt=4, ks=FAKE, ws=None, wsb=0) == -3           # accepted: decode, d_I 128
+    assert score(L, s, kdt=4, ks=FAKE + 4, ws=None, wsb=0) == -3       # exponent rows: 4-byte alignment
+    assert score(L, s, kdt=4, ks=FAKE + 2) == -1                        # exponents not 4-byte aligned
+    assert score(L, s, kdt=4) == -1                                     # exponents required
+    assert score(L, s, kdt=4, ks=FAKE, k=FAKE + 4) == -1                # codes 16-byte aligned
+    assert score(L, s, kdt=4, ks=FAKE, d_I=64) == -2                    # d_I 128 only
     sp = seqs(cu_q=FAKE, num_seqs=1, num_tokens=8, max_q_len=8)
-    assert score(L, sp, kdt=4) == -2                                    # decode calls only
+    assert score(L, sp, kdt=4, ks=FAKE) == -2                                    # decode calls only
 
 
 def test_kv_fp8_write_rejects(L):

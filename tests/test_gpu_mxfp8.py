@@ -1,8 +1,8 @@
-"""GPU parity of the MXFP8 decode indexer (IDX_MXFP8 key rows) through the C
+"""GPU parity of the MXFP8 decode indexer (IDX_MXFP8 keys) through the C
 ABI against the oracle.
 
-Keys are packed MXFP8 rows whose blocks take different E8M0 exponents
-(workloads.mxfp8_key_rows); queries are integers times a power of two that
+Keys are MXFP8 codes whose blocks take different E8M0 exponents
+(workloads.gen.mxfp8_keys); queries are integers times a power of two that
 varies per head and block of 32, so both operands' block scales take part
 and a scale applied to the wrong block or head changes the scores.  The
 oracle quantises the query with the MX rule (oracle/writer.py), decodes the
@@ -54,9 +54,9 @@ def _run(ctx, H_I, K, seed, paged=False):
         for b in range(B):
             bt[b, :npg[b]] = perm[o:o + npg[b]]
             o += npg[b]
-        keys = gen.mxfp8_key_rows(g, sum(npg) * page, "cuda")
+        keys, exps = gen.mxfp8_keys(g, sum(npg) * page, "cuda")
     else:
-        keys = gen.mxfp8_key_rows(g, B * stride, "cuda")
+        keys, exps = gen.mxfp8_keys(g, B * stride, "cuda")
     qi = torch.randint(-4, 5, (B, H_I, 128), generator=g, device="cuda").float()
     shift = torch.randint(0, 2, (B, H_I, 4), generator=g, device="cuda").float()
     q_idx = (qi * torch.pow(2.0, shift).repeat_interleave(32, dim=2)).to(torch.bfloat16)
@@ -67,9 +67,9 @@ def _run(ctx, H_I, K, seed, paged=False):
                      page_size=64)
     else:
         s = lib.Seqs(ctx_t, None, max_q_len=1, max_ctx_len=max(ctx), num_tokens=B, seq_stride=stride)
-    idx = lib.idx_score_topk(s, q_idx, keys, head_w, K)
+    idx = lib.idx_score_topk(s, q_idx, keys, head_w, K, k_scale=exps)
     torch.cuda.synchronize()
-    kf = F.mxfp8_rows_to_f64(keys.cpu().numpy())
+    kf = F.mxfp8_to_f64(keys.cpu().numpy(), exps.cpu().numpy())
     qf = oracle.bf16_bits_to_f64(U.bits16(q_idx))
     w = head_w.cpu().numpy().astype(np.float64)
     bt_h = bt.cpu().numpy() if paged else None
@@ -80,12 +80,12 @@ def _run(ctx, H_I, K, seed, paged=False):
         sc = oracle.indexer_scores(_q_oracle(qf[b]), kf[rows], w[b])
         want.append(oracle.topk_select(sc, K))
     U.check_indices(idx.cpu().numpy(), np.stack(want), "mxfp8 decode")
-    return keys
+    return exps
 
 
 def test_mxfp8_decode_indexer_contiguous():
-    keys = _run([5000, 7777, 130, 2049, 9000, 3000], 64, 512, 70)
-    e8 = keys[:, 128:].cpu().numpy()
+    exps = _run([5000, 7777, 130, 2049, 9000, 3000], 64, 512, 70)
+    e8 = exps.cpu().numpy()
     assert len(np.unique(e8)) == 3                             # the exponents do vary
 
 
@@ -101,7 +101,7 @@ def test_mxfp8_fused_decode_matches_separate_calls():
     B, H_I, K, H = len(ctx), 64, 512, 16
     g = torch.Generator(device="cuda").manual_seed(72)
     stride = max(ctx)
-    keys = gen.mxfp8_key_rows(g, B * stride, "cuda")
+    keys, exps = gen.mxfp8_keys(g, B * stride, "cuda")
     q_idx = torch.randint(-4, 5, (B, H_I, 128), generator=g, device="cuda").to(torch.bfloat16)
     head_w = torch.pow(2.0, -torch.randint(0, 4, (B, H_I), generator=g, device="cuda").float())
     q = torch.randn((B, H, 576), generator=g, device="cuda").to(torch.bfloat16)
@@ -109,8 +109,9 @@ def test_mxfp8_fused_decode_matches_separate_calls():
     ctx_t = torch.tensor(ctx, dtype=torch.int32, device="cuda")
     s = lib.Seqs(ctx_t, None, max_q_len=1, max_ctx_len=max(ctx), num_tokens=B, seq_stride=stride)
     idx = torch.empty((B, K), dtype=torch.int32, device="cuda")
-    out, lse, idx = lib.idx_sparse_attn_decode(s, q_idx, keys, head_w, K, q, kv, U.SCALE, out_idx=idx)
-    idx2 = lib.idx_score_topk(s, q_idx, keys, head_w, K)
+    out, lse, idx = lib.idx_sparse_attn_decode(s, q_idx, keys, head_w, K, q, kv, U.SCALE, k_scale=exps,
+                                               out_idx=idx)
+    idx2 = lib.idx_score_topk(s, q_idx, keys, head_w, K, k_scale=exps)
     out2, lse2 = lib.sparse_mla_attn(s, q, kv, idx2, U.SCALE)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)

@@ -151,11 +151,11 @@ def test_mx_block_follows_the_shared_exponent_rule():
     assert e8 == 0 and np.all(z == 0)
 
 
-def test_mxfp8_rows_round_trip_integer_keys():
+def test_mxfp8_round_trip_integer_keys():
     rng = np.random.default_rng(5)
     k = rng.integers(-8, 9, (6, 128)).astype(np.float64)
     k[2, :32] = 0.0
-    packed = W.mxfp8_rows_from_values(k)
-    assert packed.shape == (6, F.MX_ROW_BYTES)
-    assert np.array_equal(F.mxfp8_rows_to_f64(packed), k)
-    assert packed[2, 128] == 0                               # all-zero block: exponent byte 0
+    codes, exps = W.mxfp8_from_values(k)
+    assert codes.shape == (6, 128) and exps.shape == (6, 4)
+    assert np.array_equal(F.mxfp8_to_f64(codes, exps), k)
+    assert exps[2, 0] == 0                                   # all-zero block: exponent byte 0

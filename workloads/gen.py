@@ -181,11 +181,11 @@ def _fp8_rows(gen, n, device):
     return out
 
 
-MX_ROW_BYTES = 132   # MXFP8 index-key row: 128 e4m3 codes, 4 E8M0 block exponents
 
 
-def mxfp8_key_rows(gen, n, device, k_range=8, e8_lo=121, e8_hi=123):
-    """Packed MXFP8 index-key rows for n positions: the codes hold 32 k for
+def mxfp8_keys(gen, n, device, k_range=8, e8_lo=121, e8_hi=123):
+    """MXFP8 index keys for n positions, as (codes uint8 [n, 128], E8M0
+    block exponents uint8 [n, 4]): the codes hold 32 k for
     integers k uniform in [-k_range, k_range] (exact E4M3 values for
     k_range <= 14), and each block of 32 takes an E8M0 byte uniform in
     [e8_lo, e8_hi], so a key decodes to k * 2^(byte - 122).  With the default
@@ -195,7 +195,7 @@ def mxfp8_key_rows(gen, n, device, k_range=8, e8_lo=121, e8_hi=123):
     k = torch.randint(-k_range, k_range + 1, (n, 128), generator=gen, device=device)
     codes = (k.float() * 32.0).to(torch.float8_e4m3fn).view(torch.uint8)
     e8 = torch.randint(e8_lo, e8_hi + 1, (n, 4), generator=gen, device=device).to(torch.uint8)
-    return torch.cat([codes, e8], dim=1).contiguous()
+    return codes.contiguous(), e8.contiguous()
 
 
 def generate(wl, device="cpu", chunk_rows=1 << 20):
