@@ -79,8 +79,9 @@ typedef enum {
                           2^(byte[j / 32] - 127)).  The index quantised in
                           blocks of 32 ("Hierarchical Quantization",
                           index-cache bullet, Day 0 Inference Support...).
-                          Decode calls only; the query is quantised on the fly
-                          per head and block of 32 (shared exponent
+                          Any batch (in prefill calls each query token streams
+                          its own causal key range); the query is quantised on
+                          the fly per head and block of 32 (shared exponent
                           floor(log2 amax) - 8, codes E4M3(clamp(q / 2^e,
                           +-448))).                                            */
 } idx_dtype;
@@ -117,7 +118,7 @@ typedef struct idx_seqs {
  *
  *   q_idx    [T, H_I, d_I], dtype q_dtype (IDX_BF16)
  *   k_idx    cache rows of d_I values, dtype k_dtype (IDX_BF16, IDX_E4M3, or
- *            IDX_MXFP8: E4M3 codes, d_I = 128, decode calls); 16-byte aligned
+ *            IDX_MXFP8: E4M3 codes, d_I = 128); 16-byte aligned
  *   k_scale  bf16 / e4m3 keys: fp32 per cache row, or NULL for 1.0.  A
  *            quantisation scale, so it must be >= 0: ReLU(k * x) = k * ReLU(x)
  *            then holds, and prefill calls apply it to the head-weighted sum

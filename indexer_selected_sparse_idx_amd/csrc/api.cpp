@@ -77,9 +77,9 @@ int check_indexer(const idx_seqs* seqs, const void* q_idx, int q_dtype, const vo
   if (k_dtype != IDX_BF16 && k_dtype != IDX_E4M3 && k_dtype != IDX_MXFP8) return IDX_ERR_UNSUPPORTED;
   if (H_I > 64 || (d_I != 64 && d_I != 128) || top_k > 2048) return IDX_ERR_UNSUPPORTED;
   if (k_dtype == IDX_MXFP8) {
-    // the block exponents are required; decode calls only
+    // the block exponents are required
     if (!k_scale) return IDX_ERR_INVALID_ARG;
-    if (d_I != 128 || seqs->max_q_len != 1) return IDX_ERR_UNSUPPORTED;
+    if (d_I != 128) return IDX_ERR_UNSUPPORTED;
   }
   return IDX_OK;
 }
@@ -154,7 +154,7 @@ int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int 
   sp.out_idx = out_idx;
   const int k_format = k_dtype == IDX_E4M3 ? 1 : k_dtype == IDX_MXFP8 ? 2 : 0;
   if (launch_score(sp, k_format, stream) != hipSuccess) return IDX_ERR_HIP;
-  if (score_selects(sp.sv)) {
+  if (k_dtype != IDX_MXFP8 && score_selects(sp.sv)) {
     // the score kernel has selected: an armed Top-K timer measures nothing
     const TimerEvents t = timer_take(IDX_KERNEL_TOPK);
     if (t.start) (void)hipEventRecord(t.start, stream);

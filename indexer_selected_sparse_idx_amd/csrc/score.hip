@@ -273,10 +273,13 @@ __global__ __launch_bounds__(256) void score_mx_kernel(ScoreParams p, int keys_p
   const int c = lane & 15;
   const SeqView& sv = p.sv;
   for (int i = threadIdx.x; i < SCORE_HIST_BINS; i += 256) lhist[i] = 0;
-  const int b = blockIdx.y;
-  const int tok = first_token(sv, b);
-  const int t = sv.ctx_len[b] - 1;
-  const int wg_lo = blockIdx.x * keys_per_wg;
+  // grid x: query tokens (a decode batch: one per sequence), so that
+  // neighbouring workgroups of a prefill chunk read the same keys; grid y:
+  // runs of keys_per_wg keys of the token's causal range [0, t]
+  const int tok = blockIdx.x;
+  const int b = seq_of_token(sv, tok);
+  const int t = sv.ctx_len[b] - q_len(sv, b) + (tok - first_token(sv, b));
+  const int wg_lo = blockIdx.y * keys_per_wg;
   const int per_wave = keys_per_wg / SCORE_WAVES;
   const int key_lo = wg_lo + wave * per_wave;
   const int key_hi = min(t, key_lo + per_wave - 1);
@@ -958,16 +961,16 @@ hipError_t launch_score(const ScoreParams& p, int k_format, hipStream_t stream) 
   // the decode kernel accumulates the row histograms with atomics: clear
   // them first (a kernel, not a memset, so the call stays safe to capture in
   // a graph); the prefill kernel keeps its histograms in LDS
-  if (p.sv.max_q_len == 1 || !prefill_fits(p.sv)) {
+  if (k_format == 2 || p.sv.max_q_len == 1 || !prefill_fits(p.sv)) {
     const int64_t n4 = (int64_t)p.sv.num_tokens * SCORE_HIST_BINS / 4;
     const int64_t zblocks = std::min<int64_t>((n4 + 255) / 256, 2048);
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream, p.hist, n4);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   const TimerEvents t = timer_take(0);
-  if (k_format == 2) {  // MXFP8 keys, decode only, d_I = 128 (checked by the caller)
+  if (k_format == 2) {  // MXFP8 keys, d_I = 128 (checked by the caller); any batch
     const int kpw = MX_KPW;
-    const dim3 grid(cdiv(p.sv.max_ctx_len, kpw), p.sv.num_seqs);
+    const dim3 grid(p.sv.num_tokens, cdiv(p.sv.max_ctx_len, kpw));
     switch (cdiv(p.H_I, 16)) {
       case 1: return launch_kernel(score_mx_kernel<1>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
       case 2: return launch_kernel(score_mx_kernel<2>, grid, dim3(256), stream, t.start, t.stop, p, kpw);

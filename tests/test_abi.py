@@ -170,7 +170,7 @@ def test_mxfp8_keys_checks(L):
     assert score(L, s, kdt=4, ks=FAKE, k=FAKE + 4) == -1                # codes 16-byte aligned
     assert score(L, s, kdt=4, ks=FAKE, d_I=64) == -2                    # d_I 128 only
     sp = seqs(cu_q=FAKE, num_seqs=1, num_tokens=8, max_q_len=8)
-    assert score(L, sp, kdt=4, ks=FAKE) == -2                                    # decode calls only
+    assert score(L, sp, kdt=4, ks=FAKE, ws=None, wsb=0) == -3           # prefill batches accepted too
 
 
 def test_kv_fp8_write_rejects(L):

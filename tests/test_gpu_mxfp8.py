@@ -1,4 +1,4 @@
-"""GPU parity of the MXFP8 decode indexer (IDX_MXFP8 keys) through the C
+"""GPU parity of the MXFP8 indexer (IDX_MXFP8 keys) through the C
 ABI against the oracle.
 
 Keys are MXFP8 codes whose blocks take different E8M0 exponents
@@ -41,8 +41,13 @@ def _q_oracle(q):
     return out
 
 
-def _run(ctx, H_I, K, seed, paged=False):
+def _run(ctx, H_I, K, seed, paged=False, qlen=None):
+    """One idx_score_topk call over sequences with context lengths ctx and
+    qlen[b] query tokens each (the last qlen[b] positions; default 1: a
+    decode batch), checked token by token against the oracle."""
     B = len(ctx)
+    qlen = [1] * B if qlen is None else list(qlen)
+    T = sum(qlen)
     g = torch.Generator(device="cuda").manual_seed(seed)
     stride = max(ctx)
     if paged:
@@ -57,16 +62,18 @@ def _run(ctx, H_I, K, seed, paged=False):
         keys, exps = gen.mxfp8_keys(g, sum(npg) * page, "cuda")
     else:
         keys, exps = gen.mxfp8_keys(g, B * stride, "cuda")
-    qi = torch.randint(-4, 5, (B, H_I, 128), generator=g, device="cuda").float()
-    shift = torch.randint(0, 2, (B, H_I, 4), generator=g, device="cuda").float()
+    qi = torch.randint(-4, 5, (T, H_I, 128), generator=g, device="cuda").float()
+    shift = torch.randint(0, 2, (T, H_I, 4), generator=g, device="cuda").float()
     q_idx = (qi * torch.pow(2.0, shift).repeat_interleave(32, dim=2)).to(torch.bfloat16)
-    head_w = torch.pow(2.0, -torch.randint(0, 4, (B, H_I), generator=g, device="cuda").float())
+    head_w = torch.pow(2.0, -torch.randint(0, 4, (T, H_I), generator=g, device="cuda").float())
     ctx_t = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    cu_h = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    cu = None if max(qlen) == 1 else torch.from_numpy(cu_h).to("cuda")
     if paged:
-        s = lib.Seqs(ctx_t, None, max_q_len=1, max_ctx_len=max(ctx), num_tokens=B, block_table=bt,
+        s = lib.Seqs(ctx_t, cu, max_q_len=max(qlen), max_ctx_len=max(ctx), num_tokens=T, block_table=bt,
                      page_size=64)
     else:
-        s = lib.Seqs(ctx_t, None, max_q_len=1, max_ctx_len=max(ctx), num_tokens=B, seq_stride=stride)
+        s = lib.Seqs(ctx_t, cu, max_q_len=max(qlen), max_ctx_len=max(ctx), num_tokens=T, seq_stride=stride)
     idx = lib.idx_score_topk(s, q_idx, keys, head_w, K, k_scale=exps)
     torch.cuda.synchronize()
     kf = F.mxfp8_to_f64(keys.cpu().numpy(), exps.cpu().numpy())
@@ -77,9 +84,12 @@ def _run(ctx, H_I, K, seed, paged=False):
     for b in range(B):
         pos = np.arange(ctx[b])
         rows = (bt_h[b, pos // 64].astype(np.int64) * 64 + pos % 64) if paged else b * stride + pos
-        sc = oracle.indexer_scores(_q_oracle(qf[b]), kf[rows], w[b])
-        want.append(oracle.topk_select(sc, K))
-    U.check_indices(idx.cpu().numpy(), np.stack(want), "mxfp8 decode")
+        for i in range(qlen[b]):
+            tok = cu_h[b] + i
+            t = ctx[b] - qlen[b] + i
+            sc = oracle.indexer_scores(_q_oracle(qf[tok]), kf[rows[:t + 1]], w[tok])
+            want.append(oracle.topk_select(sc, K))
+    U.check_indices(idx.cpu().numpy(), np.stack(want), "mxfp8")
     return exps
 
 
@@ -117,3 +127,13 @@ def test_mxfp8_fused_decode_matches_separate_calls():
     assert torch.equal(idx, idx2)
     assert int((idx[2] >= 0).sum()) == 1 and int((idx[1] >= 0).sum()) == K
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_mxfp8_prefill_chunks_contiguous():
+    # chunks of 37 and 1 tokens and a whole-context chunk of 300 (rows with
+    # t + 1 <= K and a ragged tail), contiguous cache
+    _run([6000, 2500, 300], 64, 256, 73, qlen=[37, 1, 300])
+
+
+def test_mxfp8_prefill_chunks_paged_fewer_heads():
+    _run([5000, 130], 24, 512, 74, paged=True, qlen=[70, 130])
