@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--mxfp8", action="store_true",
                     help="time the decode indexer (scores + Top-K) on the 64 x 32768 decode batch with MXFP8 "
                          "key rows and with bf16 keys, and print their own figures instead of the headline line")
+    ap.add_argument("--multi-token", action="store_true",
+                    help="time multi-token decode rows (2, 4 and 8 query tokens per request, the speculative "
+                         "verification shape) on the decode batch's caches and print their own figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -331,6 +334,70 @@ def measure_mxfp8(steps, warmup):
               flush=True)
 
 
+def measure_multi_token(steps, warmup):
+    """Multi-token decode rows: the decode batch's caches (64 requests x
+    32768 positions, bf16 keys and latent rows) with Q = 2, 4, 8 query tokens
+    per request at its last Q positions (a speculative verification step),
+    through the fused prefill entry point (cu_q batches).  Queries are drawn
+    like the workload's (integer index queries, standard-normal latent
+    queries)."""
+    import numpy as np
+    import torch
+    import indexer_selected_sparse_idx_amd as lib
+    from workloads import config, generate
+    dev = torch.device("cuda:0")
+    wl = config(2)
+    inp = generate(wl, dev)
+    call = inp.calls[0]
+    B = call.num_tokens
+    g = torch.Generator(device=dev).manual_seed(9)
+    scale = 1.0 / math.sqrt(576.0)
+    names = {lib.IDX_KERNEL_SCORE: "score", lib.IDX_KERNEL_TOPK: "topk", lib.IDX_KERNEL_ATTN: "attn",
+             lib.IDX_KERNEL_COMBINE: "combine"}
+    ctx_t = torch.from_numpy(call.ctx_len.astype(np.int32)).to(dev)
+    for Q in (2, 4, 8):
+        T = B * Q
+        cu = torch.arange(0, T + 1, Q, dtype=torch.int32, device=dev)
+        seqs = lib.Seqs(ctx_t, cu, max_q_len=Q, max_ctx_len=int(call.ctx_len.max()), num_tokens=T,
+                        seq_stride=inp.seq_stride)
+        q_idx = torch.randint(-wl.q_range, wl.q_range + 1, (T, wl.H_I, wl.d_I), generator=g,
+                              device=dev).to(torch.bfloat16)
+        head_w = torch.pow(2.0, -torch.randint(0, 4, (T, wl.H_I), generator=g, device=dev).float())
+        q = torch.randn((T, wl.H, 576), generator=g, device=dev).to(torch.bfloat16)
+        out = torch.empty((T, wl.H, 512), dtype=torch.float32, device=dev)
+        lse = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
+        idx = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
+        ws = torch.empty(lib.idx_sparse_attn_workspace(seqs, wl.H_I, wl.d_I, wl.H, wl.top_k), dtype=torch.uint8,
+                         device=dev)
+
+        def run():
+            lib.idx_sparse_attn_prefill(seqs, q_idx, inp.k_idx, head_w, wl.top_k, q, inp.kv, scale, out=out,
+                                        lse=lse, out_idx=idx, ws=ws)
+        for _ in range(max(1, warmup)):
+            run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(max(1, steps)):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / max(1, steps)
+        ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in names}
+        for e0, e1 in ev.values():
+            e0.record()
+            e1.record()
+        torch.cuda.synchronize()
+        for k, (e0, e1) in ev.items():
+            lib.idx_timer_arm(k, e0, e1)
+        run()
+        torch.cuda.synchronize()
+        kt = {names[k]: e0.elapsed_time(e1) * 1e3 for k, (e0, e1) in ev.items()}
+        print(json.dumps({"workload": "multi-token decode: %d requests x %d tokens, ctx %d" % (B, Q, int(call.ctx_len.max())),
+                          "tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "kernels_us": kt}),
+              flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -367,6 +434,9 @@ def main():
         return
     if args.mxfp8:
         measure_mxfp8(args.steps, args.warmup)
+        return
+    if args.multi_token:
+        measure_multi_token(args.steps, args.warmup)
         return
     wl = config(2)
     inp = generate(wl, dev)

@@ -40,6 +40,9 @@ constexpr int NT = 2;            // key tiles (16 keys each) per pipeline stage
 // that prologue small against the key stream
 template <bool FP8>
 constexpr int decode_kpw() { return FP8 ? 2048 : 1024; }
+// keys per workgroup of the multi-token kernel (every wave takes them all,
+// for its own token)
+constexpr int MT_KPW = 1024;
 
 // max(x, 0) as one integer max on the bit pattern: negative floats (-0
 // included) are negative integers (fmaxf costs a second instruction that
@@ -75,11 +78,12 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_
   // decode: one histogram shared by the 4 waves (one token);
   // prefill: one histogram per wave (one token each)
   __shared__ uint32_t lhist[DECODE ? 1 : SCORE_WAVES][SCORE_HIST_BINS];
-  // LDS page table and score staging: a workgroup's keys (decode), or 256
-  // keys for every wave (the multi-token kernel)
-  constexpr int MAXK = DECODE ? decode_kpw<FP8>() : 256 * SCORE_WAVES;
+  // LDS page table and score staging: a workgroup's keys (decode, split
+  // over the waves), or MT_KPW keys for every wave (the multi-token kernel)
+  constexpr int MAXK = DECODE ? decode_kpw<FP8>() : MT_KPW;
+  constexpr int WAVE_KEYS = DECODE ? MAXK / SCORE_WAVES : MT_KPW;
   __shared__ int pages[MAXK];
-  __shared__ float sbuf[SCORE_WAVES][MAXK / SCORE_WAVES];
+  __shared__ float sbuf[SCORE_WAVES][WAVE_KEYS];
   const int lane = threadIdx.x & 63;
   // wave-uniform (scalar) so that the key loop is a uniform loop: a divergent
   // one merges its exit paths and waits for every load at the loop head
@@ -913,7 +917,13 @@ bool prefill_fits(const SeqView& sv) {
 
 }  // namespace
 
-bool score_selects(const SeqView& sv) { return sv.max_q_len > 1 && prefill_fits(sv); }
+// Batches of at most PF_MIN_Q - 1 tokens per sequence (decode, multi-token
+// decode rows of speculative verification) take the streaming kernel and the
+// separate Top-K: the prefill kernel gives each sequence one workgroup per 8
+// tokens, so a batch of short rows leaves most CUs idle (64 requests x 2
+// tokens at 32768 positions: 617 us in the prefill kernel).
+constexpr int PF_MIN_Q = 9;
+bool score_selects(const SeqView& sv) { return sv.max_q_len >= PF_MIN_Q && prefill_fits(sv); }
 
 namespace {
 
@@ -921,7 +931,7 @@ template <int MT, int KS, bool FP8>
 hipError_t launch_mt(const ScoreParams& p, hipStream_t stream, const TimerEvents& t) {
   const SeqView& sv = p.sv;
   const bool decode = sv.max_q_len == 1;
-  if (!decode && prefill_fits(sv)) {
+  if (score_selects(sv)) {
     dim3 grid(cdiv(sv.max_q_len, PF_TOKS), sv.num_seqs);
     return launch_kernel(score_prefill_kernel<MT, KS, FP8>, grid, dim3(PF_TOKS * WAVE), stream, t.start, t.stop, p);
   }
@@ -930,7 +940,7 @@ hipError_t launch_mt(const ScoreParams& p, hipStream_t stream, const TimerEvents
     dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs);
     return launch_kernel(score_kernel<MT, KS, FP8, true>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
   }
-  const int kpw = 256;
+  const int kpw = MT_KPW;
   dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs * cdiv(sv.max_q_len, SCORE_WAVES));
   return launch_kernel(score_kernel<MT, KS, FP8, false>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
 }
@@ -961,7 +971,7 @@ hipError_t launch_score(const ScoreParams& p, int k_format, hipStream_t stream) 
   // the decode kernel accumulates the row histograms with atomics: clear
   // them first (a kernel, not a memset, so the call stays safe to capture in
   // a graph); the prefill kernel keeps its histograms in LDS
-  if (k_format == 2 || p.sv.max_q_len == 1 || !prefill_fits(p.sv)) {
+  if (k_format == 2 || !score_selects(p.sv)) {
     const int64_t n4 = (int64_t)p.sv.num_tokens * SCORE_HIST_BINS / 4;
     const int64_t zblocks = std::min<int64_t>((n4 + 255) / 256, 2048);
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream, p.hist, n4);
