@@ -332,6 +332,34 @@ def measure_mxfp8(steps, warmup):
                           "score_median_us": us, "algorithmic_bytes": nbytes, "achieved_GBs": nbytes / us / 1e3,
                           "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "score_topk_call_us": call_us}),
               flush=True)
+    # a prefill chunk: the last 4096 positions of the first sequence as query
+    # tokens (MXFP8 keys: every token streams its causal range; bf16 keys: the
+    # prefill kernel, key tiles shared by 8 tokens)
+    Q = 4096
+    ctx0 = int(call.ctx_len[0])
+    ctx1 = torch.tensor([ctx0], dtype=torch.int32, device=dev)
+    cu = torch.tensor([0, Q], dtype=torch.int32, device=dev)
+    pseqs = lib.Seqs(ctx1, cu, max_q_len=Q, max_ctx_len=ctx0, num_tokens=Q, seq_stride=inp.seq_stride)
+    pq = torch.randint(-wl.q_range, wl.q_range + 1, (Q, wl.H_I, wl.d_I), generator=g, device=dev).to(torch.bfloat16)
+    pw = torch.pow(2.0, -torch.randint(0, 4, (Q, wl.H_I), generator=g, device=dev).float())
+    pidx = torch.empty((Q, wl.top_k), dtype=torch.int32, device=dev)
+    pws = torch.empty(lib.idx_score_topk_workspace(pseqs, wl.H_I, wl.d_I, wl.top_k), dtype=torch.uint8, device=dev)
+    pairs = float(sum(ctx0 - Q + i + 1 for i in range(Q)))
+    for label, keys, exps in (("MXFP8 keys", codes_mx, exps_mx), ("bf16 keys", inp.k_idx, None)):
+        def prun():
+            lib.idx_score_topk(pseqs, pq, keys, pw, wl.top_k, k_scale=exps, out_idx=pidx, ws=pws)
+        prun()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(3):
+            prun()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 3
+        flops = 2.0 * wl.H_I * wl.d_I * pairs
+        print(json.dumps({"kernel": "prefill chunk scores + Top-K, " + label, "tokens": Q, "ctx": ctx0,
+                          "causal_pairs": pairs, "call_ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}), flush=True)
 
 
 def measure_multi_token(steps, warmup):
