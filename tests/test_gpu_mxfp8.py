@@ -41,7 +41,7 @@ def _q_oracle(q):
     return out
 
 
-def _run(ctx, H_I, K, seed, paged=False, qlen=None):
+def _run(ctx, H_I, K, seed, paged=False, qlen=None, k_range=8):
     """One idx_score_topk call over sequences with context lengths ctx and
     qlen[b] query tokens each (the last qlen[b] positions; default 1: a
     decode batch), checked token by token against the oracle."""
@@ -59,9 +59,9 @@ def _run(ctx, H_I, K, seed, paged=False, qlen=None):
         for b in range(B):
             bt[b, :npg[b]] = perm[o:o + npg[b]]
             o += npg[b]
-        keys, exps = gen.mxfp8_keys(g, sum(npg) * page, "cuda")
+        keys, exps = gen.mxfp8_keys(g, sum(npg) * page, "cuda", k_range=k_range)
     else:
-        keys, exps = gen.mxfp8_keys(g, B * stride, "cuda")
+        keys, exps = gen.mxfp8_keys(g, B * stride, "cuda", k_range=k_range)
     qi = torch.randint(-4, 5, (T, H_I, 128), generator=g, device="cuda").float()
     shift = torch.randint(0, 2, (T, H_I, 4), generator=g, device="cuda").float()
     q_idx = (qi * torch.pow(2.0, shift).repeat_interleave(32, dim=2)).to(torch.bfloat16)
@@ -137,3 +137,20 @@ def test_mxfp8_prefill_chunks_contiguous():
 
 def test_mxfp8_prefill_chunks_paged_fewer_heads():
     _run([5000, 130], 24, 512, 74, paged=True, qlen=[70, 130])
+
+
+def test_mxfp8_largest_top_k_one_head_tile():
+    # K = 2048 (the largest), 16 heads (one MFMA row tile); rows with
+    # t + 1 = K, t + 1 = K + 1 and a single position
+    _run([3000, 2048, 2049, 1], 16, 2048, 75)
+
+
+def test_mxfp8_top_1_short_multi_token_rows():
+    # K = 1; 3 and 5 query tokens (the second sequence's chunk is its whole
+    # context), 8 heads
+    _run([700, 5], 8, 1, 76, qlen=[3, 5])
+
+
+def test_mxfp8_all_equal_scores_take_lowest_positions():
+    # every code 0: all scores are 0, so each row takes its lowest positions
+    _run([4000, 300, 2100], 64, 256, 77, k_range=0, qlen=[1, 2, 1])
