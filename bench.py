@@ -535,6 +535,21 @@ def main():
     kern_ms = {names[k]: sum(a.elapsed_time(b) for a, b in pairs) / KB for k, pairs in ev.items()}
     score_ms = sum(a.elapsed_time(b) for a, b in score_ev) / K
 
+    # reference: a plain 1 GiB device-to-device copy on the same GPU, after the
+    # timed region (read + write bytes per second)
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ca.record()
+    for _ in range(5):
+        cdst.copy_(csrc)
+    cb.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * (1 << 30) * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
+    del csrc, cdst
+
     u = algorithmic_units(wl, int(call.ctx_len[0]), T)
     score_us = score_ms * 1e3
     achieved = u["score_bytes"] / (score_ms * 1e-3) / 1e9
@@ -569,6 +584,8 @@ def main():
             "score_mfma_frac": u["score_flops"] / (score_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "step_hbm_gbs": (u["score_bytes"] + u["topk_bytes"] + u["attn_bytes"]) / (ms_per_step * 1e-3) / 1e9,
             "wall_s_timed_region": wall,
+            "copy_kernel_gbs": copy_gbs,
+            "score_frac_of_copy": achieved / copy_gbs,
         },
         "cpu_baseline": None,
     }
