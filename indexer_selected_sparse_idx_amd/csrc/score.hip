@@ -40,9 +40,13 @@ constexpr int NT = 2;            // key tiles (16 keys each) per pipeline stage
 // that prologue small against the key stream
 template <bool FP8>
 constexpr int decode_kpw() { return FP8 ? 2048 : 1024; }
-// keys per workgroup of the multi-token kernel (every wave takes them all,
-// for its own token)
+// keys per workgroup of the multi-token kernel
 constexpr int MT_KPW = 1024;
+// query tokens per workgroup of the multi-token kernel: 4 (one per wave,
+// every wave over all the workgroup's keys), or 2 when no sequence has more
+// than 2 query tokens (waves w and w + 2 take token w over the two halves of
+// the keys, so no wave idles)
+__host__ __device__ __forceinline__ int mt_tokens_per_wg(int max_q_len) { return max_q_len <= 2 ? 2 : 4; }
 
 // max(x, 0) as one integer max on the bit pattern: negative floats (-0
 // included) are negative integers (fmaxf costs a second instruction that
@@ -105,15 +109,17 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_
     key_lo = wg_lo + wave * per_wave;
     key_hi = min(t, key_lo + per_wave - 1);
   } else {
-    const int nqb = cdiv(sv.max_q_len, SCORE_WAVES);
+    const int tpw = mt_tokens_per_wg(sv.max_q_len);
+    const int nqb = cdiv(sv.max_q_len, tpw);
     b = blockIdx.y / nqb;
-    const int i = (blockIdx.y % nqb) * SCORE_WAVES + wave;
+    const int i = (blockIdx.y % nqb) * tpw + wave % tpw;
     const int ql = q_len(sv, b);
     active = i < ql;
     tok = first_token(sv, b) + (active ? i : 0);
     t = sv.ctx_len[b] - ql + i;
-    key_lo = wg_lo;
-    key_hi = min(t, key_lo + keys_per_wg - 1);
+    const int span = keys_per_wg / (SCORE_WAVES / tpw);
+    key_lo = wg_lo + (wave / tpw) * span;
+    key_hi = min(t, key_lo + span - 1);
   }
   active = active && key_lo <= key_hi;
   // block table entries of the pages that hold keys wg_lo .. min(ctx_len, wg_lo + keys_per_wg) - 1
@@ -240,18 +246,20 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p, int keys_per_
 }
 
 // ---------------------------------------------------------------------------
-// Decode indexer over MXFP8 keys (d_I = 128): the index quantised in blocks
-// of 32 values sharing a power-of-two scale ("Hierarchical Quantization",
-// index-cache bullet, in Day 0 Inference Support for New LLM Architectures;
-// section 4 of Day 0 Inference Adaptation and Performance Optimization for
-// New Models).  A key row is 128 E4M3FN codes and 4 E8M0 bytes (132 bytes,
-// read with dword loads: rows are 4-byte aligned).  The query is quantised
-// on the fly, per head and block of 32, with the same rule as the keys'
-// writer: shared exponent floor(log2(amax)) - 8, codes E4M3(clamp(q / 2^e,
+// Indexer over MXFP8 keys (d_I = 128), any batch: the index quantised in
+// blocks of 32 values sharing a power-of-two scale ("Hierarchical
+// Quantization", index-cache bullet, in Day 0 Inference Support for New LLM
+// Architectures; section 4 of Day 0 Inference Adaptation and Performance
+// Optimization for New Models).  A key is a row of 128 E4M3FN codes and 4
+// E8M0 bytes in a separate [rows, 4] array.  The query is quantised
+// on the fly, per head and block of 32, by the OCP MX rule for E4M3
+// elements: shared exponent floor(log2(amax)) - 8, codes E4M3(clamp(q / 2^e,
 // +-448)).  One v_mfma_scale_f32_16x16x128_f8f6f4 covers 16 heads x 16 keys
-// x all 128 dims: lane (c, g) holds head / key c of its tile and dims
-// 32 g .. 32 g + 31 - one MX block - with that block's E8M0 byte as its scale
-// operand.  The rest (pipeline, epilogue, histogram) is the decode kernel's.
+// x all 128 dims: lane (c, g) holds head / key c of its tile, dims
+// 16 g .. 16 g + 15 and 64 + 16 g .. 64 + 16 g + 15, and, as its scale
+// operand, the E8M0 byte of block g of that head / key (the instruction
+// takes block s of row c from lane c + 16 s).  The rest (pipeline,
+// epilogue, histogram) is the decode kernel's.
 // ---------------------------------------------------------------------------
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -942,7 +950,7 @@ hipError_t launch_mt(const ScoreParams& p, hipStream_t stream, const TimerEvents
     return launch_kernel(score_kernel<MT, KS, FP8, true>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
   }
   const int kpw = MT_KPW;
-  dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs * cdiv(sv.max_q_len, SCORE_WAVES));
+  dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs * cdiv(sv.max_q_len, mt_tokens_per_wg(sv.max_q_len)));
   return launch_kernel(score_kernel<MT, KS, FP8, false>, grid, dim3(256), stream, t.start, t.stop, p, kpw);
 }
 

@@ -296,3 +296,13 @@ def test_deterministic():
         torch.cuda.synchronize()
         for x, y in zip(a, b):
             assert torch.equal(x, y)
+
+
+def test_two_token_rows_split_keys():
+    # at most 2 query tokens per sequence: the multi-token kernel gives each
+    # token two waves, over the two halves of a workgroup's keys
+    ctx = [5000, 2100, 65, 2, 9000]
+    q_len = [2, 2, 1, 2, 2]
+    wl = Workload("two-token rows", ctx, [{"seqs": list(range(5)), "q_len": q_len}], top_k=2048, H=16,
+                  seed=34)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "two-token")
