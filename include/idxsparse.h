@@ -18,6 +18,11 @@
  *   pointers; `idx_seqs` itself is a host struct.  The caller owns all
  *   memory.  The library never allocates, never synchronises the device and
  *   keeps no state between calls (the measurement hook at the end excepted).
+ * - Thread safety: every entry point is re-entrant and may be called from
+ *   several host threads at once (on the same or different streams; calls
+ *   that share output or workspace memory race on it, like any two kernels).
+ *   A call that no armed timer measures reads one atomic word of the
+ *   library and writes none.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
  *   A call returns after enqueueing; results are ready when the stream is.
  * - Return value: IDX_OK, or a negative idx_status from host-side argument
@@ -262,7 +267,9 @@ const char *idx_status_string(int status);
  * stream it is launched on, and then disarms.  The dispatches record the
  * events themselves (hipExtLaunchKernelGGL), so an armed launch runs back to
  * back with its neighbours like an unarmed one.  One arm per kernel at a
- * time; not thread-safe (a measurement aid, not part of the compute path).
+ * time.  Arming, and the launch it measures, are not thread-safe against
+ * other arming or measured launches of the same kernel (a measurement aid,
+ * not part of the compute path); unmeasured calls are unaffected.
  * Returns IDX_OK or IDX_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------ */
 typedef enum {

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "idxsparse.h"
 #include "kernels.h"
@@ -13,11 +14,17 @@ namespace idxs {
 
 namespace {
 
+// Measurement hook state.  g_armed has bit k set while kernel k holds an
+// armed event pair in g_timers[k]; an unarmed launch only loads g_armed (an
+// atomic), so calls that nobody measures share no mutable state and may run
+// from several host threads at once.  Arming and the launch it measures are
+// a single-threaded measurement aid.
 struct Timer {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
 Timer g_timers[IDX_KERNEL_COUNT];
+std::atomic<uint32_t> g_armed{0};
 
 constexpr size_t WS_ALIGN = 256;
 size_t align_up(size_t v) { return (v + WS_ALIGN - 1) & ~(WS_ALIGN - 1); }
@@ -204,9 +211,12 @@ int run_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, int kv_
 
 TimerEvents timer_take(int kernel) {
   TimerEvents e;
+  const uint32_t bit = 1u << kernel;
+  if ((g_armed.load(std::memory_order_acquire) & bit) == 0) return e;  // the common case: nothing armed
   e.start = g_timers[kernel].start;
   e.stop = g_timers[kernel].stop;
   g_timers[kernel] = Timer{};
+  g_armed.fetch_and(~bit, std::memory_order_acq_rel);
   return e;
 }
 
@@ -342,6 +352,7 @@ int idx_timer_arm(int kernel, void* start_event, void* stop_event) {
   if (kernel < 0 || kernel >= IDX_KERNEL_COUNT || !start_event || !stop_event) return IDX_ERR_INVALID_ARG;
   g_timers[kernel].start = static_cast<hipEvent_t>(start_event);
   g_timers[kernel].stop = static_cast<hipEvent_t>(stop_event);
+  g_armed.fetch_or(1u << kernel, std::memory_order_release);
   return IDX_OK;
 }
 

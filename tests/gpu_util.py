@@ -82,31 +82,71 @@ def token_positions(call):
     return pos
 
 
+DECODED_CACHE_LIMIT = 1 << 30   # bytes of float64 kept decoded on the host per cache
+MIRROR_LIMIT = 16 << 30         # raw bytes of a cache copied whole to the host
+
+
+class _DeviceRows:
+    """Rows of a device cache fetched on demand (caches too large to mirror)."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, rows):
+        r = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.int64)).to(self.t.device)
+        return host_raw(self.t.index_select(0, r))
+
+
+def _mirror(t):
+    return host_raw(t) if t.numel() * t.element_size() <= MIRROR_LIMIT else _DeviceRows(t)
+
+
+def host_caches(inp):
+    """Host copies of the index-key cache, its per-row scales and the latent
+    cache (raw stored bytes), made once per generated workload; caches whose
+    float64 form fits DECODED_CACHE_LIMIT are also kept decoded."""
+    m = inp.extra.get("host")
+    if m is None:
+        m = {"k": _mirror(inp.k_idx), "kv": _mirror(inp.kv),
+             "ks": None if inp.k_scale is None else inp.k_scale.cpu().numpy(), "kf": None, "kvf": None}
+        if inp.k_idx.numel() * 8 <= DECODED_CACHE_LIMIT:
+            m["kf"] = oracle.bf16_bits_to_f64(m["k"]) if kdt(inp) == "bf16" else oracle.e4m3_bytes_to_f64(m["k"])
+        if kvdt(inp) == "bf16" and inp.kv.numel() * 8 <= DECODED_CACHE_LIMIT:
+            m["kvf"] = oracle.bf16_bits_to_f64(m["kv"])
+        inp.extra["host"] = m
+    return m
+
+
 def oracle_rows(inp, call, tokens):
-    """Oracle indices + attention for selected tokens of a call, gathering only
-    the cache rows each token needs (device index_select -> host copy)."""
+    """Oracle indices + attention for selected tokens of a call, read from
+    host copies of the caches (the stored bytes) and of each token's
+    queries."""
     osq = oracle_seqs(inp, call)
     pos = token_positions(call)
     K = inp.wl.top_k
+    hc = host_caches(inp)
     idx = np.empty((len(tokens), K), np.int32)
     outs, lses = [], []
     for r, tok in enumerate(tokens):
         b, t = pos[tok]
         g = call.tok_lo + tok
         phys = osq.physical_rows(b, np.arange(t + 1))
-        keys_raw = host_raw(inp.k_idx.index_select(0, torch.from_numpy(phys).to(inp.k_idx.device)))
-        keys = oracle.bf16_bits_to_f64(keys_raw) if kdt(inp) == "bf16" else oracle.e4m3_bytes_to_f64(keys_raw)
-        ks = None
-        if inp.k_scale is not None:
-            ks = inp.k_scale.index_select(0, torch.from_numpy(phys).to(inp.k_scale.device)).cpu().numpy()
+        if hc["kf"] is not None:
+            keys = hc["kf"][phys]
+        else:
+            keys_raw = hc["k"][phys]
+            keys = oracle.bf16_bits_to_f64(keys_raw) if kdt(inp) == "bf16" else oracle.e4m3_bytes_to_f64(keys_raw)
+        ks = None if hc["ks"] is None else hc["ks"][phys]
         qi = oracle.bf16_bits_to_f64(bits16(inp.q_idx[g]))
         w = inp.head_w[g].cpu().numpy().astype(np.float64)
         s = oracle.indexer_scores(qi, keys, w, ks)
         idx[r] = oracle.topk_select(s, K)
         sel = idx[r][idx[r] >= 0].astype(np.int64)
         rphys = osq.physical_rows(b, sel)
-        rows_raw = host_raw(inp.kv.index_select(0, torch.from_numpy(rphys).to(inp.kv.device)))
-        rows = R.decode_rows(rows_raw, "bf16" if kvdt(inp) == "bf16" else "fp8_656", np.arange(len(sel)))
+        if hc["kvf"] is not None:
+            rows = hc["kvf"][rphys]
+        else:
+            rows = R.decode_rows(hc["kv"][rphys], "bf16" if kvdt(inp) == "bf16" else "fp8_656", np.arange(len(sel)))
         o, l = oracle.sparse_attention(oracle.bf16_bits_to_f64(bits16(inp.q[g])), rows, SCALE)
         outs.append(o)
         lses.append(l)

@@ -2,18 +2,22 @@
 bench uses (the fused entry points over whole batches).
 
 The oracle recomputes, on the host, every row it can afford and a seeded
-sample of rows elsewhere: all rows of the tiny prefill (L = 2048) and of the
-64-request decode batch; sampled rows (first, last and random) of every
-long-prefill chunk checked; sampled requests of the FP8 decode batch; and
-sampled prefill and decode tokens of the mixed paged batch.  Indices are
-compared bit for bit as sets, attention within tol * RMS of the oracle's
-output over the compared rows.
+sample of rows elsewhere:
+- tiny prefill (L = 2048): every row;
+- decode batch (64 x 32768): every row;
+- long prefill (65,536 positions in 16 chunks of 4096): 64 rows of every
+  chunk (its first and last rows and 62 seeded ones), and every row of the
+  first chunk with t < K (the rows whose selection is the whole history);
+- FP8 decode (128 x 131072): every row;
+- mixed paged batch: every decode row, and every prefill sequence's first
+  and last token plus seeded tokens.
+Indices are compared bit for bit as sets, attention within tol * RMS of the
+oracle's output over the compared rows.
 """
 import numpy as np
 import pytest
 import torch
 
-import workloads
 from workloads import config, generate
 
 import gpu_util as U
@@ -40,8 +44,13 @@ def _check_rows(inp, call, out, lse, idx, tokens, tol, label):
 
 
 def _sample(n, k, rng):
+    """k distinct rows of n: the first, the last and k - 2 seeded others."""
     pick = {0, n - 1}
-    pick.update(int(x) for x in rng.choice(n, size=min(k, n), replace=False))
+    rest = [int(x) for x in rng.permutation(np.arange(1, n - 1))]
+    for x in rest:
+        if len(pick) >= min(k, n):
+            break
+        pick.add(x)
     return sorted(pick)
 
 
@@ -61,40 +70,90 @@ def test_full_decode_batch_all_rows():
     _check_rows(inp, call, out, lse, idx, list(range(call.num_tokens)), U.TOL_BF16, "decode-batch 64x32768")
 
 
-def test_full_long_prefill_sampled_rows():
+# ---- long prefill: one generated workload for its tests ---------------------
+
+@pytest.fixture(scope="module")
+def long_prefill():
     inp = generate(config(3), "cuda")
-    rng = np.random.default_rng(33)
-    for ci, call in enumerate(inp.calls):
+    yield inp
+    inp.extra.clear()
+
+
+def _long_prefill_chunks(inp, chunks):
+    for ci in chunks:
+        call = inp.calls[ci]
         U.log("long-prefill chunk %d: ctx %d" % (ci, int(call.ctx_len[0])))
         out, lse, idx = U.run_fused(inp, call)
         torch.cuda.synchronize()
-        if ci in (0, 1, 7, 15):
-            _check_rows(inp, call, out, lse, idx, _sample(call.num_tokens, 6, rng), U.TOL_BF16,
-                        "long-prefill chunk %d" % ci)
+        rng = np.random.default_rng(3300 + ci)
+        _check_rows(inp, call, out, lse, idx, _sample(call.num_tokens, 64, rng), U.TOL_BF16,
+                    "long-prefill chunk %d" % ci)
         del out, lse, idx
 
 
-def test_full_fp8_decode_sampled_requests():
+def test_full_long_prefill_chunk0_rows_below_k(long_prefill):
+    inp = long_prefill
+    call = inp.calls[0]
+    K = inp.wl.top_k
+    out, lse, idx = U.run_fused(inp, call)
+    torch.cuda.synchronize()
+    _check_rows(inp, call, out, lse, idx, list(range(K)), U.TOL_BF16, "long-prefill chunk 0, rows t < K")
+
+
+def test_full_long_prefill_chunks_0_to_3(long_prefill):
+    _long_prefill_chunks(long_prefill, range(0, 4))
+
+
+def test_full_long_prefill_chunks_4_to_7(long_prefill):
+    _long_prefill_chunks(long_prefill, range(4, 8))
+
+
+def test_full_long_prefill_chunks_8_to_11(long_prefill):
+    _long_prefill_chunks(long_prefill, range(8, 12))
+
+
+def test_full_long_prefill_chunks_12_to_15(long_prefill):
+    _long_prefill_chunks(long_prefill, range(12, 16))
+
+
+# ---- FP8 decode: every request ---------------------------------------------------
+
+@pytest.fixture(scope="module")
+def fp8_decode():
     inp = generate(config(4), "cuda")
     call = inp.calls[0]
     out, lse, idx = U.run_fused(inp, call)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(44)
-    _check_rows(inp, call, out, lse, idx, _sample(call.num_tokens, 10, rng), U.TOL_FP8, "fp8-decode 128x131072")
+    yield inp, call, out, lse, idx
+    inp.extra.clear()
 
 
-def test_full_mixed_paged_sampled_rows():
+def test_full_fp8_decode_requests_0_to_63(fp8_decode):
+    inp, call, out, lse, idx = fp8_decode
+    _check_rows(inp, call, out, lse, idx, list(range(0, 64)), U.TOL_FP8, "fp8-decode 128x131072, requests 0-63")
+
+
+def test_full_fp8_decode_requests_64_to_127(fp8_decode):
+    inp, call, out, lse, idx = fp8_decode
+    _check_rows(inp, call, out, lse, idx, list(range(64, 128)), U.TOL_FP8,
+                "fp8-decode 128x131072, requests 64-127")
+
+
+# ---- mixed paged batch ---------------------------------------------------------
+
+def test_full_mixed_paged_rows():
     inp = generate(config(5), "cuda")
     rng = np.random.default_rng(55)
     for ci, call in enumerate(inp.calls):
         out, lse, idx = U.run_fused(inp, call)
         torch.cuda.synchronize()
         if call.is_decode:
-            toks = _sample(call.num_tokens, 16, rng)
+            toks = list(range(call.num_tokens))
         else:
-            # every prefill request's first and last token, plus random tokens
+            # every prefill request's first and last token, plus seeded tokens
             toks = sorted(set(int(x) for x in call.cu_q[:-1]) | set(int(x) - 1 for x in call.cu_q[1:])
-                          | set(_sample(call.num_tokens, 8, rng)))
+                          | set(_sample(call.num_tokens, 64, rng)))
         _check_rows(inp, call, out, lse, idx, toks, U.TOL_BF16,
                     "mixed-paged %s call" % ("decode" if call.is_decode else "prefill"))
         del out, lse, idx
+    inp.extra.clear()

@@ -41,10 +41,29 @@ def _q_oracle(q):
     return out
 
 
-def _run(ctx, H_I, K, seed, paged=False, qlen=None, k_range=8):
+def _block_ranged_queries(g, T, H_I):
+    """Integer queries whose range differs per head and block of 32 (63,
+    20, 7 or 2): the blocks' shared exponents differ, most values fall
+    between E4M3 codes after the division by 2^e (q / 2^e = 8 q, 16 q, ...)
+    and round, and blocks whose largest |q| / 2^e exceeds 448 saturate."""
+    ranges = torch.tensor([63.0, 20.0, 7.0, 2.0], device="cuda")
+    r = ranges[torch.randint(0, 4, (T, H_I, 4), generator=g, device="cuda")].repeat_interleave(32, dim=2)
+    u = torch.rand((T, H_I, 128), generator=g, device="cuda")
+    return torch.floor(u * (2.0 * r + 1.0)) - r
+
+
+def _run(ctx, H_I, K, seed, paged=False, qlen=None, k_range=8, rounding=False):
     """One idx_score_topk call over sequences with context lengths ctx and
     qlen[b] query tokens each (the last qlen[b] positions; default 1: a
-    decode batch), checked token by token against the oracle."""
+    decode batch), checked token by token against the oracle.
+
+    rounding=False: queries are integers in [-4, 4] times a power of two per
+    head and block (exactly representable after MX quantisation).
+    rounding=True: block-ranged integer queries (see _block_ranged_queries)
+    that the MX rule must round and saturate, with head weights in {1/2, 1};
+    callers keep k_range and H_I small enough that every fp32 partial sum
+    stays exact (quantised queries are integers of at most 63, keys
+    multiples of 1/2 of at most 2 k_range)."""
     B = len(ctx)
     qlen = [1] * B if qlen is None else list(qlen)
     T = sum(qlen)
@@ -62,10 +81,14 @@ def _run(ctx, H_I, K, seed, paged=False, qlen=None, k_range=8):
         keys, exps = gen.mxfp8_keys(g, sum(npg) * page, "cuda", k_range=k_range)
     else:
         keys, exps = gen.mxfp8_keys(g, B * stride, "cuda", k_range=k_range)
-    qi = torch.randint(-4, 5, (T, H_I, 128), generator=g, device="cuda").float()
-    shift = torch.randint(0, 2, (T, H_I, 4), generator=g, device="cuda").float()
-    q_idx = (qi * torch.pow(2.0, shift).repeat_interleave(32, dim=2)).to(torch.bfloat16)
-    head_w = torch.pow(2.0, -torch.randint(0, 4, (T, H_I), generator=g, device="cuda").float())
+    if rounding:
+        q_idx = _block_ranged_queries(g, T, H_I).to(torch.bfloat16)
+        head_w = torch.pow(2.0, -torch.randint(0, 2, (T, H_I), generator=g, device="cuda").float())
+    else:
+        qi = torch.randint(-4, 5, (T, H_I, 128), generator=g, device="cuda").float()
+        shift = torch.randint(0, 2, (T, H_I, 4), generator=g, device="cuda").float()
+        q_idx = (qi * torch.pow(2.0, shift).repeat_interleave(32, dim=2)).to(torch.bfloat16)
+        head_w = torch.pow(2.0, -torch.randint(0, 4, (T, H_I), generator=g, device="cuda").float())
     ctx_t = torch.tensor(ctx, dtype=torch.int32, device="cuda")
     cu_h = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
     cu = None if max(qlen) == 1 else torch.from_numpy(cu_h).to("cuda")
@@ -90,6 +113,19 @@ def _run(ctx, H_I, K, seed, paged=False, qlen=None, k_range=8):
             sc = oracle.indexer_scores(_q_oracle(qf[tok]), kf[rows[:t + 1]], w[tok])
             want.append(oracle.topk_select(sc, K))
     U.check_indices(idx.cpu().numpy(), np.stack(want), "mxfp8")
+    if rounding:
+        # the case is what it claims: the quantiser rounds and saturates
+        rounded = saturated = 0
+        for tok in range(T):
+            qh = _q_oracle(qf[tok])
+            rounded += int(np.sum(qh != qf[tok]))
+            blocks = np.abs(qf[tok]).reshape(H_I, 4, 32)
+            amax = blocks.max(axis=2, keepdims=True)
+            e = np.frexp(np.where(amax > 0, amax, 1.0))[1] - 9     # floor(log2 amax) - 8
+            saturated += int(np.sum(blocks / 2.0 ** e > 448.0))
+        U.log("mxfp8 rounding case: %d query values rounded, %d saturated (of %d)"
+              % (rounded, saturated, qf.size))
+        assert rounded > qf.size // 10 and saturated > 0
     return exps
 
 
@@ -154,3 +190,17 @@ def test_mxfp8_top_1_short_multi_token_rows():
 def test_mxfp8_all_equal_scores_take_lowest_positions():
     # every code 0: all scores are 0, so each row takes its lowest positions
     _run([4000, 300, 2100], 64, 256, 77, k_range=0, qlen=[1, 2, 1])
+
+
+def test_mxfp8_query_rounding_and_saturation_64_heads():
+    # queries that round (values between E4M3 codes after the division by
+    # the block's power of two) and saturate (|q| / 2^e in (448, 512)),
+    # keys in [-2, 2] per block exponent, 64 heads: every partial sum is a
+    # multiple of 1/4 below 2^21, so the scores are exact in fp32
+    _run([5000, 7777, 130, 2049], 64, 512, 78, k_range=1, rounding=True)
+
+
+def test_mxfp8_query_rounding_and_saturation_prefill_paged():
+    # the same query rule through a paged prefill call, 16 heads (one MFMA
+    # row tile), keys in [-4, 4] per block exponent
+    _run([3000, 900], 16, 256, 79, paged=True, qlen=[40, 9], k_range=2, rounding=True)

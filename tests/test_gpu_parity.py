@@ -109,7 +109,8 @@ def test_prefill_e4m3_keys_small_pages_and_scales():
     _parity_all(generate(wl, "cuda"), U.TOL_FP8, "prefill e4m3 paged")
 
 
-def test_all_equal_scores_take_lowest_positions():
+def test_multi_token_all_equal_scores_take_lowest_positions():
+    # 5 query tokens: the multi-token score kernel and the decode-style Top-K
     wl = Workload("zeros", [3000], [{"seqs": [0], "q_len": [5]}], top_k=256, seed=25)
     inp = generate(wl, "cuda")
     inp.q_idx.zero_()                                          # every score is exactly 0
@@ -117,6 +118,71 @@ def test_all_equal_scores_take_lowest_positions():
     out, lse, idx = U.run_fused(inp, call)
     got = np.sort(idx.cpu().numpy(), axis=1)
     assert np.array_equal(got, np.tile(np.arange(256, dtype=np.int32), (5, 1)))
+
+
+def test_prefill_all_equal_scores_overflow_the_wave_list():
+    # 16 query tokens (the prefill kernel, which selects on its own) over
+    # about 5000 equal scores: the threshold key's 22-bit prefix holds every
+    # key of a row, more than the 2048-word LDS list of a wave (d_I = 128),
+    # so the selection takes its two-pass form over the compacted pairs
+    wl = Workload("zeros prefill", [5000], [{"seqs": [0], "q_len": [16]}], top_k=256, H=16, seed=35)
+    inp = generate(wl, "cuda")
+    inp.q_idx.zero_()
+    call = inp.calls[0]
+    out, lse, idx = U.run_fused(inp, call)
+    got = np.sort(idx.cpu().numpy(), axis=1)
+    assert np.array_equal(got, np.tile(np.arange(256, dtype=np.int32), (16, 1)))
+    w_idx, w_out, w_lse = U.oracle_rows(inp, call, list(range(16)))
+    U.check_indices(idx.cpu().numpy(), w_idx, "zeros prefill")
+    U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), w_out, w_lse, U.TOL_BF16, "zeros prefill")
+
+
+def _three_level_keys(inp, b, n, n_top, n_mid, rng):
+    """Index keys of sequence b that give scores of three values only: every
+    head's query is the unit vector on dimension 0 and every head weight is
+    1, so S = H_I * ReLU(k[0]); k[0] is 2 on n_top positions, 1 on n_mid and
+    0 elsewhere (the other dimensions do not count)."""
+    k0 = np.zeros(n, np.float32)
+    perm = rng.permutation(n)
+    k0[perm[:n_top]] = 2.0
+    k0[perm[n_top:n_top + n_mid]] = 1.0
+    rows = torch.arange(b * inp.seq_stride, b * inp.seq_stride + n, device="cuda")
+    inp.k_idx[rows, 0] = torch.from_numpy(k0).to("cuda").to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("d_I", [128, 64])
+def test_prefill_threshold_ties_overflow_the_wave_list(d_I):
+    # prefill kernel (20 query tokens); scores take three values, the K-th
+    # largest is the middle one and about 3000 keys share it: more than the
+    # wave's LDS list (2048 words at d_I = 128, 1024 at d_I = 64), so the
+    # selection's two-pass form picks the 150 keys above the threshold and
+    # the lowest positions among the ties
+    n = 9000
+    wl = Workload("ties prefill", [n], [{"seqs": [0], "q_len": [20]}], top_k=512, H=16, d_I=d_I, seed=36)
+    inp = generate(wl, "cuda")
+    inp.q_idx.zero_()
+    inp.q_idx[:, :, 0] = 1.0
+    inp.head_w.fill_(1.0)
+    _three_level_keys(inp, 0, n, 150, 3000, np.random.default_rng(36))
+    _parity_all(inp, U.TOL_BF16, "ties prefill d_I=%d" % d_I)
+
+
+def test_prefill_block_table_beyond_the_staged_pages():
+    # pages of 1 position: 5000 pages for the longest sequence, more than the
+    # 4096 block-table entries the prefill kernel stages, so the call takes
+    # the multi-token score kernel and the decode-style Top-K
+    wl = Workload("pages > 4096", [5000, 300], [{"seqs": [0, 1], "q_len": [12, 40]}], top_k=256, H=32,
+                  paged=True, page_size=1, seed=37)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "pages > 4096")
+
+
+def test_prefill_rows_longer_than_the_packed_positions():
+    # rows of more than 2^22 positions: the prefill selection cannot pack a
+    # position beside the key's low bits in its LDS list and takes the
+    # two-pass form over the compacted pairs
+    n = (1 << 22) + 3000
+    wl = Workload("rows > 2^22", [n], [{"seqs": [0], "q_len": [10]}], top_k=256, H_I=4, d_I=64, H=8, seed=38)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "rows > 2^22")
 
 
 def test_decode_all_equal_scores_whole_row_select():
@@ -180,11 +246,20 @@ def test_decode_wide_threshold_bucket():
     U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), w_out, w_lse, U.TOL_BF16, "wide bucket")
 
 
-def test_prefill_rows_longer_than_the_compacted_path():
-    # rows of more than 64 x 2048 keys: the prefill selection reads the whole
-    # row in every pass (the form for rows of any length)
+def test_multi_token_rows_of_140000_positions():
+    # 3 query tokens per sequence (the multi-token score kernel and the
+    # decode-style Top-K) over rows of 140,000 positions: 69 compaction
+    # chunks per row
     wl = Workload("long rows", [140000], [{"seqs": [0], "q_len": [3]}], top_k=256, H_I=4, d_I=64, H=8, seed=31)
     _parity_all(generate(wl, "cuda"), U.TOL_BF16, "long rows")
+
+
+def test_prefill_rows_of_140000_positions():
+    # the same rows through the prefill kernel (10 query tokens): candidate
+    # lists of rows of 140,000 keys
+    wl = Workload("long rows prefill", [140000], [{"seqs": [0], "q_len": [10]}], top_k=256, H_I=4, d_I=64, H=8,
+                  seed=39)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "long rows prefill")
 
 
 def test_separate_entry_points_match_fused():
