@@ -64,7 +64,9 @@ typedef enum {
   IDX_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or bound  */
   IDX_ERR_UNSUPPORTED = -2,   /* well-formed but outside the supported set    */
   IDX_ERR_WORKSPACE = -3,     /* workspace NULL or smaller than required      */
-  IDX_ERR_HIP = -4            /* a HIP launch reported an error               */
+  IDX_ERR_HIP = -4,           /* a HIP launch reported an error               */
+  IDX_ERR_TOO_LARGE = -5      /* idx_sparse_attn_decode_static: the call needs
+                                 more scratch than IDX_STATIC_SCRATCH_BYTES   */
 } idx_status;
 
 typedef enum {
@@ -210,6 +212,36 @@ int idx_sparse_attn_decode(const idx_seqs *seqs,
                            float softmax_scale,
                            float *out, float *lse, int32_t *out_idx,
                            void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ *
+ * Allocation-free fused decode, for callers that cannot allocate device
+ * memory (work under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc).  Same arguments, checks and results as
+ * idx_sparse_attn_decode, without the workspace: the call uses a static
+ * device buffer of IDX_STATIC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends (looked up once per device on the
+ * first call there; the calling thread's current device must be the
+ * stream's).  It allocates nothing and calls no allocating routine.
+ * Returns IDX_ERR_TOO_LARGE, before anything is enqueued, when
+ * idx_sparse_attn_workspace(seqs, H_I, d_I, H, top_k) exceeds that size (64
+ * requests x 32768 positions with Top-K 2048 and 128 heads need about 34
+ * MiB).  Every call on one GPU shares that GPU's buffer, which keeps the
+ * last call's contents (nothing in it has to start at zero: the call clears
+ * what it accumulates): two calls that can overlap on one GPU (different
+ * streams, or host threads) race and give undefined results; calls in order
+ * on one stream are safe.
+ * ------------------------------------------------------------------------ */
+#define IDX_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int idx_sparse_attn_decode_static(const idx_seqs *seqs,
+                                  const void *q_idx, int q_dtype,
+                                  const void *k_idx, int k_dtype,
+                                  const void *k_scale, const float *head_w,
+                                  int H_I, int d_I, int top_k,
+                                  const void *q, int H,
+                                  const void *kv, int kv_dtype,
+                                  float softmax_scale,
+                                  float *out, float *lse, int32_t *out_idx,
+                                  void *stream);
 
 /* ------------------------------------------------------------------------ *
  * FP8 latent-cache writer: quantise latent rows into the packed 656-byte

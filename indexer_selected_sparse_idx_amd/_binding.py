@@ -61,6 +61,8 @@ _SIGNATURES = {
                                      _P, _P, _P, _P, _SZ, _P]),
     "idx_sparse_attn_decode": (_I, [_SEQ, _P, _I, _P, _I, _P, _P, _I, _I, _I, _P, _I, _P, _I, _F,
                                     _P, _P, _P, _P, _SZ, _P]),
+    "idx_sparse_attn_decode_static": (_I, [_SEQ, _P, _I, _P, _I, _P, _P, _I, _I, _I, _P, _I, _P, _I, _F,
+                                           _P, _P, _P, _P]),
     "idx_kv_fp8_write": (_I, [_P, _I, _P, _P, _P]),
     "idx_key_fp8_write": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "idx_timer_arm": (_I, [_I, _P, _P]),
@@ -235,6 +237,28 @@ def idx_sparse_attn_decode(seqs, q_idx, k_idx, head_w, top_k, q, kv, softmax_sca
     """Fused indexer + sparse attention, one token per sequence."""
     return _fused("idx_sparse_attn_decode", seqs, q_idx, k_idx, head_w, top_k, q, kv, softmax_scale,
                   k_scale, out, lse, out_idx, want_lse, ws)
+
+
+IDX_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def idx_sparse_attn_decode_static(seqs, q_idx, k_idx, head_w, top_k, q, kv, softmax_scale, k_scale=None,
+                                  out=None, lse=None, out_idx=None, want_lse=True):
+    """Fused decode through the entry point that allocates nothing (its
+    scratch is the library's static device buffer).  Outputs not passed are
+    allocated here, by the caller's side of the boundary."""
+    T, H_I, d_I = q_idx.shape
+    H = q.shape[1]
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    rc = lib().idx_sparse_attn_decode_static(
+        seqs.ref, _ptr(q_idx), IDX_BF16 if q_idx.dtype == torch.bfloat16 else -1, _ptr(k_idx),
+        _kdtype(k_idx, k_scale), _ptr(k_scale), _ptr(head_w), H_I, d_I, top_k, _ptr(q), H, _ptr(kv), _kvdtype(kv),
+        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(out_idx), _stream())
+    _check(rc, "idx_sparse_attn_decode_static")
+    return out, lse, out_idx
 
 
 def idx_kv_fp8_write(src, dst_row, kv):

@@ -6,9 +6,18 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "idxsparse.h"
 #include "kernels.h"
+
+// Scratch memory of idx_sparse_attn_decode_static, the entry point that
+// allocates nothing: a file-scope device array of IDX_STATIC_SCRATCH_BYTES
+// that every GPU the library runs on holds until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: its device
+// address on each GPU comes from hipGetSymbolAddress (static_scratch below),
+// and only that address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[IDX_STATIC_SCRATCH_BYTES];
 
 namespace idxs {
 
@@ -207,6 +216,30 @@ int run_attn(const idx_seqs* seqs, const void* q, int H, const void* kv, int kv_
   return IDX_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept; null when
+// the lookup fails.
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> g_scratch_ptr[MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+void* static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) {
+    (void)hipGetLastError();  // leave no sticky error for the caller's next call
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(q, std::memory_order_release);
+  return q;
+}
+
 }  // namespace
 
 TimerEvents timer_take(int kernel) {
@@ -233,6 +266,9 @@ const char* idx_status_string(int status) {
     case IDX_ERR_UNSUPPORTED: return "IDX_ERR_UNSUPPORTED: dtype or dimension outside the supported set";
     case IDX_ERR_WORKSPACE: return "IDX_ERR_WORKSPACE: workspace missing or smaller than required";
     case IDX_ERR_HIP: return "IDX_ERR_HIP: a HIP kernel launch failed";
+    case IDX_ERR_TOO_LARGE:
+      return "IDX_ERR_TOO_LARGE: the call needs more scratch than the library's static buffer holds "
+             "(IDX_STATIC_SCRATCH_BYTES); use the entry point that takes a workspace";
     default: return "unknown idx_status";
   }
 }
@@ -316,6 +352,24 @@ int idx_sparse_attn_decode(const idx_seqs* seqs, const void* q_idx, int q_dtype,
   if (seqs && seqs->cu_q != nullptr) return IDX_ERR_INVALID_ARG;
   return fused(seqs, q_idx, q_dtype, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k, q, H, kv, kv_dtype,
                softmax_scale, out, lse, out_idx, ws, ws_bytes, stream);
+}
+
+int idx_sparse_attn_decode_static(const idx_seqs* seqs, const void* q_idx, int q_dtype, const void* k_idx,
+                                  int k_dtype, const void* k_scale, const float* head_w, int H_I, int d_I, int top_k,
+                                  const void* q, int H, const void* kv, int kv_dtype, float softmax_scale, float* out,
+                                  float* lse, int32_t* out_idx, void* stream) {
+  if (seqs && seqs->cu_q != nullptr) return IDX_ERR_INVALID_ARG;
+  int rc = check_indexer(seqs, q_idx, q_dtype, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k);
+  if (rc) return rc;
+  rc = check_attn(seqs, q, H, kv, kv_dtype, top_k, softmax_scale, out, lse);
+  if (rc) return rc;
+  if (seqs->num_tokens == 0) return IDX_OK;
+  const size_t need = idx_sparse_attn_workspace(seqs, H_I, d_I, H, top_k);
+  if (need > IDX_STATIC_SCRATCH_BYTES) return IDX_ERR_TOO_LARGE;
+  void* ws = static_scratch();
+  if (!ws) return IDX_ERR_HIP;
+  return fused(seqs, q_idx, q_dtype, k_idx, k_dtype, k_scale, head_w, H_I, d_I, top_k, q, H, kv, kv_dtype,
+               softmax_scale, out, lse, out_idx, ws, IDX_STATIC_SCRATCH_BYTES, stream);
 }
 
 int idx_kv_fp8_write(const void* src, int n, const int32_t* dst_row, void* kv, void* stream) {

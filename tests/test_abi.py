@@ -140,6 +140,22 @@ def test_fused_workspace_check(L):
     assert rc == -3
 
 
+def test_static_decode_rejects_calls_beyond_its_scratch(L):
+    # 64 requests x 2,000,000 positions: the score rows alone exceed the
+    # 64 MiB static buffer, so the call fails before touching the device
+    s = seqs(num_seqs=64, num_tokens=64, max_ctx_len=2_000_000, seq_stride=2_000_000)
+    assert L.idx_sparse_attn_workspace(ctypes.byref(s), 64, 128, 128, 2048) > 64 << 20
+    rc = L.idx_sparse_attn_decode_static(ctypes.byref(s), FAKE, 1, FAKE, 1, None, FAKE, 64, 128, 2048,
+                                         FAKE, 128, FAKE, 1, 1 / 24, FAKE, None, None, None)
+    assert rc == -5
+    import indexer_selected_sparse_idx_amd as m
+    assert m.idx_status_string(-5).startswith("IDX_ERR_TOO_LARGE")
+    # argument errors come first, as for the other entry points
+    bad = seqs(cu_q=FAKE, num_tokens=2)
+    assert L.idx_sparse_attn_decode_static(ctypes.byref(bad), FAKE, 1, FAKE, 1, None, FAKE, 64, 128, 2048,
+                                           FAKE, 128, FAKE, 1, 1 / 24, FAKE, None, None, None) == -1
+
+
 def test_workspace_sizes(L):
     s = seqs(num_seqs=3, num_tokens=3, max_ctx_len=1000, seq_stride=1000)
     # one fp32 score row per token padded to 64 columns, one 2048-bin key
