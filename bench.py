@@ -1,19 +1,23 @@
 #!/usr/bin/env python3
 """Throughput of the fused indexer + sparse latent attention hot path.
 
-Workload: the decode batch of 64 requests, one new token each, 32768 cached
-positions per request (contiguous latent cache of 576 bf16 per row and
-index-key cache of 128 bf16 per row), 64 indexer heads, Top-K 2048,
-128 attention heads.  One step is one idx_sparse_attn_decode call over the
-batch: score every cached position, select the Top-K, gather the selected
-latent rows and attend.  Inputs are seeded synthetic data resident in HBM
-before timing starts.
+Headline workload: the long prefill, one causal sequence of 65,536
+positions processed in 16 query chunks of 4,096 (contiguous bf16 latent
+cache of 576 per row and index-key cache of 128 per row), 64 indexer heads,
+Top-K 2048, 128 attention heads.  One step is the 16
+idx_sparse_attn_prefill calls: score every causal position of every query,
+select the Top-K, gather the selected latent rows and attend.  Inputs are
+seeded synthetic data resident in HBM before timing starts; a 1 GiB write
+flushes the caches before every timed step.
 
-Prints one JSON line.  `roofline` describes the dominant kernel (the
-indexer score, HBM-bound): its algorithmic bytes per launch over its average
-launch time, measured with HIP events the library records on the launch
-stream during the timed steps.  `cpu_baseline` is the CPU oracle timed on a
-bounded sample of the same workload (one thread).
+Prints one JSON line.  `roofline` describes the step's dominant kernel (the
+sparse attention, MFMA-bound): its algorithmic flops per launch over its
+average launch time, measured with HIP events the library records on the
+launch stream during the timed steps.  `secondary` holds the prefill
+indexer's MFMA fraction and the other four workloads (tokens/s, per-kernel
+times, the decode attention's HBM fraction).  `cpu_baseline` is the CPU
+oracle timed on a bounded row sample of the long prefill (one thread) and
+extrapolated.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -36,9 +40,8 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-sample", type=int, default=64, help="decode tokens timed on the CPU oracle")
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="run this many steps with no timing or oracle (for rocprofv3)")
@@ -57,85 +60,6 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     return ap.parse_args()
-
-
-def algorithmic_units(wl, ctx, T):
-    """Bytes / flops the method must move or compute (per step)."""
-    H_I, d_I, H, K = wl.H_I, wl.d_I, wl.H, wl.top_k
-    key_bytes = 2 if wl.k_dtype == "bf16" else 1
-    row_bytes = 1152 if wl.kv_dtype == "bf16" else 656
-    n_cand = ctx                                   # t + 1 = ctx for a decode token
-    sel = min(K, n_cand)
-    score_bytes = T * (n_cand * d_I * key_bytes + H_I * d_I * 2 + H_I * 4)
-    score_flops = T * 2 * H_I * d_I * n_cand
-    topk_bytes = T * K * 4
-    attn_bytes = T * (sel * row_bytes + H * 576 * 2 + H * 512 * 4 + H * 4 + K * 4)
-    attn_flops = T * 2176 * H * sel
-    return dict(score_bytes=score_bytes, score_flops=score_flops, topk_bytes=topk_bytes,
-                attn_bytes=attn_bytes, attn_flops=attn_flops)
-
-
-def score_source_digest():
-    h = hashlib.sha256()
-    for name in ("score.hip", "common.h", "kernels.h"):
-        with open(os.path.join(ROOT, "indexer_selected_sparse_idx_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def counter_traffic():
-    """HBM bytes per launch of the score kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(PROFILE_DIR, "score_kernel_decode_b64_ctx32768_counters.txt")
-    if not os.path.exists(path):
-        return None
-    vals = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            vals[k.strip()] = v.strip()
-    if vals.get("source_digest") != score_source_digest():
-        return None
-    try:
-        return float(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
-
-
-def cpu_baseline(inp, call, n_tokens, min_seconds=10.0):
-    """Time the oracle (indexer + Top-K + attention) on the first n_tokens
-    decode tokens, one BLAS thread, inputs already on the host."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-    import oracle
-    from oracle import reference as R
-    import torch
-
-    def bits(t):
-        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-    n_tokens = max(1, min(n_tokens, call.num_tokens))
-    seq_ids = list(range(n_tokens))
-    stride = inp.seq_stride
-    k_host = bits(inp.k_idx[: n_tokens * stride])
-    kv_host = bits(inp.kv[: n_tokens * stride])
-    q_idx = bits(inp.q_idx[:n_tokens])
-    q = bits(inp.q[:n_tokens])
-    w = inp.head_w[:n_tokens].cpu().numpy()
-    seqs = R.Seqs(ctx_len=call.ctx_len[:n_tokens].astype(np.int64), seq_stride=stride)
-    with threadpool_limits(limits=1):
-        reps, dt = 0, 0.0
-        while reps == 0 or (dt < min_seconds and reps < 50):   # bounded: about min_seconds of CPU work
-            t0 = time.perf_counter()
-            idx = oracle.score_topk(seqs, q_idx, k_host, "bf16", w, inp.wl.top_k)
-            oracle.attention(seqs, q, kv_host, "bf16", idx, 1.0 / math.sqrt(576.0))
-            dt += time.perf_counter() - t0
-            reps += 1
-    return dict(value=reps * n_tokens / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample="%d pass(es) over %d of the %d decode tokens of one step (each token: indexer over %d "
-                       "positions, Top-%d, attention over %d rows x %d heads); %.1f s on 1 thread"
-                       % (reps, n_tokens, call.num_tokens, int(call.ctx_len[0]), inp.wl.top_k, inp.wl.top_k,
-                          inp.wl.H, dt))
 
 
 def measure_workload(n, steps, warmup):
@@ -426,6 +350,292 @@ def measure_multi_token(steps, warmup):
               flush=True)
 
 
+FLUSH_BYTES = 1 << 30   # more than the L2s and the 256 MB MALL together
+
+
+class Flusher:
+    """Evicts the caches between timed steps: writes one 1 GiB buffer, then
+    reads another, so that the caches hold clean lines of the second when
+    the step starts.  (A write alone leaves them full of dirty lines, whose
+    write-back then lands inside the step: on the decode batch it slowed
+    the index-key stream from 104 to 155 us.)"""
+
+    def __init__(self, dev):
+        import torch
+        self.wbuf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+        self.rbuf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        import torch
+        self.n += 1
+        self.wbuf.fill_(self.n)
+        torch.sum(self.rbuf, dtype=torch.int64)
+
+
+def prepared_calls(wl, inp, dev):
+    """Batch descriptions and reusable outputs / workspace for every call of
+    a generated workload."""
+    import numpy as np
+    import torch
+    import indexer_selected_sparse_idx_amd as lib
+    calls = []
+    ws_bytes = 0
+    for call in inp.calls:
+        ctx = torch.from_numpy(call.ctx_len.astype(np.int32)).to(dev)
+        cu = None if call.cu_q is None else torch.from_numpy(call.cu_q.astype(np.int32)).to(dev)
+        bt_np = inp.call_block_table(call)
+        bt = None if bt_np is None else torch.from_numpy(bt_np.astype(np.int32)).to(dev)
+        s = lib.Seqs(ctx, cu, max_q_len=call.max_q_len, max_ctx_len=int(call.ctx_len.max()),
+                     num_tokens=call.num_tokens, block_table=bt, page_size=wl.page_size,
+                     seq_stride=inp.seq_stride if not wl.paged else 0)
+        s._keep = (ctx, cu, bt)
+        ws_bytes = max(ws_bytes, lib.idx_sparse_attn_workspace(s, wl.H_I, wl.d_I, wl.H, wl.top_k))
+        calls.append((call, s))
+    T_max = max(c.num_tokens for c, _ in calls)
+    bufs = dict(out=torch.empty((T_max, wl.H, 512), dtype=torch.float32, device=dev),
+                lse=torch.empty((T_max, wl.H), dtype=torch.float32, device=dev),
+                idx=torch.empty((T_max, wl.top_k), dtype=torch.int32, device=dev),
+                ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev))
+    return calls, bufs
+
+
+def run_call(lib, wl, inp, call, s, bufs, scale):
+    sl = slice(call.tok_lo, call.tok_hi)
+    fn = lib.idx_sparse_attn_decode if call.is_decode else lib.idx_sparse_attn_prefill
+    T = call.num_tokens
+    fn(s, inp.q_idx[sl], inp.k_idx, inp.head_w[sl], wl.top_k, inp.q[sl], inp.kv, scale, k_scale=inp.k_scale,
+       out=bufs["out"][:T], lse=bufs["lse"][:T], out_idx=bufs["idx"][:T], ws=bufs["ws"])
+
+
+def workload_units(wl, calls):
+    """Algorithmic work of one step over every call: indexer flops (causal
+    pairs), attention flops (selected rows), and the HBM bytes a decode call
+    must move (index keys, and the selected latent rows, queries, outputs and
+    index rows of the attention)."""
+    import numpy as np
+    key_bytes = 2 if wl.k_dtype == "bf16" else 1
+    row_bytes = 1152 if wl.kv_dtype == "bf16" else 656
+    u = dict(idx_flops=0.0, attn_flops=0.0, score_bytes=0.0, attn_bytes=0.0, tokens=0)
+    for c, _ in calls:
+        qlen = [1] * len(c.ctx_len) if c.cu_q is None else list(np.diff(c.cu_q))
+        for ctx, ql in zip(c.ctx_len, qlen):
+            ts = np.arange(int(ctx) - int(ql), int(ctx)).astype(np.float64)
+            sel = np.minimum(wl.top_k, ts + 1)
+            u["idx_flops"] += 2.0 * wl.H_I * wl.d_I * float((ts + 1).sum())
+            u["attn_flops"] += 2176.0 * wl.H * float(sel.sum())
+            u["score_bytes"] += float((ts + 1).sum()) * wl.d_I * key_bytes + ql * wl.H_I * (wl.d_I * 2 + 4)
+            u["attn_bytes"] += float(sel.sum()) * row_bytes + ql * (wl.H * (576 * 2 + 512 * 4 + 4) + wl.top_k * 4)
+        u["tokens"] += c.num_tokens
+    return u
+
+
+def pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def event_pairs(n):
+    import torch
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in pairs:          # create the underlying HIP events before handing them over
+        a.record()
+        b.record()
+    return pairs
+
+
+KERNEL_NAMES = {0: "score", 1: "topk", 2: "attn", 3: "combine"}
+
+
+def timed_steps(lib, wl, inp, calls, bufs, scale, steps, flush):
+    """`steps` steps (every call of the workload), each after a cache flush.
+    Returns per-step GPU milliseconds (events around the step on the
+    stream), the wall-clock seconds of the whole bracketed region (flushes
+    included), and per-kernel launch microseconds summed per step from the
+    events the library records around every launch of each kernel."""
+    import torch
+    # the split merge runs only in calls whose index lists are split (those
+    # need an attention workspace); its timer is armed for those calls only
+    merges = [lib.sparse_mla_attn_workspace(s, wl.H, wl.top_k) > 0 for _, s in calls]
+    step_ev = event_pairs(steps)
+    kev = {k: [event_pairs(len(calls)) for _ in range(steps)] for k in KERNEL_NAMES}
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(steps):
+        flush()
+        step_ev[i][0].record()
+        for j, (c, s) in enumerate(calls):
+            for k in KERNEL_NAMES:
+                if k != lib.IDX_KERNEL_COMBINE or merges[j]:
+                    lib.idx_timer_arm(k, kev[k][i][j][0], kev[k][i][j][1])
+            run_call(lib, wl, inp, c, s, bufs, scale)
+        step_ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = [a.elapsed_time(b) for a, b in step_ev]
+    kern = {}
+    for k, name in KERNEL_NAMES.items():
+        kern[name] = [sum(kev[k][i][j][0].elapsed_time(kev[k][i][j][1]) * 1e3
+                          for j in range(len(calls)) if k != lib.IDX_KERNEL_COMBINE or merges[j])
+                      for i in range(steps)]
+    # (a prefill call whose score kernel selects records its Top-K pair back
+    # to back: about zero)
+    return ms, wall, kern
+
+
+def measure_config(n, steps, warmup, flush, dev):
+    """One workload: per-step median / p10 / p90 and per-kernel medians."""
+    import numpy as np
+    import torch
+    import indexer_selected_sparse_idx_amd as lib
+    from workloads import config, generate
+    wl = config(n)
+    inp = generate(wl, dev)
+    calls, bufs = prepared_calls(wl, inp, dev)
+    scale = 1.0 / math.sqrt(576.0)
+    for _ in range(warmup):
+        for c, s in calls:
+            run_call(lib, wl, inp, c, s, bufs, scale)
+    torch.cuda.synchronize()
+    ms, wall, kern = timed_steps(lib, wl, inp, calls, bufs, scale, steps, flush)
+    u = workload_units(wl, calls)
+    med = pct(ms, 50)
+    km = {k: float(np.median(v)) for k, v in kern.items()}
+    res = dict(workload=wl.name, tokens=u["tokens"], steps=steps, median_ms=med, p10_ms=pct(ms, 10),
+               p90_ms=pct(ms, 90), tokens_per_s=u["tokens"] / (med * 1e-3), kernels_median_us=km)
+    attn_us = km["attn"] + km["combine"]
+    if all(c.is_decode for c, _ in calls):
+        res["score_hbm_frac"] = u["score_bytes"] / (km["score"] * 1e-6) / 1e9 / HBM_PEAK_GBS
+        res["attention_hbm_frac"] = u["attn_bytes"] / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS
+        res["attention_algorithmic_bytes"] = u["attn_bytes"]
+    res["indexer_mfma_frac"] = u["idx_flops"] / (km["score"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS
+    res["attention_mfma_frac"] = u["attn_flops"] / (attn_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS
+    del inp, calls, bufs
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return model, os.cpu_count(), avail
+
+
+def cpu_baseline_long_prefill(inp, rows_per_chunk=8, min_seconds=10.0):
+    """The oracle, on one thread, on a seeded sample of the long prefill's
+    rows, extrapolated to the whole step.  Per chunk: the chunk's keys are
+    decoded once (as the oracle's batch driver does), then each sampled row
+    is scored, selected and attended with the oracle's single-row functions.
+    The full step's time is estimated with the cost model of the work: per
+    chunk, decode time + sum over its rows of (t + 1) x (the chunk's
+    measured indexer seconds per position) + min(K, t + 1) x (its attention
+    seconds per selected row)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import torch
+    import oracle
+    from oracle import reference as R
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    wl = inp.wl
+    K = wl.top_k
+    scale = 1.0 / math.sqrt(576.0)
+    k_bits = bits(inp.k_idx)
+    kv_bits = bits(inp.kv)
+    model, ncpu, avail = cpu_info()
+    while True:
+        rng = np.random.default_rng(3)
+        est = 0.0
+        spent = 0.0
+        nrows = 0
+        with threadpool_limits(limits=1):
+            for call in inp.calls:
+                ctx = int(call.ctx_len[0])
+                T = call.num_tokens
+                t_first = ctx - T
+                pick = sorted({0, T - 1} | set(int(x) for x in rng.choice(T, size=rows_per_chunk - 2, replace=False)))
+                g = [call.tok_lo + i for i in pick]
+                q_idx = bits(inp.q_idx[g])
+                q = bits(inp.q[g])
+                w = inp.head_w[g].cpu().numpy().astype(np.float64)
+                t0 = time.perf_counter()
+                keys = R.decode_rows(k_bits, "bf16", np.arange(ctx))
+                t_dec = time.perf_counter() - t0
+                t_idx = t_att = 0.0
+                pos_sum = sel_sum = 0.0
+                for r, i in enumerate(pick):
+                    t = t_first + i
+                    a = time.perf_counter()
+                    sc = oracle.indexer_scores(oracle.bf16_bits_to_f64(q_idx[r]), keys[:t + 1], w[r])
+                    idx = oracle.topk_select(sc, K)
+                    b = time.perf_counter()
+                    sel = idx[idx >= 0].astype(np.int64)
+                    rows = R.decode_rows(kv_bits, "bf16", sel)
+                    oracle.sparse_attention(oracle.bf16_bits_to_f64(q[r]), rows, scale)
+                    c = time.perf_counter()
+                    t_idx += b - a
+                    t_att += c - b
+                    pos_sum += t + 1
+                    sel_sum += min(K, t + 1)
+                ts = np.arange(t_first, ctx, dtype=np.float64)
+                est += t_dec + t_idx * (ts + 1).sum() / pos_sum + t_att * np.minimum(K, ts + 1).sum() / sel_sum
+                spent += t_dec + t_idx + t_att
+                nrows += len(pick)
+        if spent >= min_seconds or rows_per_chunk >= 64:
+            break
+        # one more pass, sized from this one to about min_seconds
+        rows_per_chunk = min(64, int(math.ceil(rows_per_chunk * 1.1 * min_seconds / max(spent, 1e-3))))
+    tokens = sum(c.num_tokens for c in inp.calls)
+    return dict(value=tokens / est, unit="tokens/s", cores=1, kind="oracle",
+                sample="%d seeded rows (%d per 4096-token chunk, each chunk's first and last included) of the "
+                       "long prefill, indexer + Top-K + attention with the oracle's functions on 1 thread "
+                       "(BLAS pinned to 1): %.1f s measured in the final pass; the whole 65,536-token step extrapolated to %.0f s "
+                       "with the cost model (indexer ~ t + 1 per row, attention ~ min(K, t + 1)); host %s, "
+                       "%d logical CPUs (%d available to this process)"
+                       % (nrows, rows_per_chunk, spent, est, model, ncpu, avail),
+                cpu_model=model, nproc=ncpu, extrapolated=True, measured_s=spent, estimated_step_s=est)
+
+
+def attn_source_digest():
+    h = hashlib.sha256()
+    for name in ("attn.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "indexer_selected_sparse_idx_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def attn_counter_traffic():
+    """HBM bytes per launch of the prefill attention kernel over the long
+    prefill, from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, "attn_long_prefill_65536_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != attn_source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -466,77 +676,51 @@ def main():
     if args.multi_token:
         measure_multi_token(args.steps, args.warmup)
         return
-    wl = config(2)
+
+    # ---- headline: the long prefill, 65,536 positions in 16 chunks of 4,096 ----
+    wl = config(3)
     inp = generate(wl, dev)
-    call = inp.calls[0]
-    T = call.num_tokens
-    ctx_t = torch.from_numpy(call.ctx_len.astype(np.int32)).to(dev)
-    seqs = lib.Seqs(ctx_t, None, max_q_len=1, max_ctx_len=int(call.ctx_len.max()), seq_stride=inp.seq_stride)
-    out = torch.empty((T, wl.H, 512), dtype=torch.float32, device=dev)
-    lse = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
-    idx = torch.empty((T, wl.top_k), dtype=torch.int32, device=dev)
-    ws = torch.empty(lib.idx_sparse_attn_workspace(seqs, wl.H_I, wl.d_I, wl.H, wl.top_k), dtype=torch.uint8,
-                     device=dev)
+    calls, bufs = prepared_calls(wl, inp, dev)
     scale = 1.0 / math.sqrt(576.0)
-
-    def step():
-        lib.idx_sparse_attn_decode(seqs, inp.q_idx, inp.k_idx, inp.head_w, wl.top_k, inp.q, inp.kv, scale,
-                                   out=out, lse=lse, out_idx=idx, ws=ws)
-
     torch.cuda.synchronize()
     if args.profile_steps:
         for i in range(args.profile_steps):
-            step()
+            for c, s in calls:
+                run_call(lib, wl, inp, c, s, bufs, scale)
             torch.cuda.synchronize()
             print("profile step %d done" % i, flush=True)
         return
-
+    flush = Flusher(dev)
     for _ in range(args.warmup):
-        step()
+        for c, s in calls:
+            run_call(lib, wl, inp, c, s, bufs, scale)
     torch.cuda.synchronize()
-
     K = args.steps
-    names = {lib.IDX_KERNEL_SCORE: "score", lib.IDX_KERNEL_TOPK: "topk", lib.IDX_KERNEL_ATTN: "attn",
-             lib.IDX_KERNEL_COMBINE: "combine"}
+    ms, wall, kern = timed_steps(lib, wl, inp, calls, bufs, scale, K, flush)
+    u = workload_units(wl, calls)
+    ms_per_step = wall * 1e3 / K             # bracketed region / K (flushes included)
+    attn_us = float(np.mean(kern["attn"]))   # summed over the 16 launches of a step
+    score_us = float(np.mean(kern["score"]))
+    n_launch = len(calls)
+    attn_tflops = u["attn_flops"] / (attn_us * 1e-6) / 1e12
+    score_tflops = u["idx_flops"] / (score_us * 1e-6) / 1e12
+    print("headline: %.2f ms per step (median %.2f), attention %.2f ms, indexer %.2f ms"
+          % (ms_per_step, pct(ms, 50), attn_us / 1e3, score_us / 1e3), file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_long_prefill(inp)
+    del inp, calls, bufs
+    torch.cuda.empty_cache()
 
-    def event_pairs(n):
-        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for a, b in pairs:          # create the underlying HIP events before handing them over
-            a.record()
-            b.record()
-        return pairs
+    # ---- the other workloads (secondary figures) ---------------------------------
+    others = {}
+    names = {1: "tiny_prefill", 2: "decode_batch", 4: "fp8_decode", 5: "mixed_paged"}
+    for n in (1, 2, 4, 5):
+        nsteps = 20 if n in (1, 2, 4) else 5
+        others[names[n]] = measure_config(n, nsteps, 3, flush, dev)
+        print("%s: %s" % (names[n], json.dumps(others[names[n]])), file=sys.stderr, flush=True)
 
-    # timed region: K steps; the library records an event pair around every
-    # launch of the dominant (score) kernel on its launch stream
-    score_ev = event_pairs(K)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(K):
-        lib.idx_timer_arm(lib.IDX_KERNEL_SCORE, score_ev[i][0], score_ev[i][1])
-        step()
-    t_stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    gpu_ms = t_start.elapsed_time(t_stop)
-    ms_per_step = gpu_ms / K
-
-    # per-kernel breakdown in a separate (untimed) pass with every kernel armed
-    KB = min(K, 20)
-    ev = {k: event_pairs(KB) for k in names}
-    torch.cuda.synchronize()
-    for i in range(KB):
-        for k, pairs in ev.items():
-            lib.idx_timer_arm(k, pairs[i][0], pairs[i][1])
-        step()
-    torch.cuda.synchronize()
-    kern_ms = {names[k]: sum(a.elapsed_time(b) for a, b in pairs) / KB for k, pairs in ev.items()}
-    score_ms = sum(a.elapsed_time(b) for a, b in score_ev) / K
-
-    # reference: a plain 1 GiB device-to-device copy on the same GPU, after the
-    # timed region (read + write bytes per second)
+    # reference: a plain 1 GiB device-to-device copy (read + write bytes per second)
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
     cdst.copy_(csrc)
@@ -548,17 +732,12 @@ def main():
     cb.record()
     torch.cuda.synchronize()
     copy_gbs = 2.0 * (1 << 30) * 5 / (ca.elapsed_time(cb) * 1e-3) / 1e9
-    del csrc, cdst
+    del csrc, cdst, flush
 
-    u = algorithmic_units(wl, int(call.ctx_len[0]), T)
-    score_us = score_ms * 1e3
-    achieved = u["score_bytes"] / (score_ms * 1e-3) / 1e9
-    traffic = counter_traffic()
-    attn_s = (kern_ms["attn"] + kern_ms["combine"]) * 1e-3
-
+    tokens = u["tokens"]
     result = {
         "metric": "fused indexer+sparse-attn tokens/sec; achieved HBM GB/s & MFMA % of peak",
-        "value": T / (ms_per_step * 1e-3),
+        "value": tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
@@ -569,28 +748,34 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "decode batch: 64 requests x 1 token, 32768-position contiguous bf16 caches, "
-                               "indexer 64 heads d_I=128, Top-K 2048, 128 attention heads, latent 576",
-                   "batch": T, "ctx": int(call.ctx_len[0]), "H_I": wl.H_I, "d_I": wl.d_I, "top_k": wl.top_k,
-                   "H": wl.H, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "indexer score", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": u["score_bytes"], "avg_launch_us": score_us},
-        "kernels_avg_us": {k: v * 1e3 for k, v in kern_ms.items()},
+        "config": {"workload": "long prefill: one causal sequence of 65,536 positions in 16 query chunks of 4,096 "
+                               "(one idx_sparse_attn_prefill call per chunk), bf16 caches, indexer 64 heads "
+                               "d_I=128, Top-K 2048, 128 attention heads, latent 576",
+                   "seq_len": 65536, "chunk": 4096, "H_I": wl.H_I, "d_I": wl.d_I, "top_k": wl.top_k, "H": wl.H,
+                   "parallelism": "none (1 GPU)"},
+        "step_ms": {"median": pct(ms, 50), "p10": pct(ms, 10), "p90": pct(ms, 90),
+                    "note": "GPU events around each step, after a 1 GiB cache-flushing write; ms_per_step is "
+                            "the bracketed wall time / steps, flushes included"},
+        "roofline": {"bound": "mfma", "kernel": "sparse latent attention (prefill, bf16)",
+                     "achieved": attn_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / BF16_PEAK_TFLOPS, "traffic": attn_counter_traffic(),
+                     "algorithmic_flops_per_launch": u["attn_flops"] / n_launch,
+                     "avg_launch_us": attn_us / n_launch, "launches_per_step": n_launch},
+        "kernels_per_step_us": {k: float(np.mean(v)) for k, v in kern.items()},
         "secondary": {
-            "attention_hbm_gbs": u["attn_bytes"] / attn_s / 1e9,
-            "attention_hbm_frac": u["attn_bytes"] / attn_s / 1e9 / HBM_PEAK_GBS,
-            "attention_mfma_frac": u["attn_flops"] / attn_s / 1e12 / BF16_PEAK_TFLOPS,
-            "score_mfma_frac": u["score_flops"] / (score_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "step_hbm_gbs": (u["score_bytes"] + u["topk_bytes"] + u["attn_bytes"]) / (ms_per_step * 1e-3) / 1e9,
-            "wall_s_timed_region": wall,
+            "indexer_prefill": {"ms_per_step": score_us / 1e3, "tflops": score_tflops,
+                                "mfma_frac": score_tflops / BF16_PEAK_TFLOPS,
+                                "note": "score kernel with its in-kernel Top-K, 16 launches per step"},
+            "north_star_fractions": {
+                "decode_attention_hbm_decode_batch": others["decode_batch"]["attention_hbm_frac"],
+                "decode_attention_hbm_fp8_decode": others["fp8_decode"]["attention_hbm_frac"],
+                "indexer_prefill_mfma_long_prefill": score_tflops / BF16_PEAK_TFLOPS},
+            "workloads": others,
             "copy_kernel_gbs": copy_gbs,
-            "score_frac_of_copy": achieved / copy_gbs,
+            "wall_s_timed_region": wall,
         },
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, call, args.cpu_sample)
     print(json.dumps(result), flush=True)
 
 

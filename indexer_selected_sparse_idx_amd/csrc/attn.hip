@@ -32,9 +32,19 @@
 // tile, and the loop is software-pipelined: iteration k runs S of tile k
 // with the gathers of tile k + 2 spread over its k-steps, then P.V of tile
 // k - 1 with the softmax of tile k in the shadow of those MFMAs.  FP8 rows
-// (656 bytes) go into a raw LDS ring the same way and are dequantised to the
-// bf16 tile layout by the workgroup.  Splits (decode occupancy) are merged by
+// (656 bytes) go into a raw LDS ring the same way and are dequantised into
+// the tile layout by the workgroup.  Splits (decode occupancy) are merged by
 // combine_kernel.
+//
+// Products run in fp16: every wave converts the bf16 bytes its own gathers
+// brought into LDS to fp16 in place (exact for |x| in [2^-14, 65504]; below
+// that the absolute error is at most 2^-25), FP8 rows are dequantised to
+// fp16, the queries are converted once, and the softmax numerators P go into
+// the P.V product as fp16 (11 significant bits, where bf16 carries 8).  A
+// value beyond the fp16 range makes the split's softmax sum or maximum
+// non-finite; the workgroup then recomputes the split with bf16 operands
+// (and, for bf16 rows, P split into two bf16 parts, hi + lo, so the product
+// runs twice on each V^T operand).
 #include <math.h>
 
 #include <algorithm>
@@ -60,14 +70,42 @@ constexpr int DV_TILES = LATENT / 32;           // 16 dv tiles of the P.V produc
 constexpr float MAX_GROWTH = 64.0f;             // log2 growth of the max over the softmax reference tolerated
 constexpr float LN2 = 0.69314718055994530942f;
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr float MAX_GROWTH_F16 = 15.0f;         // ... when P is fp16 (p <= 2^15 < 65504)
+constexpr uint32_t RUN_GROWTH = 1u, RUN_NONFINITE = 2u;  // redo reasons
 
-// D += A * B on a 32x32 fp32 tile, K = 16 (bf16 operands).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// D += A * B on a 32x32 fp32 tile, K = 16 (fp16 operands when F16, else
+// bf16; operands are passed as their raw 16-bit patterns).
 //   a: lane l holds A[l % 32][8 * (l / 32) + 0..7]
 //   b: lane l holds B[8 * (l / 32) + 0..7][l % 32]
 //   d: register 4 i + j of lane l holds D[8 i + 4 * (l / 32) + j][l % 32]
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// Two values as raw fp16 (or bf16) bits, round to nearest even.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+// A dword of two bf16 values -> the same two values as fp16 (exact inside
+// the fp16 range).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack2<true>(__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u));
 }
 
 // O^T accumulation: the same MFMA written as inline asm with the accumulator
@@ -78,12 +116,19 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // b was just written by a VALU instruction; back-to-back MFMAs accumulating
 // into the same registers need none; o_fence() must separate the last of them
 // from any other access to the accumulators.
-template <bool NOP_B>
-__device__ __forceinline__ void mfma32_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
-  if (NOP_B)
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  else
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+template <bool F16, bool NOP_B>
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, u32x4 a, u32x4 b) {
+  if constexpr (F16) {
+    if (NOP_B)
+      asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+      asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  } else {
+    if (NOP_B)
+      asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+      asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  }
 }
 
 // max / sum of v over lanes l and l ^ 32 (both lanes get the result).
@@ -121,19 +166,39 @@ __device__ __forceinline__ int rope_off(int r, int ch) { return LAT_TILE_BYTES +
 // more than MAX_GROWTH (p could then overflow), the workgroup recomputes the
 // split with m_ref = m_max.
 struct WaveAcc {
-  bf16x8 qb[KSTEPS];
+  u32x4 qb[KSTEPS];  // raw bf16 or fp16 bits
   f32x16 o[DV_TILES];
   float m_ref, m_max, l_run;
 };
 
+// Q^T operand of the lane's head, the stored bf16 bits (convert_q<true>
+// turns them into fp16 once they have landed).
 __device__ __forceinline__ void load_q(WaveAcc& a, const AttnParams& p, int tok, int head, bool head_ok, int h) {
   const uint16_t* qrow = p.q + ((int64_t)tok * p.H + (head_ok ? head : 0)) * ROW + h * 8;
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (head_ok) v = *(const u32x4*)(qrow + ks * 16);
-    a.qb[ks] = as_bf16x8(v);
+    a.qb[ks] = v;
   }
+}
+template <bool F16>
+__device__ __forceinline__ void convert_q(WaveAcc& a) {
+  if constexpr (F16) {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a.qb[ks][j] = bf16x2_to_f16x2(a.qb[ks][j]);
+  }
+}
+
+// The 16 bytes at p (8 bf16 values) as fp16, in place.
+__device__ __forceinline__ void bf16x8_to_f16_lds(uint8_t* p) {
+  const u32x4 v = *(const u32x4*)p;
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = bf16x2_to_f16x2(v[j]);
+  *(u32x4*)p = r;
 }
 
 // Start (or restart) the accumulation; m_ref < -FLT_MAX means "take the
@@ -178,15 +243,15 @@ struct TileAddr {
   }
 };
 
-__device__ __forceinline__ bf16x8 s_operand(const uint8_t* buf, const TileAddr& ad, int ks) {
-  return *(const bf16x8*)(buf + (ks < 32 ? ad.s_lat[ks & 1] + (ks >> 1) * 64 : ad.s_rope[ks - 32]));
+__device__ __forceinline__ u32x4 s_operand(const uint8_t* buf, const TileAddr& ad, int ks) {
+  return *(const u32x4*)(buf + (ks < 32 ? ad.s_lat[ks & 1] + (ks >> 1) * 64 : ad.s_rope[ks - 32]));
 }
 
-__device__ __forceinline__ bf16x8 v_operand(const uint8_t* buf, const TileAddr& ad, int nt, int kk) {
+__device__ __forceinline__ u32x4 v_operand(const uint8_t* buf, const TileAddr& ad, int nt, int kk) {
   const int off = kk * 16 * LAT_STRIDE + nt * 64;
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + ad.v[0] + off));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(buf + ad.v[1] + off));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + ad.v[0] + off));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + ad.v[1] + off));
+  return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // S^T[32 keys x 32 heads] of one tile.  The operand of k-step ks + SPRE is
@@ -198,29 +263,29 @@ constexpr int SPRE = 3;
 // is issued (the gathers of a later tile are spread over the k-steps this
 // way).  The k-steps are expanded at compile time so that at_step sees a
 // constant.
-template <int KS, typename F>
-__device__ __forceinline__ void s_step(f32x16& acc, bf16x8 (&op)[SPRE], const WaveAcc& a, const uint8_t* buf,
+template <bool F16, int KS, typename F>
+__device__ __forceinline__ void s_step(f32x16& acc, u32x4 (&op)[SPRE], const WaveAcc& a, const uint8_t* buf,
                                        const TileAddr& ad, F& at_step) {
-  acc = mfma32(op[KS % SPRE], a.qb[KS], acc);
+  acc = mfma32<F16>(op[KS % SPRE], a.qb[KS], acc);
   if constexpr (KS + SPRE < KSTEPS) op[KS % SPRE] = s_operand(buf, ad, KS + SPRE);
   at_step(std::integral_constant<int, KS>());
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <typename F, int... KS>
+template <bool F16, typename F, int... KS>
 __device__ __forceinline__ f32x16 s_steps(const WaveAcc& a, const uint8_t* buf, const TileAddr& ad, F& at_step,
                                           std::integer_sequence<int, KS...>) {
   f32x16 acc = {};
-  bf16x8 op[SPRE];
+  u32x4 op[SPRE];
 #pragma unroll
   for (int j = 0; j < SPRE; ++j) op[j] = s_operand(buf, ad, j);
-  (s_step<KS>(acc, op, a, buf, ad, at_step), ...);
+  (s_step<F16, KS>(acc, op, a, buf, ad, at_step), ...);
   return acc;
 }
 
-template <typename F>
+template <bool F16, typename F>
 __device__ __forceinline__ f32x16 s_phase(const WaveAcc& a, const uint8_t* buf, const TileAddr& ad, F&& at_step) {
-  return s_steps(a, buf, ad, at_step, std::make_integer_sequence<int, KSTEPS>());
+  return s_steps<F16>(a, buf, ad, at_step, std::make_integer_sequence<int, KSTEPS>());
 }
 
 struct NoStep {
@@ -228,13 +293,35 @@ struct NoStep {
   __device__ __forceinline__ void operator()(std::integral_constant<int, KS>) const {}
 };
 
-// true when some head of the workgroup outgrew its reference.  `flags` is
-// one int per wave in LDS that no wave reads or writes at this point.
+// Why the workgroup must recompute the split, OR-ed over its waves:
+// RUN_GROWTH when some head outgrew its reference (by more than max_growth,
+// base 2), RUN_NONFINITE when some softmax sum or maximum is not finite (an
+// operand outside the fp16 range).  `flags` is one int per wave in LDS that
+// no wave reads or writes at this point.
 template <int NW>
-__device__ __forceinline__ bool needs_redo(const WaveAcc& a, int* flags, int wave, int lane) {
-  const bool mine = __builtin_amdgcn_ballot_w64(a.m_max > a.m_ref + MAX_GROWTH) != 0;
+__device__ __forceinline__ uint32_t redo_reasons(const WaveAcc& a, float max_growth, int* flags, int wave, int lane) {
+  const bool grew = __builtin_amdgcn_ballot_w64(a.m_max > a.m_ref + max_growth) != 0;
+  // A non-finite operand gives a NaN or infinite score: a NaN or +inf one
+  // reaches the softmax sum or the maximum.  (A -inf one gets p = 0, but 0
+  // times the infinite value makes O NaN: write_result reports that.)
+  const bool bad = __builtin_amdgcn_ballot_w64(
+                       !__builtin_isfinite(a.l_run) ||
+                       (a.l_run > 0.0f && !(__builtin_isfinite(a.m_max) && __builtin_isfinite(a.m_ref)))) != 0;
   __syncthreads();
-  if (lane == 0) flags[wave] = mine ? 1 : 0;
+  if (lane == 0) flags[wave] = (grew ? RUN_GROWTH : 0u) | (bad ? RUN_NONFINITE : 0u);
+  __syncthreads();
+  uint32_t any = 0;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) any |= (uint32_t)flags[j];
+  return any;
+}
+
+// true when `mine` holds in some lane of the workgroup (flags as above)
+template <int NW>
+__device__ __forceinline__ bool any_lane(bool mine, int* flags, int wave, int lane) {
+  const bool w = __builtin_amdgcn_ballot_w64(mine) != 0;
+  __syncthreads();
+  if (lane == 0) flags[wave] = w ? 1 : 0;
   __syncthreads();
   int any = 0;
 #pragma unroll
@@ -242,11 +329,12 @@ __device__ __forceinline__ bool needs_redo(const WaveAcc& a, int* flags, int wav
   return any != 0;
 }
 
-// P^T operand of a tile (k-step kk takes p values 8 kk .. 8 kk + 7).  With
-// SPLITP, P = P_hi + P_lo, both bf16: the product then runs twice on the same
-// V^T operand, so P carries ~16 mantissa bits instead of 8.
+// P^T operand of a tile (k-step kk takes p values 8 kk .. 8 kk + 7): fp16,
+// or bf16.  With SPLITP (bf16 only), P = P_hi + P_lo, both bf16: the product
+// then runs twice on the same V^T operand, so P carries ~16 mantissa bits
+// instead of 8.
 struct POp {
-  bf16x8 hi[2], lo[2];
+  u32x4 hi[2], lo[2];
 };
 
 // Softmax numerators of one S^T tile (base 2) against the reference, the
@@ -254,14 +342,15 @@ struct POp {
 // tile st of the previous tile's P.V MFMAs, whose shadow then hides the VALU
 // work.  The scale is positive, so the maximum is taken over the raw scores
 // and p = 2^(scale * x - m_ref) is one FMA and one exp2 per key.
-//   0-3    mask invalid keys to -inf, running maximum
+//   0-3    mask invalid keys to -inf (partial tiles only), running maximum
 //   4      start the exchange of the maximum with lane ^ 32 (same head)
 //   6      reference (first tile) and running maximum
 //   7-12   p and its sum
 //   13     running sum
 //   14-15  pack P^T (k-steps 0 and 1)
-template <bool SPLITP>
+template <bool F16, bool SPLITP>
 struct SoftmaxTile {
+  static_assert(!(F16 && SPLITP), "P is split only in bf16");
   float x[16];
   float tmax, other, psum;
   POp op;
@@ -274,12 +363,15 @@ struct SoftmaxTile {
   template <int ST>
   __device__ __forceinline__ void stage(WaveAcc& a, int nv, float scale_log2, int h) {
     if constexpr (ST < 4) {
+      if (nv < TILE) {  // (uniform: only the last tile of a split is partial)
 #pragma unroll
-      for (int j = 4 * ST; j < 4 * ST + 4; ++j) {
-        const int key = 8 * (j >> 2) + 4 * h + (j & 3);
-        x[j] = key < nv ? x[j] : -INFINITY;
-        tmax = fmaxf(tmax, x[j]);
+        for (int j = 4 * ST; j < 4 * ST + 4; ++j) {
+          const int key = 8 * (j >> 2) + 4 * h + (j & 3);
+          x[j] = key < nv ? x[j] : -INFINITY;
+        }
       }
+#pragma unroll
+      for (int j = 4 * ST; j < 4 * ST + 4; ++j) tmax = fmaxf(tmax, x[j]);
     } else if constexpr (ST == 4) {
       other = shfl_xor(tmax, 32);
     } else if constexpr (ST == 6) {
@@ -297,23 +389,22 @@ struct SoftmaxTile {
     } else if constexpr (ST == 13) {
       a.l_run += psum;
     } else if constexpr (ST >= 14) {
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
       constexpr int kk = ST - 14;
       u32x4 hi, lo;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float p0 = x[8 * kk + 2 * j], p1 = x[8 * kk + 2 * j + 1];
-        const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+        const uint32_t hw = pack2<F16>(p0, p1);
         hi[j] = hw;
         if (SPLITP) {
           const float h0 = __builtin_bit_cast(float, hw << 16), h1 = __builtin_bit_cast(float, hw & 0xffff0000u);
-          lo[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0 - h0, p1 - h1}, bf16x2));
+          lo[j] = pack2<false>(p0 - h0, p1 - h1);
         } else {
           lo[j] = 0u;
         }
       }
-      op.hi[kk] = as_bf16x8(hi);
-      op.lo[kk] = as_bf16x8(lo);
+      op.hi[kk] = hi;
+      op.lo[kk] = lo;
     }
   }
 
@@ -328,42 +419,52 @@ struct SoftmaxTile {
   }
 };
 
-// O^T += V^T . P^T over the 16 dv tiles.  The operands of dv tile nt + 1 are
-// read while the MFMAs of tile nt run; after them at_step(nt) runs (the
-// softmax stages of the next tile).  The first MFMAs wait one state in case P
-// was just written by VALU instructions.
-template <bool SPLITP, int NT, typename F>
+// O^T += V^T . P^T over the 16 dv tiles.  The operands of dv tile nt + VPRE
+// are read while the MFMAs of tile nt run; between its two MFMAs at_step(nt)
+// runs (the softmax stages of the next tile).
+// The first MFMAs wait one state in case P was just written by VALU
+// instructions.
+constexpr int VPRE = 1;
+
+template <bool F16, bool SPLITP, int NT, typename F>
 __device__ __forceinline__ void v_step(WaveAcc& a, const uint8_t* buf, const TileAddr& ad, const POp& op,
-                                       bf16x8 (&v)[2][2], F& at_step) {
-  constexpr int c = NT & 1;
-  if constexpr (NT + 1 < DV_TILES) {
-    v[c ^ 1][0] = v_operand(buf, ad, NT + 1, 0);
-    v[c ^ 1][1] = v_operand(buf, ad, NT + 1, 1);
+                                       u32x4 (&v)[VPRE + 1][2], F& at_step) {
+  constexpr int c = NT % (VPRE + 1);
+  if constexpr (NT + VPRE < DV_TILES) {
+    v[(NT + VPRE) % (VPRE + 1)][0] = v_operand(buf, ad, NT + VPRE, 0);
+    v[(NT + VPRE) % (VPRE + 1)][1] = v_operand(buf, ad, NT + VPRE, 1);
   }
   constexpr bool NOP = NT == 0;
-  mfma32_acc<NOP>(a.o[NT], v[c][0], op.hi[0]);
-  mfma32_acc<NOP>(a.o[NT], v[c][1], op.hi[1]);
-  if (SPLITP) {
-    mfma32_acc<NOP>(a.o[NT], v[c][0], op.lo[0]);
-    mfma32_acc<NOP>(a.o[NT], v[c][1], op.lo[1]);
-  }
+  // at_step(nt) goes between the tile's MFMAs: the wave issues in order, so
+  // VALU work hides under an MFMA only when it sits between two of them
+  mfma32_acc<F16, NOP>(a.o[NT], v[c][0], op.hi[0]);
+  __builtin_amdgcn_sched_barrier(0);
   at_step(std::integral_constant<int, NT>());
+  __builtin_amdgcn_sched_barrier(0);
+  mfma32_acc<F16, NOP>(a.o[NT], v[c][1], op.hi[1]);
+  if (SPLITP) {
+    mfma32_acc<F16, NOP>(a.o[NT], v[c][0], op.lo[0]);
+    mfma32_acc<F16, NOP>(a.o[NT], v[c][1], op.lo[1]);
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool SPLITP, typename F, int... NT>
+template <bool F16, bool SPLITP, typename F, int... NT>
 __device__ __forceinline__ void v_steps(WaveAcc& a, const uint8_t* buf, const TileAddr& ad, const POp& op,
                                         F& at_step, std::integer_sequence<int, NT...>) {
-  bf16x8 v[2][2];
-  v[0][0] = v_operand(buf, ad, 0, 0);
-  v[0][1] = v_operand(buf, ad, 0, 1);
-  (v_step<SPLITP, NT>(a, buf, ad, op, v, at_step), ...);
+  u32x4 v[VPRE + 1][2];
+#pragma unroll
+  for (int j = 0; j < VPRE; ++j) {
+    v[j][0] = v_operand(buf, ad, j, 0);
+    v[j][1] = v_operand(buf, ad, j, 1);
+  }
+  (v_step<F16, SPLITP, NT>(a, buf, ad, op, v, at_step), ...);
 }
 
-template <bool SPLITP, typename F>
+template <bool F16, bool SPLITP, typename F>
 __device__ __forceinline__ void v_phase(WaveAcc& a, const uint8_t* buf, const TileAddr& ad, const POp& op,
                                         F&& at_step) {
-  v_steps<SPLITP>(a, buf, ad, op, at_step, std::make_integer_sequence<int, DV_TILES>());
+  v_steps<F16, SPLITP>(a, buf, ad, op, at_step, std::make_integer_sequence<int, DV_TILES>());
 }
 
 // Normalise and store the wave's O^T (and lse) for its 32 heads.  A split's
@@ -371,35 +472,42 @@ __device__ __forceinline__ void v_phase(WaveAcc& a, const uint8_t* buf, const Ti
 // head): the head's largest |O| is brought just below 2^15, so every value
 // keeps 11 significant bits relative to that maximum (the split weights of
 // the merge are at most 1), at half the bytes of fp32 partials.
-__device__ __forceinline__ void write_result(const WaveAcc& a, const AttnParams& p, int tok, int split, int head,
+// Returns false when some O value of the lane is not finite (a NaN from an
+// operand outside the fp16 range: the caller then recomputes the split in
+// bf16 and writes again).
+__device__ __forceinline__ bool write_result(const WaveAcc& a, const AttnParams& p, int tok, int split, int head,
                                              bool head_ok, int h) {
   const float l_tot = pair_sum(a.l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_v = l_tot > 0.0f ? (a.m_ref + __builtin_amdgcn_logf(l_tot)) * LN2 : -INFINITY;
+  float osum = 0.0f;
   if (p.num_splits == 1) {
-    if (!head_ok) return;
-    float* orow = p.out + ((int64_t)tok * p.H + head) * LATENT;
+    float* orow = p.out + ((int64_t)tok * p.H + (head_ok ? head : 0)) * LATENT;
 #pragma unroll
     for (int nt = 0; nt < DV_TILES; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x4 v = {a.o[nt][4 * i], a.o[nt][4 * i + 1], a.o[nt][4 * i + 2], a.o[nt][4 * i + 3]};
-        *(f32x4*)(orow + nt * 32 + i * 8 + h * 4) = v * inv;
+        osum += (v[0] + v[1]) + (v[2] + v[3]);
+        if (head_ok) *(f32x4*)(orow + nt * 32 + i * 8 + h * 4) = v * inv;
       }
-    if (h == 0 && p.lse) p.lse[(int64_t)tok * p.H + head] = lse_v;
-    return;
+    if (head_ok && h == 0 && p.lse) p.lse[(int64_t)tok * p.H + head] = lse_v;
+    return __builtin_isfinite(osum);
   }
   float amax = 0.0f;
 #pragma unroll
   for (int nt = 0; nt < DV_TILES; ++nt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(a.o[nt][r]));
+    for (int r = 0; r < 16; ++r) {
+      amax = fmaxf(amax, fabsf(a.o[nt][r]));
+      osum += a.o[nt][r];
+    }
   amax = pair_max(amax) * inv;
   // amax < 2^e; exponents below -100 are raised so the factor stays finite
   const int e = amax > 0.0f ? max(__builtin_amdgcn_frexp_expf(amax), -100) : 0;
   const float f = __builtin_amdgcn_ldexpf(inv, 15 - e);
   const float sc = amax > 0.0f ? __builtin_amdgcn_ldexpf(1.0f, e - 15) : 0.0f;
-  if (!head_ok) return;
+  if (!head_ok) return __builtin_isfinite(osum);
   const int64_t pi = ((int64_t)tok * p.num_splits + split) * p.H + head;
   uint16_t* orow = p.part_o + pi * LATENT;
 #pragma unroll
@@ -410,6 +518,7 @@ __device__ __forceinline__ void write_result(const WaveAcc& a, const AttnParams&
       *(f16x4*)(orow + nt * 32 + i * 8 + h * 4) = __builtin_convertvector(v, f16x4);
     }
   if (h == 0) *(f32x2*)(p.part_ls + 2 * pi) = f32x2{lse_v, sc};
+  return __builtin_isfinite(osum);
 }
 
 // Work item of a workgroup.  Workgroups are dispatched round-robin over the
@@ -544,6 +653,48 @@ struct Bf16Rows {
     constexpr int J = KS * LOADS / KSTEPS;  // KSTEPS = 4 LOADS
     if constexpr (KS % (KSTEPS / LOADS) == 0) issue_one<J>(p, t, wave, lane);
   }
+
+  // fp16 copy, in place, of the 16 bytes that this lane's gather j of a tile
+  // (instruction wave * LOADS + j) brought into the tile buffer `buf`.  A wave
+  // converts only what its own gathers wrote, so its own vmcnt wait is all
+  // the conversion needs; the next barrier publishes the result.
+  __device__ __forceinline__ static int own_off(int j, int wave, int lane) {
+    const int i = wave * LOADS + j;
+    const int b = i / 9, m = i - 9 * b;
+    return (m < 8 ? (8 * b + m) * LAT_STRIDE : LAT_TILE_BYTES + b * 1024) + 16 * lane;
+  }
+  __device__ __forceinline__ static void convert_own(uint8_t* buf, int j, int wave, int lane) {
+    bf16x8_to_f16_lds(buf + own_off(j, wave, lane));
+  }
+  __device__ __forceinline__ static void convert_all(uint8_t* buf, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) convert_own(buf, j, wave, lane);
+  }
+  // The same conversion spread over the k-steps of an S phase: the wave
+  // issues in order, so VALU work hides under the MFMAs only a few
+  // instructions at a time, between them.  After the wave's own gathers of
+  // the tile have landed (wait at k-step CONV_WAIT), chunk j is read at k-step
+  // CONV0 + 3 j - 1, its dwords 0-1 converted at CONV0 + 3 j, dwords 2-3 and
+  // the write at CONV0 + 3 j + 1 (two chunks in flight).
+  static constexpr int CONV_WAIT = 4, CONV0 = 6;
+  static_assert(CONV0 + 3 * LOADS - 1 <= KSTEPS || LOADS > 9, "conversion fits the S phase");
+  template <int KS>
+  __device__ __forceinline__ static void conv_step(u32x4 (&held)[2], uint8_t* buf, int wave, int lane) {
+    constexpr int d = KS - CONV0 + 1;
+    constexpr int j = d / 3, ph = d % 3;
+    if constexpr (d >= 0 && j < LOADS) {
+      if constexpr (ph == 0) held[j & 1] = *(const u32x4*)(buf + own_off(j, wave, lane));
+      if constexpr (ph == 1) {
+        held[j & 1][0] = bf16x2_to_f16x2(held[j & 1][0]);
+        held[j & 1][1] = bf16x2_to_f16x2(held[j & 1][1]);
+      }
+      if constexpr (ph == 2) {
+        held[j & 1][2] = bf16x2_to_f16x2(held[j & 1][2]);
+        held[j & 1][3] = bf16x2_to_f16x2(held[j & 1][3]);
+        *(u32x4*)(buf + own_off(j, wave, lane)) = held[j & 1];
+      }
+    }
+  }
 };
 
 template <int NW>
@@ -563,7 +714,16 @@ struct Fp8Rows {
     }
   }
 
-  // raw packed rows (512 e4m3, 4 fp32 tile scales, 64 bf16 rope) -> bf16 tile
+  // 4 e4m3 codes times the tile scale -> 4 fp16 (or bf16) values, two dwords
+  template <bool F16>
+  __device__ __forceinline__ static u32x2 dequant4(uint32_t w, float s) {
+    const f32x2 lo = e4m3x2_lo(w), hi = e4m3x2_hi(w);
+    return u32x2{pack2<F16>(lo[0] * s, lo[1] * s), pack2<F16>(hi[0] * s, hi[1] * s)};
+  }
+
+  // raw packed rows (512 e4m3, 4 fp32 tile scales, 64 bf16 rope) -> a tile of
+  // fp16 (or bf16) values
+  template <bool F16>
   __device__ __forceinline__ static void convert(const uint8_t* raw, uint8_t* buf, int tid) {
     constexpr int THREADS = NW * WAVE;
     for (int j = tid; j < TILE * 32; j += THREADS) {
@@ -571,22 +731,34 @@ struct Fp8Rows {
       const uint8_t* src = raw + r * FP8_ROW_BYTES;
       const u32x4 codes = *(const u32x4*)(src + ch * 16);
       const float sc = *(const float*)(src + LATENT + (ch >> 3) * 4);
-      const u32x2 a0 = e4m3x4_to_bf16(codes[0], sc), a1 = e4m3x4_to_bf16(codes[1], sc);
-      const u32x2 a2 = e4m3x4_to_bf16(codes[2], sc), a3 = e4m3x4_to_bf16(codes[3], sc);
+      const u32x2 a0 = dequant4<F16>(codes[0], sc), a1 = dequant4<F16>(codes[1], sc);
+      const u32x2 a2 = dequant4<F16>(codes[2], sc), a3 = dequant4<F16>(codes[3], sc);
       *(u32x4*)(buf + lat_off(r, 2 * ch)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
       *(u32x4*)(buf + lat_off(r, 2 * ch + 1)) = u32x4{a2[0], a2[1], a3[0], a3[1]};
     }
     for (int j = tid; j < TILE * 8; j += THREADS) {
       const int r = j >> 3, ch = j & 7;
-      *(u32x4*)(buf + rope_off(r, ch)) = *(const u32x4*)(raw + r * FP8_ROW_BYTES + LATENT + 16 + ch * 16);
+      u32x4 v = *(const u32x4*)(raw + r * FP8_ROW_BYTES + LATENT + 16 + ch * 16);
+      if constexpr (F16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
+      }
+      *(u32x4*)(buf + rope_off(r, ch)) = v;
     }
   }
 };
 
 // ---------------------------------------------------------------------------
 // bf16 rows: direct HBM -> LDS gathers through an NBUF-deep ring.
+//
+// fp16 run (the default): after the S phase of tile k, each wave waits for its
+// own gathers of tile k + 1 and converts them to fp16 in place, in the shadow
+// of the P.V MFMAs of tile k - 1 (the barrier at the top of iteration k + 1
+// publishes them); tiles 0 and 1 are converted before the loop.  bf16 run
+// (the fallback when an operand leaves the fp16 range): no conversion, P split
+// into hi + lo.
 // ---------------------------------------------------------------------------
-template <int NW, int NBUF, int MAXE, bool SPLITP>
+template <int NW, int NBUF, int MAXE>
 __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * BUF_BYTES];
   __shared__ int rows_sh[MAXE];
@@ -594,6 +766,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
   // gathers of tile NBUF - 1, issued in the loop after every use of the scratch
   int* wsum = (int*)(smem + (NBUF - 1) * BUF_BYTES);
   typedef Bf16Rows<NW> R;
+  static_assert(NBUF == 4, "two tiles in flight, one in S, one in P.V");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar branches)
@@ -614,53 +787,111 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
   TileAddr ad;
   ad.init(lane);
   float m_ref = -INFINITY;
-  for (int attempt = 0; attempt < 2; ++attempt) {
+
+  auto run = [&](auto f16_tag) -> uint32_t {
+    constexpr bool F16 = decltype(f16_tag)::value;
+    constexpr bool SPLITP = !F16;
     reset_acc(a, m_ref);
     for (int k = 0; k < NBUF - 2; ++k)
       if (k < ntiles) R::issue(p, rows_sh + k * TILE, smem_base + k * BUF_BYTES, wave, lane);
     // queries and the first tiles landed: no compiler-inserted waits in the loop
     wait_vmcnt<0>();
-    // Iteration k: wait for this wave's gathers of tile k (tile k + 1 stays
-    // in flight), one barrier (tile k visible to every wave; ring slot
-    // (k + 2) % NBUF, last read by P.V of tile k - 2, free again), S of tile
-    // k with the gathers of tile k + 2 spread over its k-steps, then P.V of
-    // tile k - 1 with the softmax of tile k in the shadow of its MFMAs.
-    // Iteration 0 (no P.V before it) is peeled: a branch around the P.V
-    // inside the loop makes the compiler shuffle the AGPR-resident O^T.
+    if constexpr (F16) {
+      if (m_ref == -INFINITY) convert_q<true>(a);  // (the first fp16 run)
+      if (ntiles > 0) R::convert_all(smem, wave, lane);  // tile 0; S of tile k converts tile k + 1
+    }
+    // Iteration k: (bf16 run: wait for this wave's gathers of tile k, tile
+    // k + 1 staying in flight) one barrier (tile k visible to every wave;
+    // ring slot (k + 2) % NBUF, last read by P.V of tile k - 2, free again), S
+    // of tile k with the gathers of tile k + 2 spread over its k-steps, then
+    // P.V of tile k - 1 with the softmax of tile k (and, fp16 run, the
+    // conversion of tile k + 1) in the shadow of its MFMAs.  Iteration 0 (no
+    // P.V before it) is peeled: a branch around the P.V inside the loop makes
+    // the compiler shuffle the AGPR-resident O^T.
+    // fp16 run: S of tile k also converts tile k + 1 (this wave's gathers of
+    // it are waited for at k-step CONV_WAIT, leaving the gathers of tile k + 2
+    // issued so far in flight).  In the last iteration there is no tile k + 1:
+    // the slot converted then holds tile k - 3, read by no one any more.
     auto s_of_tile = [&](int k) {
-      if (k + 1 < ntiles) wait_vmcnt<R::LOADS>();
-      else wait_vmcnt<0>();
+      if constexpr (!F16) {
+        if (k + 1 < ntiles) wait_vmcnt<R::LOADS>();
+        else wait_vmcnt<0>();
+      }
       __syncthreads();
       const bool more = k + NBUF - 2 < ntiles;  // uniform
       const int slot_next = (k + NBUF - 2) % NBUF;
       const uint8_t* buf = smem + (k % NBUF) * BUF_BYTES;
+      uint8_t* cbuf = smem + ((k + 1) % NBUF) * BUF_BYTES;
+      u32x4 held[2];
       if (R::SPREAD && more) {
         // (the tile index goes through a scalar register so that the compiler
         // does not carry the row pointer as a VGPR induction variable)
         const int kn = __builtin_amdgcn_readfirstlane(k + NBUF - 2);
         const typename R::Tile nt = R::prepare(rows_sh + kn * TILE, smem_base + slot_next * BUF_BYTES, lane);
-        return s_phase(a, buf, ad, [&](auto ks) { R::template issue_at_step<decltype(ks)::value>(p, nt, wave, lane); });
+        return s_phase<F16>(a, buf, ad, [&](auto ks) {
+          constexpr int KS = decltype(ks)::value;
+          R::template issue_at_step<KS>(p, nt, wave, lane);
+          if constexpr (F16) {
+            // gathers of tile k + 2 issued so far: at k-steps 0, 4, .., CONV_WAIT
+            if constexpr (KS == R::CONV_WAIT) wait_vmcnt<R::CONV_WAIT / 4 + 1>();
+            R::template conv_step<KS>(held, cbuf, wave, lane);
+          }
+        });
       }
       if (more) R::issue(p, rows_sh + (k + NBUF - 2) * TILE, smem_base + slot_next * BUF_BYTES, wave, lane);
-      return s_phase(a, buf, ad, NoStep());
+      const f32x16 sres = s_phase<F16>(a, buf, ad, [&](auto ks) {
+        constexpr int KS = decltype(ks)::value;
+        if constexpr (F16) {
+          if constexpr (KS == R::CONV_WAIT) {
+            if (more) wait_vmcnt<R::LOADS>();
+            else wait_vmcnt<0>();
+          }
+          if constexpr (R::SPREAD) R::template conv_step<KS>(held, cbuf, wave, lane);
+        }
+      });
+      if constexpr (F16 && !R::SPREAD) R::convert_all(cbuf, wave, lane);
+      return sres;
     };
     POp op_prev;
     if (ntiles > 0) {
-      SoftmaxTile<SPLITP> sm(s_of_tile(0));
+      SoftmaxTile<F16, SPLITP> sm(s_of_tile(0));
       sm.run_all(a, min(TILE, n), p.scale_log2, h);
       op_prev = sm.op;
     }
     for (int k = 1; k < ntiles; ++k) {
-      SoftmaxTile<SPLITP> sm(s_of_tile(k));
+      SoftmaxTile<F16, SPLITP> sm(s_of_tile(k));
       const int nv = min(TILE, n - k * TILE);
-      v_phase<SPLITP>(a, smem + ((k - 1) % NBUF) * BUF_BYTES, ad, op_prev,
-                      [&](auto st) { sm.template stage<decltype(st)::value>(a, nv, p.scale_log2, h); });
+      v_phase<F16, SPLITP>(a, smem + ((k - 1) % NBUF) * BUF_BYTES, ad, op_prev,
+                           [&](auto st) { sm.template stage<decltype(st)::value>(a, nv, p.scale_log2, h); });
       op_prev = sm.op;
     }
-    if (ntiles > 0) v_phase<SPLITP>(a, smem + ((ntiles - 1) % NBUF) * BUF_BYTES, ad, op_prev, NoStep());
+    if (ntiles > 0) v_phase<F16, SPLITP>(a, smem + ((ntiles - 1) % NBUF) * BUF_BYTES, ad, op_prev, NoStep());
     o_fence(a);
-    if (!needs_redo<NW>(a, wsum, wave, lane)) break;
+    return redo_reasons<NW>(a, F16 ? MAX_GROWTH_F16 : MAX_GROWTH, wsum, wave, lane);
+  };
+
+  // Runs: a head that outgrew its reference (its p may then have
+  // overflowed, making the run non-finite as well) runs again against its
+  // true maximum (a second run's maximum is its reference: no further
+  // growth); a run that is non-finite otherwise, or whose O is, had an
+  // operand outside the fp16 range, and the split runs again in bf16
+  // (writing its result over the first one).
+  uint32_t why = run(std::true_type());
+  if (why & RUN_GROWTH) {
     m_ref = a.m_max;
+    why = run(std::true_type());
+  }
+  if (why == 0) {
+    const bool ok = write_result(a, p, w.tok, w.split, head, head_ok, h);
+    if (!any_lane<NW>(!ok, wsum, wave, lane)) return;
+  }
+  // bf16 operands (the result written over the fp16 one, if any)
+  m_ref = -INFINITY;
+  load_q(a, p, w.tok, head, head_ok, h);
+  why = run(std::false_type());
+  if (why & RUN_GROWTH) {
+    m_ref = a.m_max;
+    run(std::false_type());
   }
   write_result(a, p, w.tok, w.split, head, head_ok, h);
 }
@@ -693,6 +924,8 @@ __global__ __launch_bounds__(WAVE, 1) void attn_bf16_single_kernel(AttnParams p)
   TileAddr ad;
   ad.init(lane);
   float m_ref = -INFINITY;
+  // bf16 operands, P split into hi + lo (these tokens are latency-bound: few
+  // heads, short lists)
   for (int attempt = 0; attempt < 2; ++attempt) {
     reset_acc(a, m_ref);
     for (int k = 0; k < ntiles; ++k) {
@@ -700,13 +933,13 @@ __global__ __launch_bounds__(WAVE, 1) void attn_bf16_single_kernel(AttnParams p)
       // fed its MFMAs), so the buffer can be overwritten
       R::issue(p, rows_sh + k * TILE, smem_base, 0, lane);
       wait_vmcnt<0>();
-      const f32x16 sc = s_phase(a, smem, ad, NoStep());
-      SoftmaxTile<true> sm(sc);
+      const f32x16 sc = s_phase<false>(a, smem, ad, NoStep());
+      SoftmaxTile<false, true> sm(sc);
       sm.run_all(a, min(TILE, n - k * TILE), p.scale_log2, h);
-      v_phase<true>(a, smem, ad, sm.op, NoStep());
+      v_phase<false, true>(a, smem, ad, sm.op, NoStep());
     }
     o_fence(a);
-    if (!needs_redo<1>(a, wsum, 0, lane)) break;
+    if (!(redo_reasons<1>(a, MAX_GROWTH, wsum, 0, lane) & RUN_GROWTH)) break;
     m_ref = a.m_max;
   }
   write_result(a, p, w.tok, w.split, head, head_ok, h);
@@ -714,7 +947,9 @@ __global__ __launch_bounds__(WAVE, 1) void attn_bf16_single_kernel(AttnParams p)
 
 // ---------------------------------------------------------------------------
 // FP8 rows: gathers into a raw NRAW-deep ring, dequantised by the workgroup
-// into a double-buffered bf16 tile.
+// into a double-buffered tile: fp16 values (exact for the codes times their
+// tile scale inside the fp16 range) and fp16 P; bf16 values and bf16 P when
+// a value leaves the fp16 range.
 // ---------------------------------------------------------------------------
 template <int NW, int NRAW, int MAXE>
 __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
@@ -744,13 +979,15 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
   TileAddr ad;
   ad.init(lane);
   float m_ref = -INFINITY;
-  for (int attempt = 0; attempt < 2; ++attempt) {
+
+  auto run = [&](auto f16_tag) -> uint32_t {
+    constexpr bool F16 = decltype(f16_tag)::value;
     reset_acc(a, m_ref);
 #pragma unroll
     for (int k = 0; k < NRAW - 1; ++k)
       if (k < ntiles) R::issue(p, rows_sh + k * TILE, raw_base + k * RAW_TILE_BYTES, wave, lane);
     // Iteration k: raw tile k ready (barrier: visible; raw slot (k - 1) % NRAW
-    // and bf16 slot k % 2 free), issue raw tile k + NRAW - 1, dequantise tile
+    // and tile slot k % 2 free), issue raw tile k + NRAW - 1, dequantise tile
     // k, barrier, compute tile k.
     for (int k = 0; k < ntiles; ++k) {
       const int later = min(NRAW - 2, ntiles - 1 - k);
@@ -762,16 +999,35 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
         R::issue(p, rows_sh + (k + NRAW - 1) * TILE, raw_base + ((k + NRAW - 1) % NRAW) * RAW_TILE_BYTES, wave,
                  lane);
       uint8_t* buf = smem + (k & 1) * BUF_BYTES;
-      R::convert(raw + (k % NRAW) * RAW_TILE_BYTES, buf, tid);
+      R::template convert<F16>(raw + (k % NRAW) * RAW_TILE_BYTES, buf, tid);
       __syncthreads();
-      const f32x16 s = s_phase(a, buf, ad, NoStep());
-      SoftmaxTile<false> sm(s);
+      const f32x16 sc = s_phase<F16>(a, buf, ad, NoStep());
+      SoftmaxTile<F16, false> sm(sc);
       sm.run_all(a, min(TILE, n - k * TILE), p.scale_log2, h);
-      v_phase<false>(a, buf, ad, sm.op, NoStep());
+      v_phase<F16, false>(a, buf, ad, sm.op, NoStep());
     }
     o_fence(a);
-    if (!needs_redo<NW>(a, wsum, wave, lane)) break;
+    return redo_reasons<NW>(a, F16 ? MAX_GROWTH_F16 : MAX_GROWTH, wsum, wave, lane);
+  };
+
+  // attempts as in attn_bf16_kernel
+  convert_q<true>(a);
+  uint32_t why = run(std::true_type());
+  if (why & RUN_GROWTH) {
     m_ref = a.m_max;
+    why = run(std::true_type());
+  }
+  if (why == 0) {
+    const bool ok = write_result(a, p, w.tok, w.split, head, head_ok, h);
+    if (!any_lane<NW>(!ok, wsum, wave, lane)) return;
+  }
+  m_ref = -INFINITY;
+  load_q(a, p, w.tok, head, head_ok, h);  // the stored bf16 queries again
+  wait_vmcnt<0>();
+  why = run(std::false_type());
+  if (why & RUN_GROWTH) {
+    m_ref = a.m_max;
+    run(std::false_type());
   }
   write_result(a, p, w.tok, w.split, head, head_ok, h);
 }
@@ -832,8 +1088,8 @@ hipError_t launch_nw(const AttnParams& p, bool fp8, hipStream_t stream, const Ti
   if (fp8) return launch_grid(attn_fp8_kernel<NW, 3, 2048>, p, NW, stream, t);
   if (NW == 1 && p.num_splits == 1 && p.split_len <= 256)
     return launch_grid(attn_bf16_single_kernel<256>, p, 1, stream, t);
-  if (p.split_len <= 1024) return launch_grid(attn_bf16_kernel<NW, 4, 1024, true>, p, NW, stream, t);
-  return launch_grid(attn_bf16_kernel<NW, 4, 2048, true>, p, NW, stream, t);
+  if (p.split_len <= 1024) return launch_grid(attn_bf16_kernel<NW, 4, 1024>, p, NW, stream, t);
+  return launch_grid(attn_bf16_kernel<NW, 4, 2048>, p, NW, stream, t);
 }
 
 }  // namespace

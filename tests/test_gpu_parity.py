@@ -381,3 +381,49 @@ def test_two_token_rows_split_keys():
     wl = Workload("two-token rows", ctx, [{"seqs": list(range(5)), "q_len": q_len}], top_k=2048, H=16,
                   seed=34)
     _parity_all(generate(wl, "cuda"), U.TOL_BF16, "two-token")
+
+
+def test_attention_values_beyond_fp16_range():
+    """The attention computes in fp16 unless an operand leaves its range:
+    rows holding values beyond fp16's 65,504 make the split's scores or
+    output non-finite in fp16 (+inf scores where the query value is
+    positive, 0 x inf in P.V where it is negative), and the workgroup must
+    recompute it in bf16.  bf16 rows hold 70,000 (stored as 70,144); FP8
+    rows get a tile scale of 2^9, so their values (up to 448 x 512) stay
+    exact in the bf16 recomputation (with a scale that is not a power of
+    two the bf16 rounding of such large values moves scores by several
+    units, see the design notes).  Decode splits, bf16 and FP8 rows."""
+    import indexer_selected_sparse_idx_amd as lib
+    import oracle
+    from oracle import formats as Fm
+    for kv_dtype, tol in (("bf16", U.TOL_BF16), ("fp8_656", U.TOL_FP8)):
+        wl = Workload("beyond fp16", [3000, 700], [{"seqs": [0, 1], "q_len": None}], H=64, top_k=512,
+                      kv_dtype=kv_dtype, seed=40)
+        inp = generate(wl, "cuda")
+        call = inp.calls[0]
+        s = U.lib_seqs(inp, call)
+        rng = np.random.default_rng(40)
+        idx = torch.from_numpy(np.stack([np.sort(rng.choice(c, 512, replace=False)) for c in (3000, 700)])
+                               .astype(np.int32)).cuda()
+        kv = inp.kv.clone()
+        for b in range(2):
+            rows = (b * inp.seq_stride + idx[b, [7, 300]].long())
+            if kv_dtype == "bf16":
+                big = kv[rows].float()
+                big[:, 5] = 70000.0
+                kv[rows] = big.to(torch.bfloat16)
+            else:
+                # tile 0 of the row: a code of 448 at dim 5, the tile's fp32 scale 2^9
+                raw = kv[rows]
+                raw[:, 5] = 0x7E
+                raw[:, 512:516] = torch.from_numpy(np.array([512.0], np.float32).view(np.uint8)).cuda()
+                kv[rows] = raw
+        out, lse = lib.sparse_mla_attn(s, inp.q, kv, idx, U.SCALE)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+        osq = U.oracle_seqs(inp, call)
+        w_out, w_lse = oracle.attention(osq, U.bits16(inp.q), U.host_raw(kv), kv_dtype, idx.cpu().numpy(), U.SCALE)
+        assert np.abs(w_out).max() > 65504.0       # the case is what it claims
+        # scores reach thousands (natural log units): lse compared relative to that scale
+        U.check_attention(out.cpu().numpy(), lse.cpu().numpy() / 1e4, w_out, w_lse / 1e4, tol,
+                          "beyond fp16 %s" % kv_dtype)
