@@ -289,6 +289,28 @@ int idx_kv_fp8_write(const void *src, int n, const int32_t *dst_row, void *kv, v
 int idx_key_fp8_write(const void *src, int n, int d_I, const int32_t *dst_row, void *k_cache, float *k_scale,
                       void *stream);
 
+/* ------------------------------------------------------------------------ *
+ * MXFP8 index-key writer: quantises n new bf16 keys of d_I = 128 into the
+ * MXFP8 index cache that idx_score_topk reads with k_dtype IDX_MXFP8 --
+ * blocks of 32 values sharing a power-of-two scale ("Hierarchical
+ * Quantization", index-cache bullet, in Day 0 Inference Support for New LLM
+ * Architectures; section 4 of Day 0 Inference Adaptation and Performance
+ * Optimization for New Models).  Per block the OCP MX rule for E4M3
+ * elements: e = floor(log2(amax)) - 8, clamped to [-127, 127]; E8M0 byte
+ * e + 127; codes E4M3FN(clamp(k / 2^e, -448, 448)), rounded to the nearest
+ * value, ties to even, the sign kept; an all-zero block gets byte 0 and
+ * codes 0.
+ *
+ *   src      bf16 [n, 128] keys;  n >= 0 (n == 0: nothing is launched)
+ *   dst_row  device int32 [n]: destination cache row (entries < 0 skipped)
+ *   k_cache  E4M3FN codes, rows of 128 bytes, 16-byte aligned
+ *   k_exp    E8M0 block exponents, rows of 4 bytes (block j of row r at
+ *            k_exp[4 r + j]), 4-byte aligned
+ * Rows not named by dst_row are left untouched.  Errors: IDX_ERR_INVALID_ARG
+ * for n < 0, a NULL or misaligned pointer; IDX_ERR_HIP for a launch failure.
+ * ------------------------------------------------------------------------ */
+int idx_key_mxfp8_write(const void *src, int n, const int32_t *dst_row, void *k_cache, void *k_exp, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *idx_status_string(int status);
 

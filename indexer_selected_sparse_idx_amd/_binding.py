@@ -65,6 +65,7 @@ _SIGNATURES = {
                                            _P, _P, _P, _P]),
     "idx_kv_fp8_write": (_I, [_P, _I, _P, _P, _P]),
     "idx_key_fp8_write": (_I, [_P, _I, _I, _P, _P, _P, _P]),
+    "idx_key_mxfp8_write": (_I, [_P, _I, _P, _P, _P, _P]),
     "idx_timer_arm": (_I, [_I, _P, _P]),
 }
 
@@ -280,6 +281,18 @@ def idx_key_fp8_write(src, dst_row, k_cache, k_scale=None):
     rc = lib().idx_key_fp8_write(_ptr(src), n, d, _ptr(dst_row), _ptr(k_cache), _ptr(k_scale), _stream())
     _check(rc, "idx_key_fp8_write")
     return k_cache
+
+
+def idx_key_mxfp8_write(src, dst_row, k_cache, k_exp):
+    """Store bf16 index keys src [n, 128] as MXFP8 in rows dst_row[i]: E4M3FN
+    codes in k_cache (uint8 [rows, 128]) and E8M0 block exponents in k_exp
+    (uint8 [rows, 4]).  Returns (k_cache, k_exp)."""
+    n = int(src.shape[0])
+    if n and int(src.shape[1]) != 128:
+        raise ValueError("idx_key_mxfp8_write: keys must have 128 values")
+    rc = lib().idx_key_mxfp8_write(_ptr(src), n, _ptr(dst_row), _ptr(k_cache), _ptr(k_exp), _stream())
+    _check(rc, "idx_key_mxfp8_write")
+    return k_cache, k_exp
 
 
 def idx_timer_arm(kernel, start_event, stop_event):

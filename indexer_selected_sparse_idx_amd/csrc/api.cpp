@@ -402,6 +402,20 @@ int idx_key_fp8_write(const void* src, int n, int d_I, const int32_t* dst_row, v
   return launch_key_fp8_write(p, static_cast<hipStream_t>(stream)) == hipSuccess ? IDX_OK : IDX_ERR_HIP;
 }
 
+int idx_key_mxfp8_write(const void* src, int n, const int32_t* dst_row, void* k_cache, void* k_exp, void* stream) {
+  if (n < 0) return IDX_ERR_INVALID_ARG;
+  if (n == 0) return IDX_OK;
+  if (!src || !dst_row || !k_cache || !k_exp) return IDX_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(k_cache) || !aligned4(dst_row) || !aligned4(k_exp)) return IDX_ERR_INVALID_ARG;
+  KeyMxWriteParams p;
+  p.src = static_cast<const uint16_t*>(src);
+  p.n = n;
+  p.dst_row = dst_row;
+  p.k = static_cast<uint8_t*>(k_cache);
+  p.k_exp = static_cast<uint8_t*>(k_exp);
+  return launch_key_mxfp8_write(p, static_cast<hipStream_t>(stream)) == hipSuccess ? IDX_OK : IDX_ERR_HIP;
+}
+
 int idx_timer_arm(int kernel, void* start_event, void* stop_event) {
   if (kernel < 0 || kernel >= IDX_KERNEL_COUNT || !start_event || !stop_event) return IDX_ERR_INVALID_ARG;
   g_timers[kernel].start = static_cast<hipEvent_t>(start_event);

@@ -119,6 +119,16 @@ hipError_t launch_attn(const AttnParams& p, bool kv_fp8, hipStream_t stream);
 hipError_t launch_kv_fp8_write(const KvWriteParams& p, hipStream_t stream);
 hipError_t launch_key_fp8_write(const KeyWriteParams& p, hipStream_t stream);
 
+struct KeyMxWriteParams {
+  const uint16_t* src;     // bf16 [n, 128] index keys
+  int n;
+  const int32_t* dst_row;  // [n] destination cache row (< 0: skipped)
+  uint8_t* k;              // E4M3FN codes, rows of 128 bytes
+  uint8_t* k_exp;          // E8M0 block exponents, rows of 4 bytes
+};
+
+hipError_t launch_key_mxfp8_write(const KeyMxWriteParams& p, hipStream_t stream);
+
 // Timing hook (api.cpp): the events armed for the next launch of `kernel`
 // (null when none), disarmed by the call.
 struct TimerEvents {

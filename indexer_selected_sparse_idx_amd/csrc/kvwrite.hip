@@ -1,6 +1,7 @@
 // FP8 latent-cache writer on gfx950.
 //
-// Also writes FP8 index keys (key_fp8_write_kernel, below).
+// Also writes FP8 index keys (key_fp8_write_kernel, below) and MXFP8 index
+// keys (key_mxfp8_write_kernel).
 //
 // Quantises latent rows (576 bf16: 512 latent values, 64 rope values) into
 // the packed 656-byte FP8 row the sparse attention reads: per-token tiles of
@@ -130,7 +131,66 @@ __global__ __launch_bounds__(KVW_WAVES * WAVE) void key_fp8_write_kernel(KeyWrit
   }
 }
 
+// MXFP8 index keys (d_I = 128): blocks of 32 values with a shared
+// power-of-two scale ("Hierarchical Quantization", index-cache bullet, in
+// Day 0 Inference Support for New LLM Architectures; section 4 of Day 0
+// Inference Adaptation and Performance Optimization for New Models), by the
+// OCP MX rule for E4M3 elements, the rule the MXFP8 indexer applies to its
+// queries: e = floor(log2(amax)) - 8 clamped to [-127, 127] (E8M0 byte
+// e + 127; an all-zero block gets byte 0 and codes 0), codes
+// E4M3FN(clamp(k / 2^e, -448, 448)) -- the division by a power of two is
+// exact.  Lane l of a row's 16 lanes holds keys 8 l .. 8 l + 7, so a block is
+// 4 lanes and its amax a 4-lane max reduction.
+__global__ __launch_bounds__(KVW_WAVES * WAVE) void key_mxfp8_write_kernel(KeyMxWriteParams p) {
+  constexpr int D = 128, G = D / 8, RPS = WAVE / G, KW_STEPS = 4;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / G, gl = lane % G;
+  const int base = (blockIdx.x * KVW_WAVES + (threadIdx.x >> 6)) * RPS * KW_STEPS;
+  u32x4 w[KW_STEPS];
+  int dst[KW_STEPS];
+#pragma unroll
+  for (int j = 0; j < KW_STEPS; ++j) {
+    const int r = base + j * RPS + sub;
+    const int rr = min(r, p.n - 1);  // (rows past n: a valid row, not stored)
+    dst[j] = r < p.n ? p.dst_row[rr] : -1;
+    w[j] = *(const u32x4*)(p.src + (int64_t)rr * D + 8 * gl);
+  }
+#pragma unroll
+  for (int j = 0; j < KW_STEPS; ++j) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[j][e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[j][e] & 0xffff0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = fmaxf(amax, shfl_xor(amax, 1));
+    amax = fmaxf(amax, shfl_xor(amax, 2));
+    // amax = m 2^E with m in [0.5, 1): floor(log2 amax) = E - 1
+    const int e = amax > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(amax) - 1 - 8, -127), 127) : -127;
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = amax > 0.0f ? clamp_e4m3(__builtin_amdgcn_ldexpf(x[i], -e)) : 0.0f;
+    if (dst[j] < 0) continue;
+    uint32_t c0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    c0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)c0, true);
+    uint32_t c1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+    c1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], (int)c1, true);
+    *(u32x2*)(p.k + (int64_t)dst[j] * D + 8 * gl) = u32x2{c0, c1};
+    if ((gl & 3) == 0) p.k_exp[(int64_t)dst[j] * 4 + (gl >> 2)] = (uint8_t)(amax > 0.0f ? e + 127 : 0);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_key_mxfp8_write(const KeyMxWriteParams& p, hipStream_t stream) {
+  constexpr int KW_STEPS = 4;
+  const int rows_per_wg = KVW_WAVES * KW_STEPS * (WAVE / 16);
+  hipLaunchKernelGGL(key_mxfp8_write_kernel, dim3(cdiv(p.n, rows_per_wg)), dim3(KVW_WAVES * WAVE), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_key_fp8_write(const KeyWriteParams& p, hipStream_t stream) {
   constexpr int KW_STEPS = 4;

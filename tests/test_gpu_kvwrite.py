@@ -17,6 +17,7 @@ import torch
 
 import indexer_selected_sparse_idx_amd as lib
 import oracle
+from oracle import formats as F
 from oracle import writer as W
 
 import gpu_util as U
@@ -181,3 +182,88 @@ def test_written_fp8_keys_through_the_indexer():
     want = np.stack([oracle.topk_select(oracle.indexer_scores(qf[b], kf[b * ctx:(b + 1) * ctx], w[b]), K)
                      for b in range(B)])
     U.check_indices(idx.cpu().numpy(), want, "written fp8 keys")
+
+
+def _mx_keys(n, seed):
+    """bf16 keys [n, 128] whose blocks of 32 differ in range: N(0, 1) values
+    times 2^s per block (s in [-20, 20]), so most values round under the MX
+    rule; plus rows and blocks with special cases."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    k = torch.randn((n, 128), generator=g, device="cuda")
+    s = torch.randint(-20, 21, (n, 4), generator=g, device="cuda").float()
+    k = k * torch.pow(2.0, s).repeat_interleave(32, dim=1)
+    k[0] = 0.0                                               # all-zero row: bytes 0, codes 0
+    k[1] = -0.0
+    k[2, 64:96] = 0.0                                        # one all-zero block
+    # a block whose values divided by 2^e (e = 0) pass 448: they saturate
+    k[3, :32] = torch.tensor([511.0, 480.0, 449.0, 448.0, -500.0, 300.0, 1.0, -0.5] * 4, device="cuda")
+    # values halfway between E4M3 codes after the division: ties to even
+    k[4, :32] = torch.tensor([256.0, 17.0, 19.0, -26.0, 27.0, 2.0 ** -6, 3 * 2.0 ** -9, -9.0] * 4,
+                             device="cuda")
+    k[5] = torch.randint(-8, 9, (128,), generator=g, device="cuda").float()
+    return k.to(torch.bfloat16)
+
+
+def test_key_mxfp8_write_bytes_match_oracle():
+    n, rows = 300, 400
+    src = _mx_keys(n, 80)
+    rng = np.random.default_rng(81)
+    dst = rng.permutation(rows)[:n].astype(np.int32)
+    dst[[7, 150]] = -1
+    kc = torch.full((rows, 128), 0xCD, dtype=torch.uint8, device="cuda")
+    ke = torch.full((rows, 4), 0xAB, dtype=torch.uint8, device="cuda")
+    lib.idx_key_mxfp8_write(src, torch.from_numpy(dst).cuda(), kc, ke)
+    torch.cuda.synchronize()
+    want_c, want_e = W.mxfp8_from_values(oracle.bf16_bits_to_f64(U.bits16(src)))
+    got_c, got_e = kc.cpu().numpy(), ke.cpu().numpy()
+    live = dst >= 0
+    assert np.array_equal(got_e[dst[live]], want_e[live])
+    assert np.array_equal(got_c[dst[live]], want_c[live])
+    untouched = sorted(set(range(rows)) - set(dst[live].tolist()))
+    assert np.all(got_c[untouched] == 0xCD) and np.all(got_e[untouched] == 0xAB)
+    # the cases are what they claim: codes that saturate, exponents that vary
+    assert np.any(want_c[live] == 0x7E) and len(np.unique(want_e[live])) > 20
+
+
+def test_key_mxfp8_write_tiny_and_huge_blocks():
+    # blocks whose exponent clamps at -127 (bf16 values near the bottom of
+    # the range, subnormal ones included) and blocks near the bf16 maximum
+    vals = np.zeros((4, 128), dtype=np.float64)
+    vals[0, :32] = np.ldexp(1.0, -130) * np.arange(1, 33)
+    vals[1, :32] = np.ldexp(1.0, -126) * np.linspace(-3.0, 3.0, 32)
+    vals[2, :32] = np.ldexp(1.0, 120) * np.linspace(-1.5, 1.5, 32)
+    vals[3] = np.ldexp(1.0, -140)
+    src = torch.from_numpy(vals).float().to(torch.bfloat16).cuda()
+    kc = torch.zeros((4, 128), dtype=torch.uint8, device="cuda")
+    ke = torch.zeros((4, 4), dtype=torch.uint8, device="cuda")
+    lib.idx_key_mxfp8_write(src, torch.arange(4, dtype=torch.int32, device="cuda"), kc, ke)
+    torch.cuda.synchronize()
+    want_c, want_e = W.mxfp8_from_values(oracle.bf16_bits_to_f64(U.bits16(src)))
+    assert np.array_equal(ke.cpu().numpy(), want_e)
+    assert np.array_equal(kc.cpu().numpy(), want_c)
+
+
+def test_written_mxfp8_keys_through_the_indexer():
+    # integer keys times a power of two per block, written as MXFP8 (exact),
+    # scored by the MXFP8 indexer: the Top-K sets must match the oracle's
+    B, ctx, H_I, K = 4, 3000, 64, 512
+    g = torch.Generator(device="cuda").manual_seed(82)
+    k = torch.randint(-8, 9, (B * ctx, 128), generator=g, device="cuda").float()
+    s = torch.randint(-2, 1, (B * ctx, 4), generator=g, device="cuda").float()
+    keys = (k * torch.pow(2.0, s).repeat_interleave(32, dim=1)).to(torch.bfloat16)
+    kc = torch.empty((B * ctx, 128), dtype=torch.uint8, device="cuda")
+    ke = torch.empty((B * ctx, 4), dtype=torch.uint8, device="cuda")
+    lib.idx_key_mxfp8_write(keys, torch.arange(B * ctx, dtype=torch.int32, device="cuda"), kc, ke)
+    q_idx = torch.randint(-4, 5, (B, H_I, 128), generator=g, device="cuda").to(torch.bfloat16)
+    head_w = torch.pow(2.0, -torch.randint(0, 4, (B, H_I), generator=g, device="cuda").float())
+    ctx_t = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+    sq = lib.Seqs(ctx_t, None, max_q_len=1, max_ctx_len=ctx, num_tokens=B, seq_stride=ctx)
+    idx = lib.idx_score_topk(sq, q_idx, kc, head_w, K, k_scale=ke)
+    torch.cuda.synchronize()
+    kf = F.mxfp8_to_f64(kc.cpu().numpy(), ke.cpu().numpy())
+    assert np.array_equal(kf, keys.float().cpu().numpy().astype(np.float64))
+    qf = oracle.bf16_bits_to_f64(U.bits16(q_idx))
+    w = head_w.cpu().numpy().astype(np.float64)
+    want = np.stack([oracle.topk_select(oracle.indexer_scores(qf[b], kf[b * ctx:(b + 1) * ctx], w[b]), K)
+                     for b in range(B)])
+    U.check_indices(idx.cpu().numpy(), want, "written mxfp8 keys")
