@@ -257,8 +257,8 @@ def measure_mxfp8(steps, warmup):
                           "hbm_frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "score_topk_call_us": call_us}),
               flush=True)
     # a prefill chunk: the last 4096 positions of the first sequence as query
-    # tokens (MXFP8 keys: every token streams its causal range; bf16 keys: the
-    # prefill kernel, key tiles shared by 8 tokens)
+    # tokens (both key formats through the prefill kernel, key tiles shared by
+    # 8 tokens; MXFP8: one scaled fp8 MFMA per 128 dims)
     Q = 4096
     ctx0 = int(call.ctx_len[0])
     ctx1 = torch.tensor([ctx0], dtype=torch.int32, device=dev)

@@ -170,7 +170,7 @@ int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int 
   sp.out_idx = out_idx;
   const int k_format = k_dtype == IDX_E4M3 ? 1 : k_dtype == IDX_MXFP8 ? 2 : 0;
   if (launch_score(sp, k_format, stream) != hipSuccess) return IDX_ERR_HIP;
-  if (k_dtype != IDX_MXFP8 && score_selects(sp.sv)) {
+  if (score_selects(sp.sv)) {
     // the score kernel has selected: an armed Top-K timer measures nothing
     const TimerEvents t = timer_take(IDX_KERNEL_TOPK);
     if (t.start) (void)hipEventRecord(t.start, stream);

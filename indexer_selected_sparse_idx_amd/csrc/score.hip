@@ -275,6 +275,64 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
 // keys 59 us)
 constexpr int MX_KPW = 4096;
 
+// The query operand of the scaled MFMA, quantised by the MX rule.  The
+// instruction reads, in lane group g, the values k = 16 g .. +15 from bytes
+// 0..15 and k = 64 + 16 g .. +15 from bytes 16..31, and takes the exponent of
+// the 32-value block s of row m from lane m + 16 s.  So lane (c, g) finds the
+// exponent of block g of head 16 mt + c, passes it as its scale operand (qe),
+// and quantises its two 16-value halves with the exponents of blocks g >> 1
+// and 2 + (g >> 1), fetched from the lanes that own them; w gets the head
+// weights of heads 16 mt + 4 g + r (the rows of the lane's accumulator).
+template <int MT>
+__device__ __forceinline__ void mx_query(const ScoreParams& p, int tok, int g, int c, i32x8 (&qa)[MT], int (&qe)[MT],
+                                         float (&w)[MT][4]) {
+  const uint16_t* qrow = p.q_idx + (int64_t)tok * p.H_I * 128;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = mt * 16 + c;
+    const uint16_t* qh = qrow + (int64_t)h * 128;
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (h < p.H_I) raw = *(const u32x4*)(qh + 32 * g + 8 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[e] << 16)), fabsf(__uint_as_float(raw[e] & 0xffff0000u))));
+    }
+    // shared exponent floor(log2 amax) - 8 (frexp: amax = m 2^E, m in [0.5, 1))
+    const int e = amax > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(amax) - 9, -127), 127) : -127;
+    qe[mt] = e + 127;
+    const int e_lo = __shfl(e, c + 16 * (g >> 1));
+    const int e_hi = __shfl(e, c + 16 * (2 + (g >> 1)));
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int eh = half ? e_hi : e_lo;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (h < p.H_I) raw = *(const u32x4*)(qh + 64 * half + 16 * g + 8 * j);
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          float x[4];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t r = raw[2 * e2 + k];
+            x[2 * k] = fminf(fmaxf(__builtin_amdgcn_ldexpf(__uint_as_float(r << 16), -eh), -448.0f), 448.0f);
+            x[2 * k + 1] = fminf(fmaxf(__builtin_amdgcn_ldexpf(__uint_as_float(r & 0xffff0000u), -eh), -448.0f), 448.0f);
+          }
+          qa[mt][4 * half + 2 * j + e2] = (int)fp8x4(x[0], x[1], x[2], x[3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hr = mt * 16 + g * 4 + r;
+      w[mt][r] = hr < p.H_I ? p.head_w[(int64_t)tok * p.H_I + hr] : 0.0f;
+    }
+  }
+}
+
 template <int MT>
 __global__ __launch_bounds__(256) void score_mx_kernel(ScoreParams p, int keys_per_wg) {
   __shared__ uint32_t lhist[SCORE_HIST_BINS];
@@ -306,61 +364,10 @@ __global__ __launch_bounds__(256) void score_mx_kernel(ScoreParams p, int keys_p
   __syncthreads();
 
   if (active) {
-    // ---- query operand ------------------------------------------------------
-    // The scaled MFMA reads, in lane group g, the values k = 16 g .. +15 from
-    // bytes 0..15 and k = 64 + 16 g .. +15 from bytes 16..31, and takes the
-    // exponent of the 32-value block s of row m from lane m + 16 s.  So lane
-    // (c, g) finds the exponent of block g of head 16 mt + c, passes it as its
-    // scale operand, and quantises its two 16-value halves with the exponents
-    // of blocks g >> 1 and 2 + (g >> 1), fetched from the lanes that own them.
     i32x8 qa[MT];
     int qe[MT];
     float w[MT][4];
-    const uint16_t* qrow = p.q_idx + (int64_t)tok * p.H_I * 128;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int h = mt * 16 + c;
-      const uint16_t* qh = qrow + (int64_t)h * 128;
-      float amax = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (h < p.H_I) raw = *(const u32x4*)(qh + 32 * g + 8 * j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(raw[e] << 16)), fabsf(__uint_as_float(raw[e] & 0xffff0000u))));
-      }
-      // shared exponent floor(log2 amax) - 8 (frexp: amax = m 2^E, m in [0.5, 1))
-      const int e = amax > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(amax) - 9, -127), 127) : -127;
-      qe[mt] = e + 127;
-      const int e_lo = __shfl(e, c + 16 * (g >> 1));
-      const int e_hi = __shfl(e, c + 16 * (2 + (g >> 1)));
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int eh = half ? e_hi : e_lo;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u32x4 raw = {0u, 0u, 0u, 0u};
-          if (h < p.H_I) raw = *(const u32x4*)(qh + 64 * half + 16 * g + 8 * j);
-#pragma unroll
-          for (int e2 = 0; e2 < 2; ++e2) {
-            float x[4];
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-              const uint32_t r = raw[2 * e2 + k];
-              x[2 * k] = fminf(fmaxf(__builtin_amdgcn_ldexpf(__uint_as_float(r << 16), -eh), -448.0f), 448.0f);
-              x[2 * k + 1] = fminf(fmaxf(__builtin_amdgcn_ldexpf(__uint_as_float(r & 0xffff0000u), -eh), -448.0f), 448.0f);
-            }
-            qa[mt][4 * half + 2 * j + e2] = (int)fp8x4(x[0], x[1], x[2], x[3]);
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int hr = mt * 16 + g * 4 + r;
-        w[mt][r] = hr < p.H_I ? p.head_w[(int64_t)tok * p.H_I + hr] : 0.0f;
-      }
-    }
+    mx_query<MT>(p, tok, g, c, qa, qe, w);
 
     float* srow = p.scores + (int64_t)tok * p.score_stride;
     const int pmask = (1 << sv.page_shift) - 1;
@@ -743,8 +750,13 @@ __device__ void wave_select_list(uint32_t* cand_, uint32_t L, int n, int K, int3
   });
 }
 
-template <int MT, int KS, bool FP8>
+// MX: MXFP8 keys (E4M3FN codes in the tile, the 4 E8M0 block exponents of
+// each key staged beside it) and an MX-quantised query, one scaled MFMA
+// (v_mfma_scale_f32_16x16x128_f8f6f4, as score_mx_kernel) per 16 heads x 16
+// keys x 128 dims instead of four bf16 ones.
+template <int MT, int KS, bool FP8, bool MX = false>
 __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreParams p) {
+  static_assert(!MX || (FP8 && KS == 4), "MXFP8 keys are e4m3 rows of 128");
   constexpr int ROWB = FP8 ? KS * 32 : KS * 64;  // key row bytes
   constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
   constexpr int TILEB = PF_KT * ROWB;
@@ -753,7 +765,7 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   constexpr int LOADS = INSTR / PF_TOKS;         // gathers per tile every wave has at least
   __shared__ uint32_t hist[PF_TOKS][SCORE_HIST_BINS];
   __shared__ __attribute__((aligned(1024))) uint8_t ring[PF_NBUF * TILEB];
-  __shared__ float ksc[PF_NBUF][PF_KT];
+  __shared__ float ksc[PF_NBUF][PF_KT];  // per-key fp32 scale, or (MX) the key's 4 exponent bytes
   __shared__ int pages[PF_MAX_PAGES];
 
   const int tid = threadIdx.x;
@@ -784,11 +796,15 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   }
 
   // ---- query operand: Q[h = 16 mt + c][kdim(ks, g) .. +8], head weights ------
+  // (MX: the quantised query of mx_query)
   bf16x8 qa[MT][KS];
+  i32x8 qx[MT];
+  int qe[MT];
   float w[MT][4];
   const uint16_t* qrow = p.q_idx + (int64_t)tok * p.H_I * p.d_I;
+  if constexpr (MX) mx_query<MT>(p, tok, g, c, qx, qe, w);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int mt = 0; mt < MT && !MX; ++mt) {
     const int hq = mt * 16 + c;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -820,10 +836,12 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
       const int ch = (lane % CPR) ^ pf_swz<CPR>(r);
       dma16(p.k_idx + cache_row_of(k * PF_KT + r) * ROWB + ch * 16, slot + i * 1024);
     }
-    if (p.k_scale && wave == PF_TOKS - 1) {
+    if ((MX || p.k_scale) && wave == PF_TOKS - 1) {
 #pragma unroll
-      for (int j = 0; j < PF_KT / 64; ++j)
-        dma4(p.k_scale + cache_row_of(k * PF_KT + j * 64 + lane), lds_addr(&ksc[k % PF_NBUF][j * 64]));
+      for (int j = 0; j < PF_KT / 64; ++j) {
+        const int64_t row = cache_row_of(k * PF_KT + j * 64 + lane);
+        dma4(MX ? (const void*)(p.k_exp + row * 4) : (const void*)(p.k_scale + row), lds_addr(&ksc[k % PF_NBUF][j * 64]));
+      }
     }
   };
 
@@ -859,6 +877,24 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
       float xs[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
+        if constexpr (MX) {
+          // key c of the sub-tile: codes 16 g .. +15 (chunk g) and 64 + 16 g
+          // .. +15 (chunk 4 + g), and the exponent byte of its block g
+          const u32x4 lo = *(const u32x4*)(tile + st * 16 * ROWB + boff[0]);
+          const u32x4 hi = *(const u32x4*)(tile + st * 16 * ROWB + boff[1]);
+          const i32x8 kb = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          const int ke = (int)((__float_as_uint(ksc[k % PF_NBUF][qd * 64 + st * 16 + c]) >> (8 * g)) & 0xffu);
+          float v = 0.0f;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qx[mt], kb, f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                              0, 0, 0, qe[mt], 0, ke);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v += w[mt][r] * relu(acc[r]);
+          }
+          xs[st] = v;
+          continue;
+        }
         bf16x8 kb[KS];
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
@@ -885,7 +921,7 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
       }
       float keep = reduce_scatter4(xs, g);
       const int sk = k * PF_KT + qd * 64 + 16 * g + c;  // this lane's key
-      if (p.k_scale) keep *= ksc[k % PF_NBUF][qd * 64 + 16 * g + c];
+      if (!MX && p.k_scale) keep *= ksc[k % PF_NBUF][qd * 64 + 16 * g + c];
       keep += 0.0f;  // -0 -> +0
       // only candidates enter the histogram: every key at or above the
       // bound is a candidate, so the counts of the bins at or above it (all
@@ -980,14 +1016,23 @@ hipError_t launch_score(const ScoreParams& p, int k_format, hipStream_t stream) 
   // the decode kernel accumulates the row histograms with atomics: clear
   // them first (a kernel, not a memset, so the call stays safe to capture in
   // a graph); the prefill kernel keeps its histograms in LDS
-  if (k_format == 2 || !score_selects(p.sv)) {
+  if (!score_selects(p.sv)) {
     const int64_t n4 = (int64_t)p.sv.num_tokens * SCORE_HIST_BINS / 4;
     const int64_t zblocks = std::min<int64_t>((n4 + 255) / 256, 2048);
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)zblocks), dim3(256), 0, stream, p.hist, n4);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   const TimerEvents t = timer_take(0);
-  if (k_format == 2) {  // MXFP8 keys, d_I = 128 (checked by the caller); any batch
+  if (k_format == 2 && score_selects(p.sv)) {  // MXFP8 keys (d_I = 128), prefill chunks
+    const dim3 grid(cdiv(p.sv.max_q_len, PF_TOKS), p.sv.num_seqs), block(PF_TOKS * WAVE);
+    switch (cdiv(p.H_I, 16)) {
+      case 1: return launch_kernel(score_prefill_kernel<1, 4, true, true>, grid, block, stream, t.start, t.stop, p);
+      case 2: return launch_kernel(score_prefill_kernel<2, 4, true, true>, grid, block, stream, t.start, t.stop, p);
+      case 3: return launch_kernel(score_prefill_kernel<3, 4, true, true>, grid, block, stream, t.start, t.stop, p);
+      default: return launch_kernel(score_prefill_kernel<4, 4, true, true>, grid, block, stream, t.start, t.stop, p);
+    }
+  }
+  if (k_format == 2) {  // MXFP8 keys, d_I = 128 (checked by the caller); decode batches
     const int kpw = MX_KPW;
     const dim3 grid(p.sv.num_tokens, cdiv(p.sv.max_ctx_len, kpw));
     switch (cdiv(p.H_I, 16)) {
