@@ -23,6 +23,7 @@ extrapolated.
 """
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -609,10 +610,18 @@ def cpu_baseline_long_prefill(inp, rows_per_chunk=8, min_seconds=10.0):
 
 
 def attn_source_digest():
+    """Digest of what the attention kernels are built from: attn.hip,
+    common.h, and the attention parameter block and tile size of
+    kernels.h (the rest of kernels.h belongs to other kernels)."""
+    csrc = os.path.join(ROOT, "indexer_selected_sparse_idx_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("attn.hip", "common.h", "kernels.h"):
-        with open(os.path.join(ROOT, "indexer_selected_sparse_idx_amd", "csrc", name), "rb") as f:
+    for name in ("attn.hip", "common.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    kh = open(os.path.join(csrc, "kernels.h")).read()
+    a = kh.index("struct AttnParams {")
+    h.update(kh[a:kh.index("};", a) + 2].encode())
+    h.update(re.search(r"constexpr int ATTN_TILE = \d+;", kh).group(0).encode())
     return h.hexdigest()[:16]
 
 

@@ -124,15 +124,23 @@ int64_t score_stride(const idx_seqs* s) {
   return ((int64_t)s->max_ctx_len + 63) / 64 * 64;
 }
 
-// score workspace: score rows, then the per-row key histograms
+// score workspace: score rows (one per token; for the prefill kernel one
+// per wave of its workgroups, see prefill_workgroups), then the per-row key
+// histograms (prefill: its work counter)
 size_t score_rows_bytes(const idx_seqs* s) {
-  return align_up((size_t)std::max(s->num_tokens, 0) * (size_t)score_stride(s) * sizeof(float));
+  const size_t rows = score_selects(make_view(s)) ? (size_t)prefill_workgroups(s->num_seqs, s->max_q_len) * 8
+                                                  : (size_t)std::max(s->num_tokens, 0);
+  return align_up(rows * (size_t)score_stride(s) * sizeof(float));
 }
+// (the prefill kernel keeps its histograms in LDS and selects itself: no
+// global histograms or selection counts)
 size_t score_hist_bytes(const idx_seqs* s) {
+  if (score_selects(make_view(s))) return 0;
   return align_up((size_t)std::max(s->num_tokens, 0) * SCORE_HIST_BINS * sizeof(uint32_t));
 }
 int topk_nch(const idx_seqs* s) { return std::max(1, (s->max_ctx_len + TOPK_CHUNK - 1) / TOPK_CHUNK); }
 size_t score_ws_bytes(const idx_seqs* s) {
+  if (score_selects(make_view(s))) return score_rows_bytes(s) + align_up(16);
   return score_rows_bytes(s) + score_hist_bytes(s) +
          align_up((size_t)std::max(s->num_tokens, 0) * topk_nch(s) * 2 * sizeof(uint32_t));
 }
@@ -168,6 +176,8 @@ int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int 
   sp.hist = reinterpret_cast<uint32_t*>(base + hist_off);
   sp.top_k = top_k;
   sp.out_idx = out_idx;
+  sp.pf_counter = reinterpret_cast<uint32_t*>(base + score_rows_bytes(seqs));  // (prefill kernel only)
+  sp.pf_items = seqs->num_seqs * ((seqs->max_q_len + 7) / 8);
   const int k_format = k_dtype == IDX_E4M3 ? 1 : k_dtype == IDX_MXFP8 ? 2 : 0;
   if (launch_score(sp, k_format, stream) != hipSuccess) return IDX_ERR_HIP;
   if (score_selects(sp.sv)) {

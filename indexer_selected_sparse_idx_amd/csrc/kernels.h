@@ -55,7 +55,19 @@ struct ScoreParams {
   uint32_t* hist;          // [T, SCORE_HIST_BINS] histogram of the top key bits (zeroed by the launcher)
   int top_k;
   int32_t* out_idx;        // [T, top_k]: written by the prefill kernel, which also selects
+  // prefill kernel: a fixed set of workgroups takes the token blocks (8
+  // query tokens of one sequence) from the counter *pf_counter (zeroed before
+  // the launch) until pf_items = num_seqs * max blocks are taken; wave w of
+  // workgroup j keeps its candidate list in score row 8 j + w, so the
+  // workspace holds 8 rows per workgroup, not one per token
+  uint32_t* pf_counter;
+  int pf_items;
 };
+
+// Workgroups of the prefill indexer: one per token block, at most
+// PREFILL_ROW_BUDGET / 8 (the candidate rows of the workspace).
+constexpr int PREFILL_ROW_BUDGET = 2048;
+int prefill_workgroups(int num_seqs, int max_q_len);
 
 struct TopkParams {
   SeqView sv;

@@ -774,12 +774,22 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   const int g = lane >> 4, c = lane & 15;
   const SeqView& sv = p.sv;
 
-  // ---- work: heaviest token blocks first -------------------------------------
-  const int b = blockIdx.y;
+  // ---- work items: token blocks, heaviest first, taken from a counter ---------
+  // Item i is block nqb - 1 - i / num_seqs of sequence i % num_seqs (the
+  // last blocks of every sequence first).  The loop ends for every wave of
+  // the workgroup at the same item (the counter passes pf_items).
+  __shared__ int next_item;
+  for (;;) {
+  if (tid == 0) next_item = (int)atomicAdd(p.pf_counter, 1u);
+  __syncthreads();  // (also: the previous item's selection is done with the ring and the histograms)
+  const int item = next_item;
+  __syncthreads();  // every wave holds the item before thread 0 takes the next one
+  if (item >= p.pf_items) break;
+  const int b = item % sv.num_seqs;
   const int ql = q_len(sv, b);
   const int nqb = cdiv(ql, PF_TOKS);
-  const int qb = nqb - 1 - (int)blockIdx.x;
-  if (qb < 0) return;
+  const int qb = nqb - 1 - item / sv.num_seqs;
+  if (qb < 0) continue;
   const int ctx = sv.ctx_len[b];
   const int i_tok = qb * PF_TOKS + wave;           // query index inside the sequence
   const bool active = i_tok < ql;
@@ -852,9 +862,9 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
 #pragma unroll
   for (int j = 0; j < NLD; ++j) boff[j] = c * ROWB + (((4 * j + g) ^ pf_swz<CPR>(c)) << 4);
 
-  // the row's candidate pairs (key, position); the row pitch holds two words
-  // per position
-  uint32_t* cand = (uint32_t*)(p.scores + (int64_t)tok * p.score_stride);
+  // the row's candidate pairs (key, position) in this wave's score row; the
+  // row pitch holds two words per position
+  uint32_t* cand = (uint32_t*)(p.scores + ((int64_t)blockIdx.x * PF_TOKS + wave) * p.score_stride);
   uint32_t* my_hist = hist[wave];
   const uint64_t below = (1ull << lane) - 1ull;
   uint32_t d1_run = 0;  // lower bound of the row's threshold bucket
@@ -953,6 +963,8 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     wave_select_list(cand, ncand, t + 1, p.top_k, p.out_idx + (int64_t)tok * p.top_k, my_hist,
                      (uint32_t*)ring + wave * LIST, LIST, lane);
   }
+  wait_vmcnt<0>();  // this row's stores are done before the next item writes it
+  }
 }
 
 // true when the prefill kernel can stage the block table of every row
@@ -970,16 +982,33 @@ bool prefill_fits(const SeqView& sv) {
 constexpr int PF_MIN_Q = 9;
 bool score_selects(const SeqView& sv) { return sv.max_q_len >= PF_MIN_Q && prefill_fits(sv); }
 
+int prefill_workgroups(int num_seqs, int max_q_len) {
+  const int64_t items = (int64_t)std::max(num_seqs, 1) * cdiv(std::max(max_q_len, 1), PF_TOKS);
+  return (int)std::min<int64_t>(items, PREFILL_ROW_BUDGET / PF_TOKS);
+}
+
+namespace {
+
+// The prefill kernel: its work counter cleared (a kernel, not a memset, so
+// the call stays safe to capture in a graph), then prefill_workgroups
+// workgroups.
+template <typename K>
+hipError_t launch_prefill(K kernel, const ScoreParams& p, hipStream_t stream, const TimerEvents& t) {
+  hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, stream, p.pf_counter, (int64_t)1);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  const dim3 grid(prefill_workgroups(p.sv.num_seqs, p.sv.max_q_len));
+  return launch_kernel(kernel, grid, dim3(PF_TOKS * WAVE), stream, t.start, t.stop, p);
+}
+
+}  // namespace
+
 namespace {
 
 template <int MT, int KS, bool FP8>
 hipError_t launch_mt(const ScoreParams& p, hipStream_t stream, const TimerEvents& t) {
   const SeqView& sv = p.sv;
   const bool decode = sv.max_q_len == 1;
-  if (score_selects(sv)) {
-    dim3 grid(cdiv(sv.max_q_len, PF_TOKS), sv.num_seqs);
-    return launch_kernel(score_prefill_kernel<MT, KS, FP8>, grid, dim3(PF_TOKS * WAVE), stream, t.start, t.stop, p);
-  }
+  if (score_selects(sv)) return launch_prefill(score_prefill_kernel<MT, KS, FP8>, p, stream, t);
   if (decode) {
     const int kpw = decode_kpw<FP8>();
     dim3 grid(cdiv(sv.max_ctx_len, kpw), sv.num_seqs);
@@ -1024,12 +1053,11 @@ hipError_t launch_score(const ScoreParams& p, int k_format, hipStream_t stream) 
   }
   const TimerEvents t = timer_take(0);
   if (k_format == 2 && score_selects(p.sv)) {  // MXFP8 keys (d_I = 128), prefill chunks
-    const dim3 grid(cdiv(p.sv.max_q_len, PF_TOKS), p.sv.num_seqs), block(PF_TOKS * WAVE);
     switch (cdiv(p.H_I, 16)) {
-      case 1: return launch_kernel(score_prefill_kernel<1, 4, true, true>, grid, block, stream, t.start, t.stop, p);
-      case 2: return launch_kernel(score_prefill_kernel<2, 4, true, true>, grid, block, stream, t.start, t.stop, p);
-      case 3: return launch_kernel(score_prefill_kernel<3, 4, true, true>, grid, block, stream, t.start, t.stop, p);
-      default: return launch_kernel(score_prefill_kernel<4, 4, true, true>, grid, block, stream, t.start, t.stop, p);
+      case 1: return launch_prefill(score_prefill_kernel<1, 4, true, true>, p, stream, t);
+      case 2: return launch_prefill(score_prefill_kernel<2, 4, true, true>, p, stream, t);
+      case 3: return launch_prefill(score_prefill_kernel<3, 4, true, true>, p, stream, t);
+      default: return launch_prefill(score_prefill_kernel<4, 4, true, true>, p, stream, t);
     }
   }
   if (k_format == 2) {  // MXFP8 keys, d_I = 128 (checked by the caller); decode batches

@@ -170,6 +170,23 @@ def test_workspace_sizes(L):
     assert L.sparse_mla_attn_workspace(ctypes.byref(big), 128, 2048) == 0  # no split needed
 
 
+def test_prefill_workspace_is_bounded(L):
+    # prefill batches (max_q_len >= 9) run the selecting prefill kernel with
+    # at most 256 workgroups taking token blocks from a counter: the
+    # workspace is 8 candidate rows per workgroup (one (key, position) pair
+    # per position plus a spare pair, padded to 64 positions) and the
+    # counter, whatever the token count
+    up = lambda b: -(-b // 256) * 256
+    for T in (4096, 16384):
+        s = seqs(num_seqs=1, num_tokens=T, cu_q=FAKE, max_q_len=T, max_ctx_len=65536, seq_stride=65536)
+        assert L.idx_score_topk_workspace(ctypes.byref(s), 64, 128, 2048) == up(2048 * 2 * 65600 * 4) + 256
+    s = seqs(num_seqs=32, num_tokens=32 * 512, cu_q=FAKE, max_q_len=512, max_ctx_len=131072, seq_stride=131072)
+    assert L.idx_score_topk_workspace(ctypes.byref(s), 64, 128, 2048) == up(2048 * 2 * 131136 * 4) + 256
+    # a short prefill batch: one workgroup per token block (2 sequences x 3)
+    s = seqs(num_seqs=2, num_tokens=40, cu_q=FAKE, max_q_len=20, max_ctx_len=1000, seq_stride=1000)
+    assert L.idx_score_topk_workspace(ctypes.byref(s), 64, 128, 2048) == up(6 * 8 * 2 * 1024 * 4) + 256
+
+
 def test_timer_arm_rejects_bad_kernel(L):
     assert L.idx_timer_arm(9, FAKE, FAKE) == -1
     assert L.idx_timer_arm(0, None, FAKE) == -1

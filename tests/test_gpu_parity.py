@@ -185,6 +185,27 @@ def test_prefill_rows_longer_than_the_packed_positions():
     _parity_all(generate(wl, "cuda"), U.TOL_BF16, "rows > 2^22")
 
 
+def test_prefill_many_sequences_more_blocks_than_workgroups():
+    # 300 sequences, q_len 9 .. 24 (2 or 3 token blocks each): more token
+    # blocks than the 256 workgroups of the prefill kernel, so workgroups take
+    # several blocks from the counter and reuse their candidate rows, and
+    # items past a sequence's blocks are skipped
+    rng = np.random.default_rng(39)
+    B = 300
+    ql = [int(x) for x in rng.integers(9, 25, B)]
+    ctx = [int(q + x) for q, x in zip(ql, rng.integers(0, 500, B))]
+    wl = Workload("prefill items", ctx, [{"seqs": list(range(B)), "q_len": ql}], top_k=64, H_I=8, d_I=64, H=8,
+                  seed=39)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "prefill items")
+
+
+def test_prefill_one_sequence_more_blocks_than_workgroups():
+    # 263 token blocks of one sequence over 256 workgroups
+    wl = Workload("prefill 263 blocks", [2500], [{"seqs": [0], "q_len": [2100]}], top_k=128, H_I=8, d_I=64, H=8,
+                  seed=40)
+    _parity_all(generate(wl, "cuda"), U.TOL_BF16, "prefill 263 blocks")
+
+
 def test_decode_all_equal_scores_whole_row_select():
     # every score 0: the threshold bucket holds the whole row (40,000 and 33,000
     # keys, more than the 24,576-entry candidate list), so decode selection
