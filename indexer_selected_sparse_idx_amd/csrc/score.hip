@@ -903,31 +903,54 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
             for (int r = 0; r < 4; ++r) v += w[mt][r] * relu(acc[r]);
           }
           xs[st] = v;
-          continue;
         }
-        bf16x8 kb[KS];
+      }
+      if constexpr (!MX) {
+        // Software pipeline over the 4 sub-tiles: step st issues the key
+        // operand reads of sub-tile st + 1, the MFMAs of sub-tile st, and,
+        // one value per slot between them, the ReLU / head-weight epilogue of
+        // sub-tile st - 1, whose MFMA results have long landed (in-order
+        // issue hides VALU work only between MFMAs).  The k-steps go
+        // outermost, so the MT accumulation chains interleave.
+        auto load_kb = [&](int st, bf16x8 (&kb)[KS]) {
 #pragma unroll
-        for (int j = 0; j < NLD; ++j) {
-          const u32x4 raw = *(const u32x4*)(tile + st * 16 * ROWB + boff[j]);
-          if (FP8) {
-            const u32x2 a0 = e4m3x4_to_bf16(raw[0], 1.0f), a1 = e4m3x4_to_bf16(raw[1], 1.0f);
-            const u32x2 a2 = e4m3x4_to_bf16(raw[2], 1.0f), a3 = e4m3x4_to_bf16(raw[3], 1.0f);
-            kb[2 * j] = as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]});
-            kb[2 * j + 1] = as_bf16x8(u32x4{a2[0], a2[1], a3[0], a3[1]});
-          } else {
-            kb[j] = as_bf16x8(raw);
+          for (int j = 0; j < NLD; ++j) {
+            const u32x4 raw = *(const u32x4*)(tile + st * 16 * ROWB + boff[j]);
+            if (FP8) {
+              const u32x2 a0 = e4m3x4_to_bf16(raw[0], 1.0f), a1 = e4m3x4_to_bf16(raw[1], 1.0f);
+              const u32x2 a2 = e4m3x4_to_bf16(raw[2], 1.0f), a3 = e4m3x4_to_bf16(raw[3], 1.0f);
+              kb[2 * j] = as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]});
+              kb[2 * j + 1] = as_bf16x8(u32x4{a2[0], a2[1], a3[0], a3[1]});
+            } else {
+              kb[j] = as_bf16x8(raw);
+            }
           }
+        };
+        constexpr int NMF = MT * KS, NV = MT * 4;       // MFMAs, epilogue values per sub-tile
+        constexpr int NSLOT = NMF > NV ? NMF : NV;
+        bf16x8 kb[2][KS];
+        f32x4 acc[2][MT];
+        load_kb(0, kb[0]);
+#pragma unroll
+        for (int st = 0; st <= 4; ++st) {
+          if (st + 1 < 4) load_kb(st + 1, kb[(st + 1) & 1]);
+          float v = 0.0f;
+#pragma unroll
+          for (int e = 0; e < NSLOT; ++e) {
+            if (st < 4 && e < NMF) {
+              const int ks = e / MT, mt = e % MT;
+              acc[st & 1][mt] = mfma16(qa[mt][ks], kb[st & 1][ks],
+                                       ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[st & 1][mt]);
+            }
+            if (st > 0) {
+#pragma unroll
+              for (int i = 0; i < NV; ++i)
+                if (i * NSLOT / NV == e) v += w[i / 4][i % 4] * relu(acc[(st - 1) & 1][i / 4][i % 4]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (st > 0) xs[st - 1] = v;
         }
-        float v = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = mfma16(qa[mt][ks], kb[ks], acc);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v += w[mt][r] * relu(acc[r]);
-        }
-        xs[st] = v;
       }
       float keep = reduce_scatter4(xs, g);
       const int sk = k * PF_KT + qd * 64 + 16 * g + c;  // this lane's key
