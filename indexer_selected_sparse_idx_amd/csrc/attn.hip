@@ -42,9 +42,10 @@
 // fp16, the queries are converted once, and the softmax numerators P go into
 // the P.V product as fp16 (11 significant bits, where bf16 carries 8).  A
 // value beyond the fp16 range makes the split's softmax sum or maximum
-// non-finite; the workgroup then recomputes the split with bf16 operands
-// (and, for bf16 rows, P split into two bf16 parts, hi + lo, so the product
-// runs twice on each V^T operand).
+// non-finite, and a head whose whole output is below 2^-14 was computed from
+// subnormal fp16 values; in both cases the workgroup recomputes the split
+// with bf16 operands (and, for bf16 rows, P split into two bf16 parts, hi +
+// lo, so the product runs twice on each V^T operand).
 #include <math.h>
 
 #include <algorithm>
@@ -472,15 +473,21 @@ __device__ __forceinline__ void v_phase(WaveAcc& a, const uint8_t* buf, const Ti
 // head): the head's largest |O| is brought just below 2^15, so every value
 // keeps 11 significant bits relative to that maximum (the split weights of
 // the merge are at most 1), at half the bytes of fp32 partials.
-// Returns false when some O value of the lane is not finite (a NaN from an
-// operand outside the fp16 range: the caller then recomputes the split in
-// bf16 and writes again).
+// Returns false when the fp16 run's result must be recomputed in bf16 (the
+// caller then writes again): some O value of the lane is not finite (a NaN
+// from an operand outside the fp16 range), or, with tiny_check, the head's
+// output is nonzero but below 2^-14 everywhere (its values came from fp16
+// subnormals, whose absolute spacing of 2^-24 is no longer small against
+// them; a whole output tensor that small would miss the tolerance).
+constexpr float TINY_OUT = 0x1p-14f;
+
 __device__ __forceinline__ bool write_result(const WaveAcc& a, const AttnParams& p, int tok, int split, int head,
-                                             bool head_ok, int h) {
+                                             bool head_ok, int h, bool tiny_check) {
   const float l_tot = pair_sum(a.l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   const float lse_v = l_tot > 0.0f ? (a.m_ref + __builtin_amdgcn_logf(l_tot)) * LN2 : -INFINITY;
   float osum = 0.0f;
+  float amax = 0.0f;
   if (p.num_splits == 1) {
     float* orow = p.out + ((int64_t)tok * p.H + (head_ok ? head : 0)) * LATENT;
 #pragma unroll
@@ -489,12 +496,13 @@ __device__ __forceinline__ bool write_result(const WaveAcc& a, const AttnParams&
       for (int i = 0; i < 4; ++i) {
         const f32x4 v = {a.o[nt][4 * i], a.o[nt][4 * i + 1], a.o[nt][4 * i + 2], a.o[nt][4 * i + 3]};
         osum += (v[0] + v[1]) + (v[2] + v[3]);
+        if (tiny_check) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
         if (head_ok) *(f32x4*)(orow + nt * 32 + i * 8 + h * 4) = v * inv;
       }
     if (head_ok && h == 0 && p.lse) p.lse[(int64_t)tok * p.H + head] = lse_v;
-    return __builtin_isfinite(osum);
+    amax = pair_max(amax) * inv;
+    return __builtin_isfinite(osum) && !(tiny_check && head_ok && amax > 0.0f && amax < TINY_OUT);
   }
-  float amax = 0.0f;
 #pragma unroll
   for (int nt = 0; nt < DV_TILES; ++nt)
 #pragma unroll
@@ -503,6 +511,7 @@ __device__ __forceinline__ bool write_result(const WaveAcc& a, const AttnParams&
       osum += a.o[nt][r];
     }
   amax = pair_max(amax) * inv;
+  const bool tiny = tiny_check && head_ok && amax > 0.0f && amax < TINY_OUT;
   // amax < 2^e; exponents below -100 are raised so the factor stays finite
   const int e = amax > 0.0f ? max(__builtin_amdgcn_frexp_expf(amax), -100) : 0;
   const float f = __builtin_amdgcn_ldexpf(inv, 15 - e);
@@ -518,7 +527,7 @@ __device__ __forceinline__ bool write_result(const WaveAcc& a, const AttnParams&
       *(f16x4*)(orow + nt * 32 + i * 8 + h * 4) = __builtin_convertvector(v, f16x4);
     }
   if (h == 0) *(f32x2*)(p.part_ls + 2 * pi) = f32x2{lse_v, sc};
-  return __builtin_isfinite(osum);
+  return __builtin_isfinite(osum) && !tiny;
 }
 
 // Work item of a workgroup.  Workgroups are dispatched round-robin over the
@@ -874,15 +883,16 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
   // overflowed, making the run non-finite as well) runs again against its
   // true maximum (a second run's maximum is its reference: no further
   // growth); a run that is non-finite otherwise, or whose O is, had an
-  // operand outside the fp16 range, and the split runs again in bf16
-  // (writing its result over the first one).
+  // operand outside the fp16 range, and a run whose O is nonzero but below
+  // 2^-14 for some head came from fp16 subnormals: the split runs again in
+  // bf16 (writing its result over the first one).
   uint32_t why = run(std::true_type());
   if (why & RUN_GROWTH) {
     m_ref = a.m_max;
     why = run(std::true_type());
   }
   if (why == 0) {
-    const bool ok = write_result(a, p, w.tok, w.split, head, head_ok, h);
+    const bool ok = write_result(a, p, w.tok, w.split, head, head_ok, h, true);
     if (!any_lane<NW>(!ok, wsum, wave, lane)) return;
   }
   // bf16 operands (the result written over the fp16 one, if any)
@@ -893,7 +903,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
     m_ref = a.m_max;
     run(std::false_type());
   }
-  write_result(a, p, w.tok, w.split, head, head_ok, h);
+  write_result(a, p, w.tok, w.split, head, head_ok, h, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -942,7 +952,7 @@ __global__ __launch_bounds__(WAVE, 1) void attn_bf16_single_kernel(AttnParams p)
     if (!(redo_reasons<1>(a, MAX_GROWTH, wsum, 0, lane) & RUN_GROWTH)) break;
     m_ref = a.m_max;
   }
-  write_result(a, p, w.tok, w.split, head, head_ok, h);
+  write_result(a, p, w.tok, w.split, head, head_ok, h, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -1018,7 +1028,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
     why = run(std::true_type());
   }
   if (why == 0) {
-    const bool ok = write_result(a, p, w.tok, w.split, head, head_ok, h);
+    const bool ok = write_result(a, p, w.tok, w.split, head, head_ok, h, true);
     if (!any_lane<NW>(!ok, wsum, wave, lane)) return;
   }
   m_ref = -INFINITY;
@@ -1029,7 +1039,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
     m_ref = a.m_max;
     run(std::false_type());
   }
-  write_result(a, p, w.tok, w.split, head, head_ok, h);
+  write_result(a, p, w.tok, w.split, head, head_ok, h, false);
 }
 
 // Merge split partials: lse = log sum_s exp(lse_s); O = sum_s exp(lse_s - lse) O_s,

@@ -448,3 +448,38 @@ def test_attention_values_beyond_fp16_range():
         # scores reach thousands (natural log units): lse compared relative to that scale
         U.check_attention(out.cpu().numpy(), lse.cpu().numpy() / 1e4, w_out, w_lse / 1e4, tol,
                           "beyond fp16 %s" % kv_dtype)
+
+
+def test_attention_values_below_fp16_normals():
+    """Rows whose latent values are all far below fp16's smallest normal
+    (2^-14): in fp16 they would be subnormals with an absolute spacing of
+    2^-24, coarse against values of about 1e-6, so every head's output is
+    tiny and the workgroup must recompute the split in bf16.  bf16 rows
+    times 2^-20; FP8 rows with tile scales of 2^-27 (values up to 448 x
+    2^-27, exact in bf16).  A decode batch with split rows and a prefill
+    chunk (one split per row)."""
+    import indexer_selected_sparse_idx_amd as lib
+    import oracle
+    for kv_dtype, tol in (("bf16", U.TOL_BF16), ("fp8_656", U.TOL_FP8)):
+        for q_len in (None, [40]):
+            calls = [{"seqs": [0, 1], "q_len": None}] if q_len is None else [{"seqs": [0], "q_len": q_len}]
+            wl = Workload("below fp16 normals", [3000, 700], calls, H=64, top_k=512, kv_dtype=kv_dtype, seed=41)
+            inp = generate(wl, "cuda")
+            call = inp.calls[0]
+            kv = inp.kv.clone()
+            if kv_dtype == "bf16":
+                kv = (kv.float() * 2.0 ** -20).to(torch.bfloat16)
+            else:
+                tiny = torch.from_numpy(np.full(4, 2.0 ** -27, np.float32).view(np.uint8)).cuda()
+                kv[:, 512:528] = tiny
+            inp.kv = kv
+            out, lse, idx = U.run_fused(inp, call)
+            torch.cuda.synchronize()
+            tokens = list(range(call.num_tokens))
+            w_idx, w_out, w_lse = U.oracle_rows(inp, call, tokens)
+            U.check_indices(idx.cpu().numpy(), w_idx, "tiny %s" % kv_dtype)
+            rms = float(np.sqrt(np.mean(w_out ** 2)))
+            assert 0.0 < rms < 2.0 ** -16                   # the case is what it claims
+            err = U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), w_out, w_lse, tol,
+                                    "tiny %s q_len %s" % (kv_dtype, q_len))
+            U.log("  tiny %s q_len %s: err/RMS %.2e" % (kv_dtype, q_len, err))
