@@ -36,11 +36,13 @@
 // the tile layout by the workgroup.  Splits (decode occupancy) are merged by
 // combine_kernel.
 //
-// Products run in fp16: every wave converts the bf16 bytes its own gathers
-// brought into LDS to fp16 in place (exact for |x| in [2^-14, 65504]; below
-// that the absolute error is at most 2^-25), FP8 rows are dequantised to
-// fp16, the queries are converted once, and the softmax numerators P go into
-// the P.V product as fp16 (11 significant bits, where bf16 carries 8).  A
+// Products run in fp16: every wave converts the bf16 latent values its own
+// gathers brought into LDS to fp16 in place (exact for |x| in [2^-14,
+// 65504]; below that the absolute error is at most 2^-25), FP8 rows are
+// dequantised to fp16, the queries' latent part is converted once, and the
+// softmax numerators P go into the P.V product as fp16 (11 significant bits,
+// where bf16 carries 8).  The rope part of S (4 of its 36 k-steps) stays in
+// bf16 on both operands.  A
 // value beyond the fp16 range makes the split's softmax sum or maximum
 // non-finite, and a head whose whole output is below 2^-14 was computed from
 // subnormal fp16 values; in both cases the workgroup recomputes the split
@@ -67,6 +69,7 @@ constexpr int BUF_BYTES = LAT_TILE_BYTES + ROPE_TILE_BYTES;
 constexpr int RAW_TILE_BYTES = TILE * FP8_ROW_BYTES;
 constexpr int RAW_CHUNKS = RAW_TILE_BYTES / 16;  // 16-byte chunks of a raw FP8 tile
 constexpr int KSTEPS = ROW / 16;                // 36 k-steps of the S product
+constexpr int LAT_KSTEPS = LATENT / 16;         // the first 32 cover the latent dims, the last 4 the rope
 constexpr int DV_TILES = LATENT / 32;           // 16 dv tiles of the P.V product
 constexpr float MAX_GROWTH = 64.0f;             // log2 growth of the max over the softmax reference tolerated
 constexpr float LN2 = 0.69314718055994530942f;
@@ -183,11 +186,12 @@ __device__ __forceinline__ void load_q(WaveAcc& a, const AttnParams& p, int tok,
     a.qb[ks] = v;
   }
 }
+// (the latent k-steps only: the rope part of S stays bf16 on both sides)
 template <bool F16>
 __device__ __forceinline__ void convert_q(WaveAcc& a) {
   if constexpr (F16) {
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
+    for (int ks = 0; ks < LAT_KSTEPS; ++ks)
 #pragma unroll
       for (int j = 0; j < 4; ++j) a.qb[ks][j] = bf16x2_to_f16x2(a.qb[ks][j]);
   }
@@ -267,7 +271,7 @@ constexpr int SPRE = 3;
 template <bool F16, int KS, typename F>
 __device__ __forceinline__ void s_step(f32x16& acc, u32x4 (&op)[SPRE], const WaveAcc& a, const uint8_t* buf,
                                        const TileAddr& ad, F& at_step) {
-  acc = mfma32<F16>(op[KS % SPRE], a.qb[KS], acc);
+  acc = mfma32<F16 && (KS < LAT_KSTEPS)>(op[KS % SPRE], a.qb[KS], acc);
   if constexpr (KS + SPRE < KSTEPS) op[KS % SPRE] = s_operand(buf, ad, KS + SPRE);
   at_step(std::integral_constant<int, KS>());
   __builtin_amdgcn_sched_barrier(0);
@@ -672,8 +676,19 @@ struct Bf16Rows {
     const int b = i / 9, m = i - 9 * b;
     return (m < 8 ? (8 * b + m) * LAT_STRIDE : LAT_TILE_BYTES + b * 1024) + 16 * lane;
   }
+  // (latent chunks only: the rope stays bf16)
   __device__ __forceinline__ static void convert_own(uint8_t* buf, int j, int wave, int lane) {
-    bf16x8_to_f16_lds(buf + own_off(j, wave, lane));
+    uint8_t* q = buf + own_off(j, wave, lane);
+    if constexpr (LOADS % 9 == 0) {
+      if (j % 9 < 8) bf16x8_to_f16_lds(q);
+    } else {  // the gather's place in its block depends on the wave: a select, not a branch
+      const bool lat = (wave * LOADS + j) % 9 < 8;
+      const u32x4 v = *(const u32x4*)q;
+      u32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = lat ? bf16x2_to_f16x2(v[e]) : v[e];
+      *(u32x4*)q = r;
+    }
   }
   __device__ __forceinline__ static void convert_all(uint8_t* buf, int wave, int lane) {
 #pragma unroll
@@ -687,11 +702,13 @@ struct Bf16Rows {
   // the write at CONV0 + 3 j + 1 (two chunks in flight).
   static constexpr int CONV_WAIT = 4, CONV0 = 6;
   static_assert(CONV0 + 3 * LOADS - 1 <= KSTEPS || LOADS > 9, "conversion fits the S phase");
+  // (with one block of 9 gathers per wave, gather 8 is the rope: not converted)
   template <int KS>
   __device__ __forceinline__ static void conv_step(u32x4 (&held)[2], uint8_t* buf, int wave, int lane) {
     constexpr int d = KS - CONV0 + 1;
     constexpr int j = d / 3, ph = d % 3;
-    if constexpr (d >= 0 && j < LOADS) {
+    static_assert(!SPREAD || LOADS == 9, "one block of 9 gathers per wave");
+    if constexpr (d >= 0 && j < 8) {
       if constexpr (ph == 0) held[j & 1] = *(const u32x4*)(buf + own_off(j, wave, lane));
       if constexpr (ph == 1) {
         held[j & 1][0] = bf16x2_to_f16x2(held[j & 1][0]);
@@ -745,14 +762,9 @@ struct Fp8Rows {
       *(u32x4*)(buf + lat_off(r, 2 * ch)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
       *(u32x4*)(buf + lat_off(r, 2 * ch + 1)) = u32x4{a2[0], a2[1], a3[0], a3[1]};
     }
-    for (int j = tid; j < TILE * 8; j += THREADS) {
+    for (int j = tid; j < TILE * 8; j += THREADS) {  // the rope, bf16 as stored
       const int r = j >> 3, ch = j & 7;
-      u32x4 v = *(const u32x4*)(raw + r * FP8_ROW_BYTES + LATENT + 16 + ch * 16);
-      if constexpr (F16) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(v[e]);
-      }
-      *(u32x4*)(buf + rope_off(r, ch)) = v;
+      *(u32x4*)(buf + rope_off(r, ch)) = *(const u32x4*)(raw + r * FP8_ROW_BYTES + LATENT + 16 + ch * 16);
     }
   }
 };
