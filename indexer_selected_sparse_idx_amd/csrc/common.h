@@ -95,9 +95,14 @@ __device__ __forceinline__ void dma16(const uint8_t* gptr, uint32_t lds_addr) {
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma16_s(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
+  // (the base goes through readfirstlane as well: where the compiler cannot
+  // prove it uniform it would otherwise hand the asm a VGPR pair)
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint64_t bs = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "v"(voff), "s"((const uint8_t*)(uintptr_t)bs), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory", "m0");
 }
 
