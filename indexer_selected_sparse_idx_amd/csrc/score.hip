@@ -832,19 +832,39 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   __syncthreads();  // histograms cleared, block-table entries staged
 
   // ---- gathers of tile k into ring slot k % PF_NBUF --------------------------
+  // Wave w issues the 1 KiB instructions w, w + 8, ... of the tile; lane l of
+  // instruction i reads one 16-byte chunk of key row i * RPI + l / CPR.  A
+  // contiguous cache whose tile lies wholly inside the causal range takes a
+  // scalar base per tile and a fixed 32-bit offset per lane and instruction.
+  constexpr int NG = INSTR / PF_TOKS;  // instructions per wave and tile
+  static_assert(INSTR % PF_TOKS == 0, "the gathers of a tile split evenly over the waves");
   const uint32_t ring_base = lds_addr(ring);
   auto cache_row_of = [&](int s) -> int64_t {
     s = min(s, t_last);  // keys past the last token are masked later; stay in bounds
     if (!paged) return (int64_t)b * sv.seq_stride + s;
     return ((int64_t)pages[s >> sv.page_shift] << sv.page_shift) + (s & ((1 << sv.page_shift) - 1));
   };
+  const uint8_t* seq_keys = p.k_idx + (int64_t)b * sv.seq_stride * ROWB;
+  uint32_t goff[NG];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int r = (wave + PF_TOKS * j) * RPI + lane / CPR;
+    goff[j] = (uint32_t)(r * ROWB + (((lane % CPR) ^ pf_swz<CPR>(r)) << 4));
+  }
   auto issue = [&](int k) {
     const uint32_t slot = ring_base + (k % PF_NBUF) * TILEB;
+    if (!paged && (k + 1) * PF_KT - 1 <= t_last) {
+      const uint8_t* tb = seq_keys + (int64_t)k * TILEB;
 #pragma unroll
-    for (int i = wave; i < INSTR; i += PF_TOKS) {
-      const int r = i * RPI + lane / CPR;
-      const int ch = (lane % CPR) ^ pf_swz<CPR>(r);
-      dma16(p.k_idx + cache_row_of(k * PF_KT + r) * ROWB + ch * 16, slot + i * 1024);
+      for (int j = 0; j < NG; ++j) dma16_s(tb, goff[j], slot + (wave + PF_TOKS * j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const int i = wave + PF_TOKS * j;
+        const int r = i * RPI + lane / CPR;
+        const int ch = (lane % CPR) ^ pf_swz<CPR>(r);
+        dma16(p.k_idx + cache_row_of(k * PF_KT + r) * ROWB + ch * 16, slot + i * 1024);
+      }
     }
     if ((MX || p.k_scale) && wave == PF_TOKS - 1) {
 #pragma unroll
@@ -870,6 +890,80 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   uint32_t d1_run = 0;  // lower bound of the row's threshold bucket
   uint32_t ncand = 0;   // candidate pairs written (wave-uniform)
 
+  // the 64 scores of quad qd of tile k (xs[st]: this lane group's partial of
+  // sub-tile st) into the histogram and the candidate list
+  auto quad_out = [&](int k, int qd, const float* xs) {
+    float keep = reduce_scatter4(*(const float(*)[4])xs, g);
+    const int sk = k * PF_KT + qd * 64 + 16 * g + c;  // this lane's key
+    if (!MX && p.k_scale) keep *= ksc[k % PF_NBUF][qd * 64 + 16 * g + c];
+    keep += 0.0f;  // -0 -> +0
+    // only candidates enter the histogram: every key at or above the
+    // bound is a candidate, so the counts of the bins at or above it (all
+    // that the bound refresh and the selection read) are the row's own
+    const uint32_t key = score_key(keep);
+    const uint32_t bin = key >> (32 - SCORE_HIST_BITS);
+    const uint64_t cm = __builtin_amdgcn_ballot_w64(sk <= t && bin >= d1_run);
+    if ((cm >> lane) & 1ull) {
+      *(u32x2*)(cand + 2 * (ncand + __popcll(cm & below))) = u32x2{key, (uint32_t)sk};
+      atomicAdd(&my_hist[bin], 1u);
+    }
+    ncand += __popcll(cm);
+  };
+
+  // Software pipeline over the NST sub-tiles of 16 keys from `tile` (4: one
+  // quad; 8: both quads of the tile): step st issues the key operand reads of
+  // sub-tile st + 1, the MFMAs of sub-tile st and, one value per slot between
+  // them, the ReLU / head-weight epilogue of sub-tile st - 1, whose MFMA
+  // results have long landed (in-order issue hides VALU work only between
+  // MFMAs).  The k-steps go outermost, so the MT accumulation chains
+  // interleave.  With both quads, the first quad's scores go out after step 4
+  // (its last epilogue then sits under the MFMAs of sub-tile 4).
+  auto load_kb = [&](const uint8_t* tile, int st, bf16x8 (&kb)[KS]) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const u32x4 raw = *(const u32x4*)(tile + st * 16 * ROWB + boff[j]);
+      if (FP8) {
+        const u32x2 a0 = e4m3x4_to_bf16(raw[0], 1.0f), a1 = e4m3x4_to_bf16(raw[1], 1.0f);
+        const u32x2 a2 = e4m3x4_to_bf16(raw[2], 1.0f), a3 = e4m3x4_to_bf16(raw[3], 1.0f);
+        kb[2 * j] = as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]});
+        kb[2 * j + 1] = as_bf16x8(u32x4{a2[0], a2[1], a3[0], a3[1]});
+      } else {
+        kb[j] = as_bf16x8(raw);
+      }
+    }
+  };
+  auto pipeline = [&](auto nst_tag, int k, const uint8_t* tile) {
+    constexpr int NST = decltype(nst_tag)::value;
+    constexpr int NMF = MT * KS, NV = MT * 4;  // MFMAs, epilogue values per sub-tile
+    constexpr int NSLOT = NMF > NV ? NMF : NV;
+    float xs[NST];
+    bf16x8 kb[2][KS];
+    f32x4 acc[2][MT];
+    load_kb(tile, 0, kb[0]);
+#pragma unroll
+    for (int st = 0; st <= NST; ++st) {
+      if (st + 1 < NST) load_kb(tile, st + 1, kb[(st + 1) & 1]);
+      float v = 0.0f;
+#pragma unroll
+      for (int e = 0; e < NSLOT; ++e) {
+        if (st < NST && e < NMF) {
+          const int ks = e / MT, mt = e % MT;
+          acc[st & 1][mt] = mfma16(qa[mt][ks], kb[st & 1][ks],
+                                   ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[st & 1][mt]);
+        }
+        if (st > 0) {
+#pragma unroll
+          for (int i = 0; i < NV; ++i)
+            if (i * NSLOT / NV == e) v += w[i / 4][i % 4] * relu(acc[(st - 1) & 1][i / 4][i % 4]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (st > 0) xs[st - 1] = v;
+      if (st == 4) quad_out(k, 0, xs);
+      if (st == 8) quad_out(k, 1, xs + 4);
+    }
+  };
+
 #pragma unroll
   for (int k = 0; k < PF_NBUF - 1; ++k)
     if (k < ntiles) issue(k);
@@ -880,94 +974,38 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     else wait_vmcnt<0>();
     __syncthreads();  // tile k visible; slot (k - 1) % PF_NBUF free
     if (k + PF_NBUF - 1 < ntiles) issue(k + PF_NBUF - 1);
+    const uint8_t* tile_k = ring + (k % PF_NBUF) * TILEB;
+    if constexpr (!MX) {
+      // 64-key quads inside the causal range of the wave's token
+      if (active && k * PF_KT + 64 <= t) pipeline(std::integral_constant<int, 8>(), k, tile_k);
+      else if (active && k * PF_KT <= t) pipeline(std::integral_constant<int, 4>(), k, tile_k);
+    } else {
 #pragma unroll
-    for (int qd = 0; qd < PF_KT / 64; ++qd) {  // 64-key quads of the tile
-    if (active && k * PF_KT + qd * 64 <= t) {
-      const uint8_t* tile = ring + (k % PF_NBUF) * TILEB + qd * 64 * ROWB;
-      float xs[4];
+      for (int qd = 0; qd < PF_KT / 64; ++qd) {  // 64-key quads of the tile
+        if (active && k * PF_KT + qd * 64 <= t) {
+          const uint8_t* tile = tile_k + qd * 64 * ROWB;
+          float xs[4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        if constexpr (MX) {
-          // key c of the sub-tile: codes 16 g .. +15 (chunk g) and 64 + 16 g
-          // .. +15 (chunk 4 + g), and the exponent byte of its block g
-          const u32x4 lo = *(const u32x4*)(tile + st * 16 * ROWB + boff[0]);
-          const u32x4 hi = *(const u32x4*)(tile + st * 16 * ROWB + boff[1]);
-          const i32x8 kb = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          const int ke = (int)((__float_as_uint(ksc[k % PF_NBUF][qd * 64 + st * 16 + c]) >> (8 * g)) & 0xffu);
-          float v = 0.0f;
+          for (int st = 0; st < 4; ++st) {
+            // key c of the sub-tile: codes 16 g .. +15 (chunk g) and 64 + 16 g
+            // .. +15 (chunk 4 + g), and the exponent byte of its block g
+            const u32x4 lo = *(const u32x4*)(tile + st * 16 * ROWB + boff[0]);
+            const u32x4 hi = *(const u32x4*)(tile + st * 16 * ROWB + boff[1]);
+            const i32x8 kb = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            const int ke = (int)((__float_as_uint(ksc[k % PF_NBUF][qd * 64 + st * 16 + c]) >> (8 * g)) & 0xffu);
+            float v = 0.0f;
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qx[mt], kb, f32x4{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                              0, 0, 0, qe[mt], 0, ke);
+            for (int mt = 0; mt < MT; ++mt) {
+              const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qx[mt], kb, f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                                0, 0, 0, qe[mt], 0, ke);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v += w[mt][r] * relu(acc[r]);
+              for (int r = 0; r < 4; ++r) v += w[mt][r] * relu(acc[r]);
+            }
+            xs[st] = v;
           }
-          xs[st] = v;
+          quad_out(k, qd, xs);
         }
       }
-      if constexpr (!MX) {
-        // Software pipeline over the 4 sub-tiles: step st issues the key
-        // operand reads of sub-tile st + 1, the MFMAs of sub-tile st, and,
-        // one value per slot between them, the ReLU / head-weight epilogue of
-        // sub-tile st - 1, whose MFMA results have long landed (in-order
-        // issue hides VALU work only between MFMAs).  The k-steps go
-        // outermost, so the MT accumulation chains interleave.
-        auto load_kb = [&](int st, bf16x8 (&kb)[KS]) {
-#pragma unroll
-          for (int j = 0; j < NLD; ++j) {
-            const u32x4 raw = *(const u32x4*)(tile + st * 16 * ROWB + boff[j]);
-            if (FP8) {
-              const u32x2 a0 = e4m3x4_to_bf16(raw[0], 1.0f), a1 = e4m3x4_to_bf16(raw[1], 1.0f);
-              const u32x2 a2 = e4m3x4_to_bf16(raw[2], 1.0f), a3 = e4m3x4_to_bf16(raw[3], 1.0f);
-              kb[2 * j] = as_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]});
-              kb[2 * j + 1] = as_bf16x8(u32x4{a2[0], a2[1], a3[0], a3[1]});
-            } else {
-              kb[j] = as_bf16x8(raw);
-            }
-          }
-        };
-        constexpr int NMF = MT * KS, NV = MT * 4;       // MFMAs, epilogue values per sub-tile
-        constexpr int NSLOT = NMF > NV ? NMF : NV;
-        bf16x8 kb[2][KS];
-        f32x4 acc[2][MT];
-        load_kb(0, kb[0]);
-#pragma unroll
-        for (int st = 0; st <= 4; ++st) {
-          if (st + 1 < 4) load_kb(st + 1, kb[(st + 1) & 1]);
-          float v = 0.0f;
-#pragma unroll
-          for (int e = 0; e < NSLOT; ++e) {
-            if (st < 4 && e < NMF) {
-              const int ks = e / MT, mt = e % MT;
-              acc[st & 1][mt] = mfma16(qa[mt][ks], kb[st & 1][ks],
-                                       ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[st & 1][mt]);
-            }
-            if (st > 0) {
-#pragma unroll
-              for (int i = 0; i < NV; ++i)
-                if (i * NSLOT / NV == e) v += w[i / 4][i % 4] * relu(acc[(st - 1) & 1][i / 4][i % 4]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          if (st > 0) xs[st - 1] = v;
-        }
-      }
-      float keep = reduce_scatter4(xs, g);
-      const int sk = k * PF_KT + qd * 64 + 16 * g + c;  // this lane's key
-      if (!MX && p.k_scale) keep *= ksc[k % PF_NBUF][qd * 64 + 16 * g + c];
-      keep += 0.0f;  // -0 -> +0
-      // only candidates enter the histogram: every key at or above the
-      // bound is a candidate, so the counts of the bins at or above it (all
-      // that the bound refresh and the selection read) are the row's own
-      const uint32_t key = score_key(keep);
-      const uint32_t bin = key >> (32 - SCORE_HIST_BITS);
-      const uint64_t cm = __builtin_amdgcn_ballot_w64(sk <= t && bin >= d1_run);
-      if ((cm >> lane) & 1ull) {
-        *(u32x2*)(cand + 2 * (ncand + __popcll(cm & below))) = u32x2{key, (uint32_t)sk};
-        atomicAdd(&my_hist[bin], 1u);
-      }
-      ncand += __popcll(cm);
-    }
     }
     // refresh the bound every 1024 keys: the bucket of the K-th largest key
     // of the row so far
