@@ -128,7 +128,7 @@ int64_t score_stride(const idx_seqs* s) {
 // per wave of its workgroups, see prefill_workgroups), then the per-row key
 // histograms (prefill: its work counter)
 size_t score_rows_bytes(const idx_seqs* s) {
-  const size_t rows = score_selects(make_view(s)) ? (size_t)prefill_workgroups(s->num_seqs, s->max_q_len) * 8
+  const size_t rows = score_selects(make_view(s)) ? (size_t)prefill_workgroups(s->num_seqs, s->max_q_len) * PREFILL_TOKS
                                                   : (size_t)std::max(s->num_tokens, 0);
   return align_up(rows * (size_t)score_stride(s) * sizeof(float));
 }
@@ -177,7 +177,7 @@ int run_indexer(const idx_seqs* seqs, const void* q_idx, const void* k_idx, int 
   sp.top_k = top_k;
   sp.out_idx = out_idx;
   sp.pf_counter = reinterpret_cast<uint32_t*>(base + score_rows_bytes(seqs));  // (prefill kernel only)
-  sp.pf_items = seqs->num_seqs * ((seqs->max_q_len + 7) / 8);
+  sp.pf_items = seqs->num_seqs * ((seqs->max_q_len + PREFILL_TOKS - 1) / PREFILL_TOKS);
   const int k_format = k_dtype == IDX_E4M3 ? 1 : k_dtype == IDX_MXFP8 ? 2 : 0;
   if (launch_score(sp, k_format, stream) != hipSuccess) return IDX_ERR_HIP;
   if (score_selects(sp.sv)) {

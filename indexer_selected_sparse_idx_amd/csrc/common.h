@@ -65,9 +65,9 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
 // Order-preserving map fp32 -> uint32 (larger float => larger key); -0 and
 // +0 map to the same key.
 __device__ __forceinline__ uint32_t score_key(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if (u == 0x80000000u) u = 0u;  // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __builtin_bit_cast(uint32_t, f + 0.0f);  // -0 -> +0; every other value unchanged
+  // negative: every bit flipped; otherwise: the sign bit set
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;

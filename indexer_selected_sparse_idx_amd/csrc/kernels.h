@@ -67,6 +67,7 @@ struct ScoreParams {
 // Workgroups of the prefill indexer: one per token block, at most
 // PREFILL_ROW_BUDGET / 8 (the candidate rows of the workspace).
 constexpr int PREFILL_ROW_BUDGET = 2048;
+constexpr int PREFILL_TOKS = 8;  // query tokens (= waves, = candidate rows) per prefill workgroup
 int prefill_workgroups(int num_seqs, int max_q_len);
 
 struct TopkParams {

@@ -467,7 +467,7 @@ __global__ void zero_kernel(uint32_t* p, int64_t n4) {
 // ch ^ swz(r) of the row, so the 16 keys of a sub-tile read at one logical
 // chunk (16 lanes of a 128-bit read) hit 16 different bank windows.
 // ---------------------------------------------------------------------------
-constexpr int PF_TOKS = 8;        // tokens (= waves) per workgroup
+constexpr int PF_TOKS = PREFILL_TOKS;  // tokens (= waves) per workgroup
 constexpr int PF_KT = 128;        // keys per tile (one barrier per tile)
 constexpr int PF_NBUF = 2;        // tile ring depth (tile k + 1 loads while tile k is computed)
 constexpr int PF_MAX_PAGES = 4096;  // block-table entries a workgroup can stage
@@ -896,15 +896,16 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     float keep = reduce_scatter4(*(const float(*)[4])xs, g);
     const int sk = k * PF_KT + qd * 64 + 16 * g + c;  // this lane's key
     if (!MX && p.k_scale) keep *= ksc[k % PF_NBUF][qd * 64 + 16 * g + c];
-    keep += 0.0f;  // -0 -> +0
     // only candidates enter the histogram: every key at or above the
     // bound is a candidate, so the counts of the bins at or above it (all
     // that the bound refresh and the selection read) are the row's own
     const uint32_t key = score_key(keep);
     const uint32_t bin = key >> (32 - SCORE_HIST_BITS);
-    const uint64_t cm = __builtin_amdgcn_ballot_w64(sk <= t && bin >= d1_run);
-    if ((cm >> lane) & 1ull) {
-      *(u32x2*)(cand + 2 * (ncand + __popcll(cm & below))) = u32x2{key, (uint32_t)sk};
+    const bool take = sk <= t && bin >= d1_run;
+    const uint64_t cm = __builtin_amdgcn_ballot_w64(take);
+    if (take) {
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(cm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cm, 0u));
+      *(u32x2*)(cand + 2 * (ncand + rank)) = u32x2{key, (uint32_t)sk};
       atomicAdd(&my_hist[bin], 1u);
     }
     ncand += __popcll(cm);
@@ -940,11 +941,13 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     bf16x8 kb[2][KS];
     f32x4 acc[2][MT];
     load_kb(tile, 0, kb[0]);
-#pragma unroll
+    // (unrolled in full: the indices of the operand and accumulator arrays
+    // must be constants, or the arrays leave the registers)
+#pragma clang loop unroll(full)
     for (int st = 0; st <= NST; ++st) {
       if (st + 1 < NST) load_kb(tile, st + 1, kb[(st + 1) & 1]);
       float v = 0.0f;
-#pragma unroll
+#pragma clang loop unroll(full)
       for (int e = 0; e < NSLOT; ++e) {
         if (st < NST && e < NMF) {
           const int ks = e / MT, mt = e % MT;
@@ -977,8 +980,13 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     const uint8_t* tile_k = ring + (k % PF_NBUF) * TILEB;
     if constexpr (!MX) {
       // 64-key quads inside the causal range of the wave's token
-      if (active && k * PF_KT + 64 <= t) pipeline(std::integral_constant<int, 8>(), k, tile_k);
-      else if (active && k * PF_KT <= t) pipeline(std::integral_constant<int, 4>(), k, tile_k);
+      if constexpr (PF_KT == 128) {
+        if (active && k * PF_KT + 64 <= t) pipeline(std::integral_constant<int, 8>(), k, tile_k);
+        else if (active && k * PF_KT <= t) pipeline(std::integral_constant<int, 4>(), k, tile_k);
+      } else {
+        static_assert(PF_KT == 64, "tiles of one or two quads");
+        if (active && k * PF_KT <= t) pipeline(std::integral_constant<int, 4>(), k, tile_k);
+      }
     } else {
 #pragma unroll
       for (int qd = 0; qd < PF_KT / 64; ++qd) {  // 64-key quads of the tile
