@@ -892,10 +892,12 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
 
   // the 64 scores of quad qd of tile k (xs[st]: this lane group's partial of
   // sub-tile st) into the histogram and the candidate list
-  auto quad_out = [&](int k, int qd, const float* xs) {
+  // (sc: the fp32 scale of the lane's key, e4m3 keys only)
+  auto quad_sc = [&](int k, int qd) { return ksc[k % PF_NBUF][qd * 64 + 16 * g + c]; };
+  auto quad_out = [&](int k, int qd, const float* xs, float sc) {
     float keep = reduce_scatter4(*(const float(*)[4])xs, g);
     const int sk = k * PF_KT + qd * 64 + 16 * g + c;  // this lane's key
-    if (!MX && p.k_scale) keep *= ksc[k % PF_NBUF][qd * 64 + 16 * g + c];
+    if (!MX && p.k_scale) keep *= sc;
     // only candidates enter the histogram: every key at or above the
     // bound is a candidate, so the counts of the bins at or above it (all
     // that the bound refresh and the selection read) are the row's own
@@ -918,7 +920,12 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   // results have long landed (in-order issue hides VALU work only between
   // MFMAs).  The k-steps go outermost, so the MT accumulation chains
   // interleave.  With both quads, the first quad's scores go out after step 4
-  // (its last epilogue then sits under the MFMAs of sub-tile 4).
+  // (its last epilogue then sits under the MFMAs of sub-tile 4), and the
+  // tile's last sub-tile is carried into the next tile: its epilogue runs
+  // under the MFMAs of the next tile's sub-tile 0 and the second quad's scores
+  // go out after them (carry: the tile index, or -1; acc[1] and xs[4 .. 6]
+  // hold its state, csc the key scale).  A partial tile, or the end of the
+  // row, flushes the carry first.
   auto load_kb = [&](const uint8_t* tile, int st, bf16x8 (&kb)[KS]) {
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
@@ -933,18 +940,36 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
       }
     }
   };
+  constexpr int NMF = MT * KS, NV = MT * 4;  // MFMAs, epilogue values per sub-tile
+  constexpr int NSLOT = NMF > NV ? NMF : NV;
+  float xs[8];
+  f32x4 acc[2][MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[1][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  int carry = -1;
+  float csc = 1.0f;
+  auto epilogue = [&](const f32x4 (&a)[MT]) {
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v += w[i / 4][i % 4] * relu(a[i / 4][i % 4]);
+    return v;
+  };
+  auto flush = [&]() {
+    if (carry >= 0) {
+      xs[7] = epilogue(acc[1]);
+      quad_out(carry, 1, xs + 4, csc);
+      carry = -1;
+    }
+  };
   auto pipeline = [&](auto nst_tag, int k, const uint8_t* tile) {
     constexpr int NST = decltype(nst_tag)::value;
-    constexpr int NMF = MT * KS, NV = MT * 4;  // MFMAs, epilogue values per sub-tile
-    constexpr int NSLOT = NMF > NV ? NMF : NV;
-    float xs[NST];
+    constexpr bool CARRY = NST == 8;
     bf16x8 kb[2][KS];
-    f32x4 acc[2][MT];
     load_kb(tile, 0, kb[0]);
     // (unrolled in full: the indices of the operand and accumulator arrays
     // must be constants, or the arrays leave the registers)
 #pragma clang loop unroll(full)
-    for (int st = 0; st <= NST; ++st) {
+    for (int st = 0; st <= (CARRY ? NST - 1 : NST); ++st) {
       if (st + 1 < NST) load_kb(tile, st + 1, kb[(st + 1) & 1]);
       float v = 0.0f;
 #pragma clang loop unroll(full)
@@ -954,16 +979,25 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
           acc[st & 1][mt] = mfma16(qa[mt][ks], kb[st & 1][ks],
                                    ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[st & 1][mt]);
         }
-        if (st > 0) {
+        // (step 0 of a carrying pipeline: the carried sub-tile, in acc[1])
+        if (st > 0 || CARRY) {
 #pragma unroll
           for (int i = 0; i < NV; ++i)
-            if (i * NSLOT / NV == e) v += w[i / 4][i % 4] * relu(acc[(st - 1) & 1][i / 4][i % 4]);
+            if (i * NSLOT / NV == e) v += w[i / 4][i % 4] * relu(acc[(st + 1) & 1][i / 4][i % 4]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       if (st > 0) xs[st - 1] = v;
-      if (st == 4) quad_out(k, 0, xs);
-      if (st == 8) quad_out(k, 1, xs + 4);
+      if (CARRY && st == 0) {
+        xs[7] = v;
+        if (carry >= 0) quad_out(carry, 1, xs + 4, csc);
+      }
+      if (st == 4) quad_out(k, 0, xs, quad_sc(k, 0));
+      if (!CARRY && st == 8) quad_out(k, 1, xs + 4, quad_sc(k, 1));
+    }
+    if constexpr (CARRY) {
+      carry = k;
+      csc = quad_sc(k, 1);
     }
   };
 
@@ -981,8 +1015,12 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     if constexpr (!MX) {
       // 64-key quads inside the causal range of the wave's token
       if constexpr (PF_KT == 128) {
-        if (active && k * PF_KT + 64 <= t) pipeline(std::integral_constant<int, 8>(), k, tile_k);
-        else if (active && k * PF_KT <= t) pipeline(std::integral_constant<int, 4>(), k, tile_k);
+        if (active && k * PF_KT + 64 <= t) {
+          pipeline(std::integral_constant<int, 8>(), k, tile_k);
+        } else if (active && k * PF_KT <= t) {
+          flush();
+          pipeline(std::integral_constant<int, 4>(), k, tile_k);
+        }
       } else {
         static_assert(PF_KT == 64, "tiles of one or two quads");
         if (active && k * PF_KT <= t) pipeline(std::integral_constant<int, 4>(), k, tile_k);
@@ -1011,7 +1049,7 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
             }
             xs[st] = v;
           }
-          quad_out(k, qd, xs);
+          quad_out(k, qd, xs, quad_sc(k, qd));
         }
       }
     }
@@ -1022,6 +1060,8 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
       wave_pick<SCORE_HIST_BINS>(my_hist, (uint32_t)p.top_k, lane, d1_run, a_, c_);
     }
   }
+
+  if constexpr (!MX) flush();
 
   // ---- each wave selects the Top-K of its token's complete row -----------------
   __syncthreads();
