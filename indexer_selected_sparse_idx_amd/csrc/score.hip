@@ -987,6 +987,9 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      // (kept here: a value used only on a conditional path would be computed
+      // there, after the MFMAs instead of between them)
+      asm volatile("" ::"v"(v));
       if (st > 0) xs[st - 1] = v;
       if (CARRY && st == 0) {
         xs[7] = v;
