@@ -471,6 +471,8 @@ constexpr int PF_TOKS = PREFILL_TOKS;  // tokens (= waves) per workgroup
 constexpr int PF_KT = 128;        // keys per tile (one barrier per tile)
 constexpr int PF_NBUF = 2;        // tile ring depth (tile k + 1 loads while tile k is computed)
 constexpr int PF_MAX_PAGES = 4096;  // block-table entries a workgroup can stage
+constexpr int PF_SUB_BITS = 8;      // finer bins inside the bound's bucket: key bits 20 .. 13
+constexpr int PF_SUB_BINS = 1 << PF_SUB_BITS;
 
 template <int CPR>
 __device__ __forceinline__ int pf_swz(int r) {
@@ -532,8 +534,10 @@ __device__ __forceinline__ float reduce_scatter4(const float (&x)[4], int g) {
 
 // The bin d of an NB-bin LDS histogram (bins in key order) holding the
 // want-th largest key: S(> d) < want <= S(>= d); above = S(> d), cnt = h[d].
+// Returns false (d, above, cnt unset) when the histogram holds fewer than
+// want keys.
 template <int NB, typename H>
-__device__ __forceinline__ void wave_pick(const H* h, uint32_t want, int lane, uint32_t& d, uint32_t& above,
+__device__ __forceinline__ bool wave_pick(const H* h, uint32_t want, int lane, uint32_t& d, uint32_t& above,
                                           uint32_t& cnt) {
   constexpr int PER = NB / WAVE;
   uint32_t v[PER];
@@ -561,10 +565,13 @@ __device__ __forceinline__ void wave_pick(const H* h, uint32_t want, int lane, u
     }
     run += v[j];
   }
-  const int src = __builtin_ctzll(__builtin_amdgcn_ballot_w64(found));
+  const uint64_t fm = __builtin_amdgcn_ballot_w64(found);
+  if (fm == 0) return false;
+  const int src = __builtin_ctzll(fm);
   d = __builtin_amdgcn_readlane(fd, src);
   above = __builtin_amdgcn_readlane(fa, src);
   cnt = __builtin_amdgcn_readlane(fc, src);
+  return true;
 }
 
 // The selection reads and writes the score rows and the output through
@@ -764,6 +771,7 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   constexpr int RPI = 1024 / ROWB;               // key rows per gather
   constexpr int LOADS = INSTR / PF_TOKS;         // gathers per tile every wave has at least
   __shared__ uint32_t hist[PF_TOKS][SCORE_HIST_BINS];
+  __shared__ uint32_t subh[PF_TOKS][PF_SUB_BINS];
   __shared__ __attribute__((aligned(1024))) uint8_t ring[PF_NBUF * TILEB];
   __shared__ float ksc[PF_NBUF][PF_KT];  // per-key fp32 scale, or (MX) the key's 4 exponent bytes
   __shared__ int pages[PF_MAX_PAGES];
@@ -800,6 +808,7 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   const bool paged = sv.block_table != nullptr;
 
   for (int i = tid; i < PF_TOKS * SCORE_HIST_BINS; i += PF_TOKS * WAVE) (&hist[0][0])[i] = 0u;
+  for (int i = tid; i < PF_TOKS * PF_SUB_BINS; i += PF_TOKS * WAVE) (&subh[0][0])[i] = 0u;
   if (paged) {
     const int np = (t_last >> sv.page_shift) + 1;
     for (int i = tid; i < np; i += PF_TOKS * WAVE) pages[i] = sv.block_table[(int64_t)b * sv.bt_stride + i];
@@ -886,9 +895,17 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   // row pitch holds two words per position
   uint32_t* cand = (uint32_t*)(p.scores + ((int64_t)blockIdx.x * PF_TOKS + wave) * p.score_stride);
   uint32_t* my_hist = hist[wave];
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint32_t d1_run = 0;  // lower bound of the row's threshold bucket
-  uint32_t ncand = 0;   // candidate pairs written (wave-uniform)
+  uint32_t* my_sub = subh[wave];
+  // The running bound: a lower bound of the K-th largest key of the row,
+  // from the histogram (the K-th largest key seen so far lies in bucket
+  // d1_cur) refined by my_sub, the histogram of key bits 20 .. 13 of the
+  // candidates of bucket d1_cur that arrived since it became the bucket.
+  // Those are a subset of the bucket's keys, so the threshold they give
+  // (enough keys above it, with the exact count of the buckets above) never
+  // exceeds the K-th largest.
+  uint32_t bound = 0;              // every key at or above it is a candidate
+  uint32_t d1_cur = 0xffffffffu;   // bucket that my_sub refines (none yet)
+  uint32_t ncand = 0;              // candidate pairs written (wave-uniform)
 
   // the 64 scores of quad qd of tile k (xs[st]: this lane group's partial of
   // sub-tile st) into the histogram and the candidate list
@@ -903,12 +920,13 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     // that the bound refresh and the selection read) are the row's own
     const uint32_t key = score_key(keep);
     const uint32_t bin = key >> (32 - SCORE_HIST_BITS);
-    const bool take = sk <= t && bin >= d1_run;
+    const bool take = sk <= t && key >= bound;
     const uint64_t cm = __builtin_amdgcn_ballot_w64(take);
     if (take) {
       const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(cm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cm, 0u));
       *(u32x2*)(cand + 2 * (ncand + rank)) = u32x2{key, (uint32_t)sk};
       atomicAdd(&my_hist[bin], 1u);
+      if (bin == d1_cur) atomicAdd(&my_sub[(key >> (32 - SCORE_HIST_BITS - PF_SUB_BITS)) & (PF_SUB_BINS - 1)], 1u);
     }
     ncand += __popcll(cm);
   };
@@ -1057,10 +1075,21 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
       }
     }
     // refresh the bound every 1024 keys: the bucket of the K-th largest key
-    // of the row so far
+    // of the row so far (all candidates: the K largest keys of a prefix are
+    // at or above the bound); within an unchanged bucket, the finer bins
     if (active && ((k + 1) * PF_KT) % 1024 == 0 && min(t + 1, (k + 1) * PF_KT) > p.top_k) {
-      uint32_t a_, c_;
-      wave_pick<SCORE_HIST_BINS>(my_hist, (uint32_t)p.top_k, lane, d1_run, a_, c_);
+      uint32_t d, above, cnt;
+      wave_pick<SCORE_HIST_BINS>(my_hist, (uint32_t)p.top_k, lane, d, above, cnt);
+      constexpr int SUB_SHIFT = 32 - SCORE_HIST_BITS - PF_SUB_BITS;
+      if (d != d1_cur) {
+        for (int j = lane; j < PF_SUB_BINS; j += WAVE) my_sub[j] = 0u;
+        d1_cur = d;
+        bound = max(bound, d << (32 - SCORE_HIST_BITS));
+      } else {
+        uint32_t sd, sa, sc_;
+        if (wave_pick<PF_SUB_BINS>(my_sub, (uint32_t)p.top_k - above, lane, sd, sa, sc_))
+          bound = max(bound, (d << (32 - SCORE_HIST_BITS)) | (sd << SUB_SHIFT));
+      }
     }
   }
 
