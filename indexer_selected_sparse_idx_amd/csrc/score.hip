@@ -532,45 +532,50 @@ __device__ __forceinline__ float reduce_scatter4(const float (&x)[4], int g) {
 // do the same without it.
 // ---------------------------------------------------------------------------
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: four
+// shifts inside each row of 16 lanes (lanes without a source add 0), then
+// the last lane of row 0 (and of row 2) added to rows 1 (and 3), then lane 31
+// to rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // The bin d of an NB-bin LDS histogram (bins in key order) holding the
 // want-th largest key: S(> d) < want <= S(>= d); above = S(> d), cnt = h[d].
 // Returns false (d, above, cnt unset) when the histogram holds fewer than
-// want keys.
+// want keys.  Lane l sums bins PER l .. PER l + PER - 1; a wave scan finds
+// the lane whose bins hold the want-th largest key, and its PER bins, read
+// again one per lane, a second scan.
 template <int NB, typename H>
 __device__ __forceinline__ bool wave_pick(const H* h, uint32_t want, int lane, uint32_t& d, uint32_t& above,
                                           uint32_t& cnt) {
   constexpr int PER = NB / WAVE;
-  uint32_t v[PER];
+  static_assert(PER >= 1 && PER <= WAVE, "one to 64 bins per lane");
   uint32_t tot = 0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    v[j] = h[PER * lane + j];
-    tot += v[j];
-  }
-  uint32_t suf = tot;  // keys in the bins of lanes >= this one
-#pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) {
-    const uint32_t o = __shfl_down(suf, off);
-    if (lane + off < WAVE) suf += o;
-  }
-  uint32_t run = suf - tot, fd = 0, fa = 0, fc = 0;
-  bool found = false;
-#pragma unroll
-  for (int j = PER - 1; j >= 0; --j) {
-    if (run < want && run + v[j] >= want) {
-      found = true;
-      fd = PER * lane + j;
-      fa = run;
-      fc = v[j];
-    }
-    run += v[j];
-  }
-  const uint64_t fm = __builtin_amdgcn_ballot_w64(found);
-  if (fm == 0) return false;
-  const int src = __builtin_ctzll(fm);
-  d = __builtin_amdgcn_readlane(fd, src);
-  above = __builtin_amdgcn_readlane(fa, src);
-  cnt = __builtin_amdgcn_readlane(fc, src);
+  for (int j = 0; j < PER; ++j) tot += h[PER * lane + j];
+  const uint32_t incl = wave_prefix_incl(tot);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, WAVE - 1);
+  const uint32_t suf = total - incl + tot;  // keys in the bins of lanes >= this one
+  const uint64_t m = __builtin_amdgcn_ballot_w64(suf >= want && suf - tot < want);
+  if (m == 0) return false;
+  const int L = __builtin_ctzll(m);
+  const uint32_t run = (uint32_t)__builtin_amdgcn_readlane((int)(suf - tot), L);  // keys above lane L's bins
+  const uint32_t bv = lane < PER ? h[PER * L + lane] : 0u;
+  const uint32_t bincl = wave_prefix_incl(bv);
+  const uint32_t btot = (uint32_t)__builtin_amdgcn_readlane((int)bincl, PER - 1);
+  const uint32_t bsuf = run + btot - bincl + bv;  // keys in bins >= PER L + lane
+  const uint64_t m2 = __builtin_amdgcn_ballot_w64(lane < PER && bsuf >= want && bsuf - bv < want);
+  const int i = __builtin_ctzll(m2);
+  d = (uint32_t)(PER * L + i);
+  above = (uint32_t)__builtin_amdgcn_readlane((int)(bsuf - bv), i);
+  cnt = (uint32_t)__builtin_amdgcn_readlane((int)bv, i);
   return true;
 }
 
