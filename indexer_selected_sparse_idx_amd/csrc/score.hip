@@ -558,8 +558,22 @@ __device__ __forceinline__ bool wave_pick(const H* h, uint32_t want, int lane, u
   constexpr int PER = NB / WAVE;
   static_assert(PER >= 1 && PER <= WAVE, "one to 64 bins per lane");
   uint32_t tot = 0;
+  if constexpr (PER % 4 == 0) {
+    // 16-byte reads, lane l's chunks in the order (c + l / (16 / CH)) mod CH:
+    // the 16 lanes of one LDS cycle then cover 16 distinct bank groups
+    // (lanes PER words apart would otherwise collide CH ways)
+    constexpr int CH = PER / 4;
+    constexpr int SPAN = CH >= 16 ? 1 : 16 / CH;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) tot += h[PER * lane + j];
+    for (int c = 0; c < CH; ++c) {
+      const int cc = (c + lane / SPAN) % CH;
+      const u32x4 v = *(const u32x4*)(h + PER * lane + 4 * cc);
+      tot += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) tot += h[PER * lane + j];
+  }
   const uint32_t incl = wave_prefix_incl(tot);
   const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, WAVE - 1);
   const uint32_t suf = total - incl + tot;  // keys in the bins of lanes >= this one
