@@ -924,6 +924,7 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   // exceeds the K-th largest.
   uint32_t bound = 0;              // every key at or above it is a candidate
   uint32_t d1_cur = 0xffffffffu;   // bucket that my_sub refines (none yet)
+  uint32_t above_cur = 0;          // candidates in the buckets above d1_cur
   uint32_t ncand = 0;              // candidate pairs written (wave-uniform)
 
   // the 64 scores of quad qd of tile k (xs[st]: this lane group's partial of
@@ -948,6 +949,7 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
       if (bin == d1_cur) atomicAdd(&my_sub[(key >> (32 - SCORE_HIST_BITS - PF_SUB_BITS)) & (PF_SUB_BINS - 1)], 1u);
     }
     ncand += __popcll(cm);
+    if (d1_cur != 0xffffffffu) above_cur += __popcll(__builtin_amdgcn_ballot_w64(take && bin > d1_cur));
   };
 
   // Software pipeline over the NST sub-tiles of 16 keys from `tile` (4: one
@@ -1097,16 +1099,41 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     // of the row so far (all candidates: the K largest keys of a prefix are
     // at or above the bound); within an unchanged bucket, the finer bins
     if (active && ((k + 1) * PF_KT) % 1024 == 0 && min(t + 1, (k + 1) * PF_KT) > p.top_k) {
-      uint32_t d, above, cnt;
-      wave_pick<SCORE_HIST_BINS>(my_hist, (uint32_t)p.top_k, lane, d, above, cnt);
+      // The bucket moves up from d1_cur while the candidates above it are
+      // K or more: a window of the 64 buckets above it and one wave scan
+      // find the new bucket (a pick over the whole histogram the first time,
+      // or when it moves further).
+      const uint32_t K = (uint32_t)p.top_k;
+      uint32_t d = d1_cur, above = above_cur;
+      bool moved = false;
+      if (d1_cur == 0xffffffffu) {
+        uint32_t cnt;
+        wave_pick<SCORE_HIST_BINS>(my_hist, K, lane, d, above, cnt);
+        moved = true;
+      } else if (above_cur >= K) {
+        const uint32_t b = d1_cur + 1 + lane;
+        const uint32_t wv = b < SCORE_HIST_BINS ? my_hist[b] : 0u;
+        const uint32_t pw = wave_prefix_incl(wv);  // candidates in buckets d1_cur + 1 .. b
+        const uint64_t mv = __builtin_amdgcn_ballot_w64(above_cur - pw < K);
+        if (mv != 0) {
+          const int i = __builtin_ctzll(mv);
+          d = d1_cur + 1 + i;
+          above = above_cur - (uint32_t)__builtin_amdgcn_readlane((int)pw, i);
+        } else {
+          uint32_t cnt;
+          wave_pick<SCORE_HIST_BINS>(my_hist, K, lane, d, above, cnt);
+        }
+        moved = true;
+      }
       constexpr int SUB_SHIFT = 32 - SCORE_HIST_BITS - PF_SUB_BITS;
-      if (d != d1_cur) {
+      if (moved) {
         for (int j = lane; j < PF_SUB_BINS; j += WAVE) my_sub[j] = 0u;
         d1_cur = d;
+        above_cur = above;
         bound = max(bound, d << (32 - SCORE_HIST_BITS));
       } else {
         uint32_t sd, sa, sc_;
-        if (wave_pick<PF_SUB_BINS>(my_sub, (uint32_t)p.top_k - above, lane, sd, sa, sc_))
+        if (wave_pick<PF_SUB_BINS>(my_sub, K - above, lane, sd, sa, sc_))
           bound = max(bound, (d << (32 - SCORE_HIST_BITS)) | (sd << SUB_SHIFT));
       }
     }
