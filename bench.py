@@ -450,20 +450,23 @@ KERNEL_NAMES = {0: "score", 1: "topk", 2: "attn", 3: "combine"}
 
 def timed_steps(lib, wl, inp, calls, bufs, scale, steps, flush):
     """`steps` steps (every call of the workload), each after a cache flush.
-    Returns per-step GPU milliseconds (events around the step on the
-    stream), the wall-clock seconds of the whole bracketed region (flushes
-    included), and per-kernel launch microseconds summed per step from the
-    events the library records around every launch of each kernel."""
+    Each step is bracketed by device synchronisations; its flush runs
+    before the opening one, outside the bracket.  Returns per-step GPU
+    milliseconds (events around the step on the stream), the wall-clock
+    seconds summed over the step brackets, and per-kernel launch
+    microseconds summed per step from the events the library records
+    around every launch of each kernel."""
     import torch
     # the split merge runs only in calls whose index lists are split (those
     # need an attention workspace); its timer is armed for those calls only
     merges = [lib.sparse_mla_attn_workspace(s, wl.H, wl.top_k) > 0 for _, s in calls]
     step_ev = event_pairs(steps)
     kev = {k: [event_pairs(len(calls)) for _ in range(steps)] for k in KERNEL_NAMES}
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
+    wall = 0.0
     for i in range(steps):
         flush()
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
         step_ev[i][0].record()
         for j, (c, s) in enumerate(calls):
             for k in KERNEL_NAMES:
@@ -471,8 +474,8 @@ def timed_steps(lib, wl, inp, calls, bufs, scale, steps, flush):
                     lib.idx_timer_arm(k, kev[k][i][j][0], kev[k][i][j][1])
             run_call(lib, wl, inp, c, s, bufs, scale)
         step_ev[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - wall0
     ms = [a.elapsed_time(b) for a, b in step_ev]
     kern = {}
     for k, name in KERNEL_NAMES.items():
@@ -707,7 +710,7 @@ def main():
     K = args.steps
     ms, wall, kern = timed_steps(lib, wl, inp, calls, bufs, scale, K, flush)
     u = workload_units(wl, calls)
-    ms_per_step = wall * 1e3 / K             # bracketed region / K (flushes included)
+    ms_per_step = wall * 1e3 / K             # the K step brackets / K (flushes outside them)
     attn_us = float(np.mean(kern["attn"]))   # summed over the 16 launches of a step
     score_us = float(np.mean(kern["score"]))
     n_launch = len(calls)
@@ -764,7 +767,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "step_ms": {"median": pct(ms, 50), "p10": pct(ms, 10), "p90": pct(ms, 90),
                     "note": "GPU events around each step, after a 1 GiB cache-flushing write; ms_per_step is "
-                            "the bracketed wall time / steps, flushes included"},
+                            "the wall time of the K step brackets / K (each step between two device "
+                            "synchronisations, its cache flush before the first)"},
         "roofline": {"bound": "mfma", "kernel": "sparse latent attention (prefill, bf16)",
                      "achieved": attn_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / BF16_PEAK_TFLOPS, "traffic": attn_counter_traffic(),
