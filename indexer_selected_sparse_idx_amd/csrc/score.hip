@@ -930,11 +930,35 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   // the 64 scores of quad qd of tile k (xs[st]: this lane group's partial of
   // sub-tile st) into the histogram and the candidate list
   // (sc: the fp32 scale of the lane's key, e4m3 keys only)
-  auto quad_sc = [&](int k, int qd) { return ksc[k % PF_NBUF][qd * 64 + 16 * g + c]; };
-  auto quad_out = [&](int k, int qd, const float* xs, float sc) {
-    float keep = reduce_scatter4(*(const float(*)[4])xs, g);
+  auto quad_sc = [&](int k, int qd) { return (!MX && p.k_scale) ? ksc[k % PF_NBUF][qd * 64 + 16 * g + c] : 1.0f; };
+  // The quad's arithmetic in five pieces (quad_part(s), s = 0 .. 4: the
+  // reduce-scatter of reduce_scatter4 and the key scale), so that a pipeline
+  // step can spread them over its MFMA slots; then quad_emit.
+  struct QuadState {
+    float a0, b0, a1, b1, y, z, keep;
+  };
+  auto quad_part = [&](int s, QuadState& q, const float* xs, float sc) {
+    if (s == 0) {
+      q.a0 = xs[0];
+      q.b0 = xs[1];
+      permlane16_swap(q.a0, q.b0);
+    } else if (s == 1) {
+      q.a1 = xs[2];
+      q.b1 = xs[3];
+      permlane16_swap(q.a1, q.b1);
+    } else if (s == 2) {
+      q.y = (g & 1) ? xs[1] + q.a0 : xs[0] + q.b0;
+    } else if (s == 3) {
+      q.z = (g & 1) ? xs[3] + q.a1 : xs[2] + q.b1;
+    } else if (s == 4) {
+      float ya = q.y, zb = q.z;
+      permlane32_swap(ya, zb);
+      q.keep = (g < 2 ? q.y + zb : q.z + ya) * sc;
+    }
+  };
+  constexpr int QPARTS = 5;
+  auto quad_emit = [&](int k, int qd, float keep) {
     const int sk = k * PF_KT + qd * 64 + 16 * g + c;  // this lane's key
-    if (!MX && p.k_scale) keep *= sc;
     // only candidates enter the histogram: every key at or above the
     // bound is a candidate, so the counts of the bins at or above it (all
     // that the bound refresh and the selection read) are the row's own
@@ -950,6 +974,12 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     }
     ncand += __popcll(cm);
     if (d1_cur != 0xffffffffu) above_cur += __popcll(__builtin_amdgcn_ballot_w64(take && bin > d1_cur));
+  };
+  auto quad_out = [&](int k, int qd, const float* xs, float sc) {
+    QuadState q;
+#pragma unroll
+    for (int s = 0; s < QPARTS; ++s) quad_part(s, q, xs, sc);
+    quad_emit(k, qd, q.keep);
   };
 
   // Software pipeline over the NST sub-tiles of 16 keys from `tile` (4: one
@@ -981,7 +1011,7 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   };
   constexpr int NMF = MT * KS, NV = MT * 4;  // MFMAs, epilogue values per sub-tile
   constexpr int NSLOT = NMF > NV ? NMF : NV;
-  float xs[8];
+  float xs[8] = {};
   f32x4 acc[2][MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[1][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -1004,6 +1034,10 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
     constexpr int NST = decltype(nst_tag)::value;
     constexpr bool CARRY = NST == 8;
     bf16x8 kb[2][KS];
+    // with both quads: the carried quad's pieces go into the slots of step 1,
+    // the first quad's into those of step 5; each is emitted after its step
+    QuadState qc, q0;
+    const float sc0 = quad_sc(k, 0);
     load_kb(tile, 0, kb[0]);
     // (unrolled in full: the indices of the operand and accumulator arrays
     // must be constants, or the arrays leave the registers)
@@ -1024,18 +1058,29 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
           for (int i = 0; i < NV; ++i)
             if (i * NSLOT / NV == e) v += w[i / 4][i % 4] * relu(acc[(st + 1) & 1][i / 4][i % 4]);
         }
+        if (CARRY && st == 1 && e < QPARTS) quad_part(e, qc, xs + 4, csc);
+        if (CARRY && st == 5 && e < QPARTS) quad_part(e, q0, xs, sc0);
         __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int e = NSLOT; e < QPARTS; ++e) {  // (pieces beyond the step's slots)
+        if (CARRY && st == 1) quad_part(e, qc, xs + 4, csc);
+        if (CARRY && st == 5) quad_part(e, q0, xs, sc0);
       }
       // (kept here: a value used only on a conditional path would be computed
       // there, after the MFMAs instead of between them)
       asm volatile("" ::"v"(v));
       if (st > 0) xs[st - 1] = v;
-      if (CARRY && st == 0) {
-        xs[7] = v;
-        if (carry >= 0) quad_out(carry, 1, xs + 4, csc);
+      if (CARRY && st == 0) xs[7] = v;
+      if (CARRY && st == 1) {
+        asm volatile("" ::"v"(qc.keep));
+        if (carry >= 0) quad_emit(carry, 1, qc.keep);
       }
-      if (st == 4) quad_out(k, 0, xs, quad_sc(k, 0));
-      if (!CARRY && st == 8) quad_out(k, 1, xs + 4, quad_sc(k, 1));
+      if (CARRY && st == 5) {
+        asm volatile("" ::"v"(q0.keep));
+        quad_emit(k, 0, q0.keep);
+      }
+      if (!CARRY && st == 4) quad_out(k, 0, xs, sc0);
     }
     if constexpr (CARRY) {
       carry = k;
