@@ -448,14 +448,16 @@ def event_pairs(n):
 KERNEL_NAMES = {0: "score", 1: "topk", 2: "attn", 3: "combine"}
 
 
-def timed_steps(lib, wl, inp, calls, bufs, scale, steps, flush):
+def timed_steps(lib, wl, inp, calls, bufs, scale, steps, flush, bracket=True):
     """`steps` steps (every call of the workload), each after a cache flush.
-    Each step is bracketed by device synchronisations; its flush runs
-    before the opening one, outside the bracket.  Returns per-step GPU
-    milliseconds (events around the step on the stream), the wall-clock
-    seconds summed over the step brackets, and per-kernel launch
-    microseconds summed per step from the events the library records
-    around every launch of each kernel."""
+    With `bracket`, each step is bracketed by device synchronisations and
+    its flush runs before the opening one, outside the bracket; without it
+    (steps of a fraction of a millisecond, whose launches would then show
+    as gaps) flushes and steps are queued back to back and the wall clock
+    spans the whole region.  Returns per-step GPU milliseconds (events
+    around the step on the stream), the wall-clock seconds of the timed
+    steps, and per-kernel launch microseconds summed per step from the
+    events the library records around every launch of each kernel."""
     import torch
     # the split merge runs only in calls whose index lists are split (those
     # need an attention workspace); its timer is armed for those calls only
@@ -463,10 +465,13 @@ def timed_steps(lib, wl, inp, calls, bufs, scale, steps, flush):
     step_ev = event_pairs(steps)
     kev = {k: [event_pairs(len(calls)) for _ in range(steps)] for k in KERNEL_NAMES}
     wall = 0.0
+    torch.cuda.synchronize()
+    region0 = time.perf_counter()
     for i in range(steps):
         flush()
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
+        if bracket:
+            torch.cuda.synchronize()
+            wall0 = time.perf_counter()
         step_ev[i][0].record()
         for j, (c, s) in enumerate(calls):
             for k in KERNEL_NAMES:
@@ -474,8 +479,12 @@ def timed_steps(lib, wl, inp, calls, bufs, scale, steps, flush):
                     lib.idx_timer_arm(k, kev[k][i][j][0], kev[k][i][j][1])
             run_call(lib, wl, inp, c, s, bufs, scale)
         step_ev[i][1].record()
-        torch.cuda.synchronize()
-        wall += time.perf_counter() - wall0
+        if bracket:
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - wall0
+    torch.cuda.synchronize()
+    if not bracket:
+        wall = time.perf_counter() - region0
     ms = [a.elapsed_time(b) for a, b in step_ev]
     kern = {}
     for k, name in KERNEL_NAMES.items():
@@ -501,7 +510,7 @@ def measure_config(n, steps, warmup, flush, dev):
         for c, s in calls:
             run_call(lib, wl, inp, c, s, bufs, scale)
     torch.cuda.synchronize()
-    ms, wall, kern = timed_steps(lib, wl, inp, calls, bufs, scale, steps, flush)
+    ms, wall, kern = timed_steps(lib, wl, inp, calls, bufs, scale, steps, flush, bracket=False)
     u = workload_units(wl, calls)
     med = pct(ms, 50)
     km = {k: float(np.median(v)) for k, v in kern.items()}
