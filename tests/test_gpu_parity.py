@@ -167,6 +167,27 @@ def test_prefill_threshold_ties_overflow_the_wave_list(d_I):
     _parity_all(inp, U.TOL_BF16, "ties prefill d_I=%d" % d_I)
 
 
+def test_prefill_bound_jumps_beyond_the_bucket_window():
+    # prefill kernel (16 query tokens over 6144 keys): the keys' scale grows
+    # by 2^17 every 1024 positions (scores H_I * k[0], k[0] = (1 + s % 7) *
+    # 2^(17 (s // 1024)), exact in fp32), so at each refresh of the running
+    # bound the bucket of the K-th largest key moves up by about 68 buckets:
+    # more than the 64-bucket window above the last one, and the refresh
+    # falls back to a pick over the whole histogram; ties (7 values per
+    # block) go to the lowest positions
+    n = 6144
+    wl = Workload("bound jumps", [n], [{"seqs": [0], "q_len": [16]}], top_k=256, H_I=16, H=16, seed=41)
+    inp = generate(wl, "cuda")
+    inp.q_idx.zero_()
+    inp.q_idx[:, :, 0] = 1.0
+    inp.head_w.fill_(1.0)
+    s = np.arange(n)
+    k0 = (1.0 + (s % 7)) * np.exp2(17.0 * (s // 1024))
+    rows = torch.arange(0, n, device="cuda")
+    inp.k_idx[rows, 0] = torch.from_numpy(k0.astype(np.float32)).to("cuda").to(torch.bfloat16)
+    _parity_all(inp, U.TOL_BF16, "bound jumps")
+
+
 def test_prefill_block_table_beyond_the_staged_pages():
     # pages of 1 position: 5000 pages for the longest sequence, more than the
     # 4096 block-table entries the prefill kernel stages, so the call takes
