@@ -479,32 +479,21 @@ __device__ __forceinline__ int pf_swz(int r) {
   return (r / (16 / CPR)) & (CPR - 1);
 }
 
-// Reduce-scatter over the 4 lane groups (rows of 16 lanes): x[st] holds the
-// group's partial for sub-tile st; the result at lane (g, c) is the sum over
-// the four groups of x[g].  Two butterfly steps with the gfx950 row swaps:
-// v_permlane16_swap exchanges rows 1, 3 of its first operand with rows 0, 2 of
-// its second, v_permlane32_swap the upper half of the first with the lower
-// half of the second.  (Inline asm: the builtins fold their two results into
-// one when both inputs are the same value.)
+// Reduce-scatter over the 4 lane groups (rows of 16 lanes; the prefill
+// kernel's quad_part): x[st] holds the group's partial for sub-tile st; the
+// result at lane (g, c) is the sum over the four groups of x[g].  Two
+// butterfly steps with the gfx950 row swaps: v_permlane16_swap exchanges rows
+// 1, 3 of its first operand with rows 0, 2 of its second (rows 2 r and 2 r + 1
+// exchange: even rows keep sub-tiles 0 and 2, odd rows 1 and 3),
+// v_permlane32_swap the upper half of the first with the lower half of the
+// second (rows r and r + 2 exchange: rows 0, 1 keep the first sum, rows 2, 3
+// the second).  (Inline asm: the builtins fold their two results into one
+// when both inputs are the same value.)
 __device__ __forceinline__ void permlane16_swap(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
 __device__ __forceinline__ void permlane32_swap(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ float reduce_scatter4(const float (&x)[4], int g) {
-  // step 1: rows 2 r and 2 r + 1 exchange; even rows keep sub-tiles 0 and 2,
-  // odd rows 1 and 3
-  float a0 = x[0], b0 = x[1], a1 = x[2], b1 = x[3];
-  permlane16_swap(a0, b0);  // a0: odd rows now hold the even row's x[1]; b0: even rows the odd row's x[0]
-  permlane16_swap(a1, b1);
-  const bool odd = g & 1;
-  const float y = odd ? x[1] + a0 : x[0] + b0;  // sub-tile 0 (even rows) or 1 (odd rows)
-  const float z = odd ? x[3] + a1 : x[2] + b1;  // sub-tile 2 or 3
-  // step 2: rows r and r + 2 exchange; rows 0, 1 keep y, rows 2, 3 keep z
-  float ya = y, zb = z;
-  permlane32_swap(ya, zb);  // ya: upper rows hold the lower rows' z; zb: lower rows the upper rows' y
-  return g < 2 ? y + zb : z + ya;
 }
 
 // ---------------------------------------------------------------------------
@@ -932,8 +921,8 @@ __global__ __launch_bounds__(PF_TOKS * WAVE, 1) void score_prefill_kernel(ScoreP
   // (sc: the fp32 scale of the lane's key, e4m3 keys only)
   auto quad_sc = [&](int k, int qd) { return (!MX && p.k_scale) ? ksc[k % PF_NBUF][qd * 64 + 16 * g + c] : 1.0f; };
   // The quad's arithmetic in five pieces (quad_part(s), s = 0 .. 4: the
-  // reduce-scatter of reduce_scatter4 and the key scale), so that a pipeline
-  // step can spread them over its MFMA slots; then quad_emit.
+  // reduce-scatter over the lane groups, then the key scale), so that a
+  // pipeline step can spread them over its MFMA slots; then quad_emit.
   struct QuadState {
     float a0, b0, a1, b1, y, z, keep;
   };
