@@ -534,6 +534,77 @@ __device__ __forceinline__ bool write_result(const WaveAcc& a, const AttnParams&
   return __builtin_isfinite(osum) && !tiny;
 }
 
+// write_result for the ring kernels, the same values through LDS: every wave
+// puts its heads' rows into `stage` (free once the split's tiles are done:
+// ROWS x 1040 bytes, a row of 512 fp16 or half a row of fp32 plus 16 bytes
+// of padding, so that the 16 lanes of a 128-bit write hit 16 bank groups),
+// and each head's row then goes to memory as one 1 KiB wave store (fp32
+// output in two halves).  Stored by lane, each 16-byte piece of a row is its
+// own partial-line write.  All waves of the workgroup must call it.
+template <int NW>
+__device__ __forceinline__ bool write_result_staged(const WaveAcc& a, const AttnParams& p, int tok, int split,
+                                                    int head, bool head_ok, int h, bool tiny_check, uint8_t* stage,
+                                                    int wave, int lane) {
+  constexpr int ROWS = NW * HPW;
+  constexpr int SROW = 1040;
+  const int r = wave * HPW + (lane & 31);  // this lane's head, the stage row
+  const float l_tot = pair_sum(a.l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse_v = l_tot > 0.0f ? (a.m_ref + __builtin_amdgcn_logf(l_tot)) * LN2 : -INFINITY;
+  float osum = 0.0f;
+  float amax = 0.0f;
+  if (p.num_splits == 1) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int nt = 8 * half; nt < 8 * half + 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 v = {a.o[nt][4 * i], a.o[nt][4 * i + 1], a.o[nt][4 * i + 2], a.o[nt][4 * i + 3]};
+          osum += (v[0] + v[1]) + (v[2] + v[3]);
+          if (tiny_check) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+          *(f32x4*)(stage + r * SROW + ((nt - 8 * half) * 32 + i * 8 + h * 4) * 4) = v * inv;
+        }
+      __syncthreads();
+      for (int rr = wave; rr < ROWS; rr += NW)
+        if (rr < p.H)
+          *(f32x4*)(p.out + ((int64_t)tok * p.H + rr) * LATENT + 256 * half + 4 * lane) =
+              *(const f32x4*)(stage + rr * SROW + 16 * lane);
+      __syncthreads();
+    }
+    if (head_ok && h == 0 && p.lse) p.lse[(int64_t)tok * p.H + head] = lse_v;
+    amax = pair_max(amax) * inv;
+    return __builtin_isfinite(osum) && !(tiny_check && head_ok && amax > 0.0f && amax < TINY_OUT);
+  }
+#pragma unroll
+  for (int nt = 0; nt < DV_TILES; ++nt)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      amax = fmaxf(amax, fabsf(a.o[nt][q]));
+      osum += a.o[nt][q];
+    }
+  amax = pair_max(amax) * inv;
+  const bool tiny = tiny_check && head_ok && amax > 0.0f && amax < TINY_OUT;
+  // amax < 2^e; exponents below -100 are raised so the factor stays finite
+  const int e = amax > 0.0f ? max(__builtin_amdgcn_frexp_expf(amax), -100) : 0;
+  const float f = __builtin_amdgcn_ldexpf(inv, 15 - e);
+  const float sc = amax > 0.0f ? __builtin_amdgcn_ldexpf(1.0f, e - 15) : 0.0f;
+#pragma unroll
+  for (int nt = 0; nt < DV_TILES; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = f32x4{a.o[nt][4 * i], a.o[nt][4 * i + 1], a.o[nt][4 * i + 2], a.o[nt][4 * i + 3]} * f;
+      *(f16x4*)(stage + r * SROW + (nt * 32 + i * 8 + h * 4) * 2) = __builtin_convertvector(v, f16x4);
+    }
+  __syncthreads();
+  const int64_t pi0 = ((int64_t)tok * p.num_splits + split) * p.H;
+  for (int rr = wave; rr < ROWS; rr += NW)
+    if (rr < p.H) *(u32x4*)(p.part_o + (pi0 + rr) * LATENT + 8 * lane) = *(const u32x4*)(stage + rr * SROW + 16 * lane);
+  __syncthreads();
+  if (head_ok && h == 0) *(f32x2*)(p.part_ls + 2 * (pi0 + head)) = f32x2{lse_v, sc};
+  return __builtin_isfinite(osum) && !tiny;
+}
+
 // Work item of a workgroup.  Workgroups are dispatched round-robin over the
 // 8 XCDs; the splits of one token are placed 8 blocks apart so that they
 // share an XCD (the token's queries are then read into one L2).
@@ -904,7 +975,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
     why = run(std::true_type());
   }
   if (why == 0) {
-    const bool ok = write_result(a, p, w.tok, w.split, head, head_ok, h, true);
+    const bool ok = write_result_staged<NW>(a, p, w.tok, w.split, head, head_ok, h, true, smem, wave, lane);
     if (!any_lane<NW>(!ok, wsum, wave, lane)) return;
   }
   // bf16 operands (the result written over the fp16 one, if any)
@@ -915,7 +986,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_bf16_kernel(AttnParams p) {
     m_ref = a.m_max;
     run(std::false_type());
   }
-  write_result(a, p, w.tok, w.split, head, head_ok, h, false);
+  write_result_staged<NW>(a, p, w.tok, w.split, head, head_ok, h, false, smem, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1040,7 +1111,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
     why = run(std::true_type());
   }
   if (why == 0) {
-    const bool ok = write_result(a, p, w.tok, w.split, head, head_ok, h, true);
+    const bool ok = write_result_staged<NW>(a, p, w.tok, w.split, head, head_ok, h, true, smem, wave, lane);
     if (!any_lane<NW>(!ok, wsum, wave, lane)) return;
   }
   m_ref = -INFINITY;
@@ -1051,7 +1122,7 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
     m_ref = a.m_max;
     run(std::false_type());
   }
-  write_result(a, p, w.tok, w.split, head, head_ok, h, false);
+  write_result_staged<NW>(a, p, w.tok, w.split, head, head_ok, h, false, smem, wave, lane);
 }
 
 // Merge split partials: lse = log sum_s exp(lse_s); O = sum_s exp(lse_s - lse) O_s,
