@@ -1127,46 +1127,56 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
 
 // Merge split partials: lse = log sum_s exp(lse_s); O = sum_s exp(lse_s - lse) O_s,
 // with O_s = scale_s * (stored fp16 values).
-// One workgroup per (token, pair of heads), 128 lanes per head, each lane 4
-// of the 512 values.  The partials of COMBINE_BATCH splits are loaded before
-// any is used (one memory latency per batch, not per split); a split whose
-// weight is zero (no valid entry) contributes nothing even if its values are
-// not finite.
+// One workgroup per (token, 4 heads), a wave per head, each lane 8 of the
+// 512 values (16-byte loads of the partials, two 16-byte stores).  The
+// (lse, scale) pairs and partials of COMBINE_BATCH splits are loaded before
+// any is used, so with at most COMBINE_BATCH splits the merge waits for one
+// memory latency; a split whose weight is zero (no valid entry) contributes
+// nothing even if its values are not finite.
 constexpr int COMBINE_BATCH = 4;
+constexpr int COMBINE_HEADS = 4;  // heads (waves) per workgroup
 
-__global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
-  const int th = blockIdx.x * 2 + (threadIdx.x >> 7);
+__global__ __launch_bounds__(COMBINE_HEADS * WAVE) void combine_kernel(AttnParams p) {
+  const int th = blockIdx.x * COMBINE_HEADS + (threadIdx.x >> 6);
   if (th >= p.sv.num_tokens * p.H) return;
-  const int lane = threadIdx.x & 127;
+  const int lane = threadIdx.x & 63;
   const int tok = th / p.H, h = th % p.H;
   const int S = p.num_splits;
   const int64_t base = (int64_t)tok * S * p.H + h;
-  float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, p.part_ls[2 * (base + (int64_t)s * p.H)]);
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  float wsum = 0.0f;
-  if (mx != -INFINITY) {
-    for (int s0 = 0; s0 < S; s0 += COMBINE_BATCH) {
-      f16x4 v[COMBINE_BATCH];
-      f32x2 ls[COMBINE_BATCH];
+  f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+  float wsum = 0.0f, mx = -INFINITY;
+  // (more splits than a batch: the maximum first, over every split)
+  if (S > COMBINE_BATCH)
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, p.part_ls[2 * (base + (int64_t)s * p.H)]);
+  for (int s0 = 0; s0 < S; s0 += COMBINE_BATCH) {
+    f16x8 v[COMBINE_BATCH];
+    f32x2 ls[COMBINE_BATCH];
 #pragma unroll
-      for (int j = 0; j < COMBINE_BATCH; ++j) {
-        const int64_t pi = base + (int64_t)min(s0 + j, S - 1) * p.H;
-        v[j] = *(const f16x4*)(p.part_o + pi * LATENT + lane * 4);
-        ls[j] = *(const f32x2*)(p.part_ls + 2 * pi);
-      }
+    for (int j = 0; j < COMBINE_BATCH; ++j) {
+      const int64_t pi = base + (int64_t)min(s0 + j, S - 1) * p.H;
+      v[j] = *(const f16x8*)(p.part_o + pi * LATENT + lane * 8);
+      ls[j] = *(const f32x2*)(p.part_ls + 2 * pi);
+    }
+    if (S <= COMBINE_BATCH) {
 #pragma unroll
-      for (int j = 0; j < COMBINE_BATCH; ++j) {
-        const float wgt = s0 + j < S ? expf(ls[j][0] - mx) : 0.0f;
-        if (wgt > 0.0f) {
-          wsum += wgt;
-          acc += (wgt * ls[j][1]) * __builtin_convertvector(v[j], f32x4);
-        }
+      for (int j = 0; j < COMBINE_BATCH; ++j) mx = fmaxf(mx, s0 + j < S ? ls[j][0] : -INFINITY);
+    }
+    if (mx == -INFINITY) break;
+#pragma unroll
+    for (int j = 0; j < COMBINE_BATCH; ++j) {
+      const float wgt = s0 + j < S ? expf(ls[j][0] - mx) : 0.0f;
+      if (wgt > 0.0f) {
+        wsum += wgt;
+        const float f = wgt * ls[j][1];
+        acc0 += f * f32x4{(float)v[j][0], (float)v[j][1], (float)v[j][2], (float)v[j][3]};
+        acc1 += f * f32x4{(float)v[j][4], (float)v[j][5], (float)v[j][6], (float)v[j][7]};
       }
     }
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  *(f32x4*)(p.out + ((int64_t)tok * p.H + h) * LATENT + lane * 4) = acc * inv;
+  float* orow = p.out + ((int64_t)tok * p.H + h) * LATENT + lane * 8;
+  *(f32x4*)orow = acc0 * inv;
+  *(f32x4*)(orow + 4) = acc1 * inv;
   if (lane == 0 && p.lse) p.lse[(int64_t)tok * p.H + h] = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
 }
 
@@ -1205,8 +1215,8 @@ hipError_t launch_attn(const AttnParams& p, bool kv_fp8, hipStream_t stream) {
   else e = launch_nw<4>(p, kv_fp8, stream, t);
   if (e != hipSuccess || p.num_splits == 1) return e;
   const TimerEvents tc = timer_take(3);
-  return launch_kernel(combine_kernel, dim3(cdiv(p.sv.num_tokens * p.H, 2)), dim3(256), stream, tc.start, tc.stop,
-                       p);
+  return launch_kernel(combine_kernel, dim3(cdiv(p.sv.num_tokens * p.H, COMBINE_HEADS)), dim3(COMBINE_HEADS * WAVE),
+                       stream, tc.start, tc.stop, p);
 }
 
 }  // namespace idxs
