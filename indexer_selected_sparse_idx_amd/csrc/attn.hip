@@ -811,11 +811,23 @@ struct Fp8Rows {
     }
   }
 
-  // 4 e4m3 codes times the tile scale -> 4 fp16 (or bf16) values, two dwords
+  // 4 e4m3 codes times the tile scale s -> 4 fp16 (or bf16) values, two
+  // dwords.  fp16: the gfx950 scaled conversion multiplies by the power of
+  // two 2^floor(log2 s) (it reads only the exponent field of s; exact while
+  // the product is an fp16 normal), then a packed fp16 multiply by the rest of
+  // s, m = s / 2^floor(log2 s) in [1, 2) rounded to fp16: two roundings of
+  // 2^-11 each instead of one, and a product beyond the fp16 range still ends
+  // as infinity.  bf16: fp32 products, rounded once.
   template <bool F16>
-  __device__ __forceinline__ static u32x2 dequant4(uint32_t w, float s) {
-    const f32x2 lo = e4m3x2_lo(w), hi = e4m3x2_hi(w);
-    return u32x2{pack2<F16>(lo[0] * s, lo[1] * s), pack2<F16>(hi[0] * s, hi[1] * s)};
+  __device__ __forceinline__ static u32x2 dequant4(uint32_t w, float s, f16x2 m) {
+    if constexpr (F16) {
+      const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, s, false) * m;
+      const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, s, true) * m;
+      return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    } else {
+      const f32x2 lo = e4m3x2_lo(w), hi = e4m3x2_hi(w);
+      return u32x2{pack2<F16>(lo[0] * s, lo[1] * s), pack2<F16>(hi[0] * s, hi[1] * s)};
+    }
   }
 
   // raw packed rows (512 e4m3, 4 fp32 tile scales, 64 bf16 rope) -> a tile of
@@ -828,8 +840,11 @@ struct Fp8Rows {
       const uint8_t* src = raw + r * FP8_ROW_BYTES;
       const u32x4 codes = *(const u32x4*)(src + ch * 16);
       const float sc = *(const float*)(src + LATENT + (ch >> 3) * 4);
-      const u32x2 a0 = dequant4<F16>(codes[0], sc), a1 = dequant4<F16>(codes[1], sc);
-      const u32x2 a2 = dequant4<F16>(codes[2], sc), a3 = dequant4<F16>(codes[3], sc);
+      // the mantissa of sc with a zero exponent: sc / 2^floor(log2 sc)
+      const _Float16 mh = (_Float16)__builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sc) & 0x007fffffu) | 0x3f800000u);
+      const f16x2 m = {mh, mh};
+      const u32x2 a0 = dequant4<F16>(codes[0], sc, m), a1 = dequant4<F16>(codes[1], sc, m);
+      const u32x2 a2 = dequant4<F16>(codes[2], sc, m), a3 = dequant4<F16>(codes[3], sc, m);
       *(u32x4*)(buf + lat_off(r, 2 * ch)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
       *(u32x4*)(buf + lat_off(r, 2 * ch + 1)) = u32x4{a2[0], a2[1], a3[0], a3[1]};
     }
@@ -1040,9 +1055,9 @@ __global__ __launch_bounds__(WAVE, 1) void attn_bf16_single_kernel(AttnParams p)
 
 // ---------------------------------------------------------------------------
 // FP8 rows: gathers into a raw NRAW-deep ring, dequantised by the workgroup
-// into a double-buffered tile: fp16 values (exact for the codes times their
-// tile scale inside the fp16 range) and fp16 P; bf16 values and bf16 P when
-// a value leaves the fp16 range.
+// into a double-buffered tile: fp16 values (the codes times their tile scale,
+// within two fp16 roundings inside the fp16 range) and fp16 P; bf16 values
+// and bf16 P when a value leaves the fp16 range.
 // ---------------------------------------------------------------------------
 template <int NW, int NRAW, int MAXE>
 __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
