@@ -66,8 +66,7 @@ constexpr int LAT_STRIDE = 1024 + 64;           // 512 bf16 per row, padded by f
 constexpr int LAT_TILE_BYTES = TILE * LAT_STRIDE;
 constexpr int ROPE_TILE_BYTES = TILE * 128;     // 64 bf16 per row
 constexpr int BUF_BYTES = LAT_TILE_BYTES + ROPE_TILE_BYTES;
-constexpr int RAW_TILE_BYTES = TILE * FP8_ROW_BYTES;
-constexpr int RAW_CHUNKS = RAW_TILE_BYTES / 16;  // 16-byte chunks of a raw FP8 tile
+constexpr int ROW_CHUNKS = FP8_ROW_BYTES / 16;   // 41 16-byte chunks of a packed FP8 row
 constexpr int KSTEPS = ROW / 16;                // 36 k-steps of the S product
 constexpr int LAT_KSTEPS = LATENT / 16;         // the first 32 cover the latent dims, the last 4 the rope
 constexpr int DV_TILES = LATENT / 32;           // 16 dv tiles of the P.V product
@@ -796,18 +795,28 @@ struct Bf16Rows {
 
 template <int NW>
 struct Fp8Rows {
-  static constexpr int INSTR = (RAW_CHUNKS + 63) / 64;  // 21 (the last one half full)
-  static constexpr int LOADS = INSTR / NW;
+  // Wave w gathers and dequantises the tile rows w, w + NW, .. of its own:
+  // the workgroup needs no barrier between a raw tile's arrival and its
+  // dequantisation, only the one per tile that publishes the fp16 tile.
+  static constexpr int ROWS = (TILE + NW - 1) / NW;               // rows of a wave (at most)
+  static constexpr int LOADS = (ROWS * ROW_CHUNKS + 63) / 64;      // gathers of a wave per tile
+  static constexpr int WAVE_BYTES = LOADS * 1024;                  // a wave's part of a raw slot
+  static constexpr int SLOT_BYTES = NW * WAVE_BYTES;               // one raw ring slot
 
+  // The wave's rows of one tile, packed at raw + wave * WAVE_BYTES (row j of
+  // the wave at j * FP8_ROW_BYTES).  Every lane of every gather is active, so
+  // each wave issues exactly LOADS gathers per tile (its waits count them):
+  // lanes past the wave's rows fetch their own first row again into the
+  // unused end of the wave's part.
   __device__ __forceinline__ static void issue(const AttnParams& p, const int* rows, uint32_t raw, int wave,
                                                int lane) {
+    const int nrows = (TILE - wave + NW - 1) / NW;
 #pragma unroll
-    for (int i = wave; i < INSTR; i += NW) {
+    for (int i = 0; i < LOADS; ++i) {
       const int q = i * 64 + lane;
-      if (q < RAW_CHUNKS) {
-        const int r = q / (FP8_ROW_BYTES / 16), ch = q % (FP8_ROW_BYTES / 16);
-        dma16(p.kv + (int64_t)rows[r] * FP8_ROW_BYTES + ch * 16, raw + i * 1024);
-      }
+      const int j = q / ROW_CHUNKS, ch = q % ROW_CHUNKS;
+      const int r = j < nrows ? wave + NW * j : wave;
+      dma16(p.kv + (int64_t)rows[r] * FP8_ROW_BYTES + ch * 16, raw + wave * WAVE_BYTES + i * 1024);
     }
   }
 
@@ -830,27 +839,42 @@ struct Fp8Rows {
     }
   }
 
-  // raw packed rows (512 e4m3, 4 fp32 tile scales, 64 bf16 rope) -> a tile of
-  // fp16 (or bf16) values
+  // 16 codes (latent chunk ch of the wave's row j) -> two 16-byte chunks of
+  // the tile layout.
   template <bool F16>
-  __device__ __forceinline__ static void convert(const uint8_t* raw, uint8_t* buf, int tid) {
-    constexpr int THREADS = NW * WAVE;
-    for (int j = tid; j < TILE * 32; j += THREADS) {
-      const int r = j >> 5, ch = j & 31;
-      const uint8_t* src = raw + r * FP8_ROW_BYTES;
-      const u32x4 codes = *(const u32x4*)(src + ch * 16);
-      const float sc = *(const float*)(src + LATENT + (ch >> 3) * 4);
-      // the mantissa of sc with a zero exponent: sc / 2^floor(log2 sc)
-      const _Float16 mh = (_Float16)__builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sc) & 0x007fffffu) | 0x3f800000u);
-      const f16x2 m = {mh, mh};
-      const u32x2 a0 = dequant4<F16>(codes[0], sc, m), a1 = dequant4<F16>(codes[1], sc, m);
-      const u32x2 a2 = dequant4<F16>(codes[2], sc, m), a3 = dequant4<F16>(codes[3], sc, m);
-      *(u32x4*)(buf + lat_off(r, 2 * ch)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
-      *(u32x4*)(buf + lat_off(r, 2 * ch + 1)) = u32x4{a2[0], a2[1], a3[0], a3[1]};
+  __device__ __forceinline__ static void lat_item(const uint8_t* own, uint8_t* buf, int wave, int j, int ch) {
+    const uint8_t* src = own + j * FP8_ROW_BYTES;
+    const u32x4 codes = *(const u32x4*)(src + ch * 16);
+    const float sc = *(const float*)(src + LATENT + (ch >> 3) * 4);
+    // the mantissa of sc with a zero exponent: sc / 2^floor(log2 sc)
+    const _Float16 mh = (_Float16)__builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sc) & 0x007fffffu) | 0x3f800000u);
+    const f16x2 m = {mh, mh};
+    const u32x2 a0 = dequant4<F16>(codes[0], sc, m), a1 = dequant4<F16>(codes[1], sc, m);
+    const u32x2 a2 = dequant4<F16>(codes[2], sc, m), a3 = dequant4<F16>(codes[3], sc, m);
+    const int r = wave + NW * j;
+    *(u32x4*)(buf + lat_off(r, 2 * ch)) = u32x4{a0[0], a0[1], a1[0], a1[1]};
+    *(u32x4*)(buf + lat_off(r, 2 * ch + 1)) = u32x4{a2[0], a2[1], a3[0], a3[1]};
+  }
+
+  // The wave's rows of a raw tile -> the fp16 (or bf16) tile layout; the rope
+  // is copied, bf16 as stored.  The caller has waited for the wave's gathers.
+  template <bool F16>
+  __device__ __forceinline__ static void convert_own(const uint8_t* raw, uint8_t* buf, int wave, int lane) {
+    const uint8_t* own = raw + wave * WAVE_BYTES;
+    const int nrows = (TILE - wave + NW - 1) / NW;
+    // (two items at a time: the queries, O^T and P are live around this)
+#pragma unroll 2
+    for (int i = 0; i < (ROWS * 32 + 63) / 64; ++i) {
+      const int q = i * 64 + lane;
+      if (q < nrows * 32) lat_item<F16>(own, buf, wave, q >> 5, q & 31);
     }
-    for (int j = tid; j < TILE * 8; j += THREADS) {  // the rope, bf16 as stored
-      const int r = j >> 3, ch = j & 7;
-      *(u32x4*)(buf + rope_off(r, ch)) = *(const u32x4*)(raw + r * FP8_ROW_BYTES + LATENT + 16 + ch * 16);
+#pragma unroll 2
+    for (int i = 0; i < (ROWS * 8 + 63) / 64; ++i) {
+      const int q = i * 64 + lane;
+      if (q < nrows * 8) {
+        const int j = q >> 3, ch = q & 7;
+        *(u32x4*)(buf + rope_off(wave + NW * j, ch)) = *(const u32x4*)(own + j * FP8_ROW_BYTES + LATENT + 16 + ch * 16);
+      }
     }
   }
 };
@@ -1054,19 +1078,19 @@ __global__ __launch_bounds__(WAVE, 1) void attn_bf16_single_kernel(AttnParams p)
 }
 
 // ---------------------------------------------------------------------------
-// FP8 rows: gathers into a raw NRAW-deep ring, dequantised by the workgroup
-// into a double-buffered tile: fp16 values (the codes times their tile scale,
-// within two fp16 roundings inside the fp16 range) and fp16 P; bf16 values
-// and bf16 P when a value leaves the fp16 range.
+// FP8 rows: gathers into a raw NRAW-deep ring, each wave dequantising the
+// rows it gathered into a double-buffered tile: fp16 values (the codes times
+// their tile scale, within two fp16 roundings inside the fp16 range) and fp16
+// P; bf16 values and bf16 P when a value leaves the fp16 range.
 // ---------------------------------------------------------------------------
 template <int NW, int NRAW, int MAXE>
 __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF_BYTES + NRAW * RAW_TILE_BYTES];
+  typedef Fp8Rows<NW> R;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF_BYTES + NRAW * R::SLOT_BYTES];
   __shared__ int rows_sh[MAXE];
   // per-wave scratch ints in the last raw ring slot: it is first filled by
   // the gather issued in iteration 0, after every use of the scratch
-  int* wsum = (int*)(smem + 2 * BUF_BYTES + (NRAW - 1) * RAW_TILE_BYTES);
-  typedef Fp8Rows<NW> R;
+  int* wsum = (int*)(smem + 2 * BUF_BYTES + (NRAW - 1) * R::SLOT_BYTES);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar branches)
@@ -1093,25 +1117,38 @@ __global__ __launch_bounds__(NW * WAVE, 1) void attn_fp8_kernel(AttnParams p) {
     reset_acc(a, m_ref);
 #pragma unroll
     for (int k = 0; k < NRAW - 1; ++k)
-      if (k < ntiles) R::issue(p, rows_sh + k * TILE, raw_base + k * RAW_TILE_BYTES, wave, lane);
-    // Iteration k: raw tile k ready (barrier: visible; raw slot (k - 1) % NRAW
-    // and tile slot k % 2 free), issue raw tile k + NRAW - 1, dequantise tile
-    // k, barrier, compute tile k.
-    for (int k = 0; k < ntiles; ++k) {
-      const int later = min(NRAW - 2, ntiles - 1 - k);
-      if (later >= 2) wait_vmcnt<2 * R::LOADS>();
-      else if (later == 1) wait_vmcnt<R::LOADS>();
+      if (k < ntiles) R::issue(p, rows_sh + k * TILE, raw_base + k * R::SLOT_BYTES, wave, lane);
+    // this wave's rows of tile 0 (the gathers of tile 1 stay in flight)
+    if (ntiles > 0) {
+      if (ntiles > 1) wait_vmcnt<R::LOADS>();
       else wait_vmcnt<0>();
+      R::template convert_own<F16>(raw, smem, wave, lane);
+    }
+    // Iteration k: one barrier (every wave's rows of tile k are in tile slot
+    // k % 2; every wave is done with tile k - 1, so slot (k + 1) % 2 is free),
+    // this wave's gathers of tile k + NRAW - 1 (into the raw slot of tile
+    // k - 1, which this wave dequantised in iteration k - 2), S and softmax
+    // of tile k, this wave's rows of tile k + 1 dequantised (its gathers
+    // waited for, those of the next tile left in flight), P.V of tile k.
+    // (Dequantising between the P.V MFMAs instead spilled registers and
+    // measured slower.)
+    for (int k = 0; k < ntiles; ++k) {
       __syncthreads();
       if (k + NRAW - 1 < ntiles)
-        R::issue(p, rows_sh + (k + NRAW - 1) * TILE, raw_base + ((k + NRAW - 1) % NRAW) * RAW_TILE_BYTES, wave,
+        R::issue(p, rows_sh + (k + NRAW - 1) * TILE, raw_base + ((k + NRAW - 1) % NRAW) * R::SLOT_BYTES, wave,
                  lane);
-      uint8_t* buf = smem + (k & 1) * BUF_BYTES;
-      R::template convert<F16>(raw + (k % NRAW) * RAW_TILE_BYTES, buf, tid);
-      __syncthreads();
+      const uint8_t* buf = smem + (k & 1) * BUF_BYTES;
       const f32x16 sc = s_phase<F16>(a, buf, ad, NoStep());
       SoftmaxTile<F16, false> sm(sc);
       sm.run_all(a, min(TILE, n - k * TILE), p.scale_log2, h);
+      if (k + 1 < ntiles) {
+        const int later = min(NRAW - 2, ntiles - 2 - k);  // tiles issued after tile k + 1
+        if (later >= 2) wait_vmcnt<2 * R::LOADS>();
+        else if (later == 1) wait_vmcnt<R::LOADS>();
+        else wait_vmcnt<0>();
+        R::template convert_own<F16>(raw + ((k + 1) % NRAW) * R::SLOT_BYTES, smem + ((k + 1) & 1) * BUF_BYTES,
+                                     wave, lane);
+      }
       v_phase<F16, false>(a, buf, ad, sm.op, NoStep());
     }
     o_fence(a);
