@@ -73,6 +73,19 @@ def test_prefill_small_topk_many_ties():
     _parity_all(generate(wl, "cuda"), U.TOL_BF16, "prefill-ties")
 
 
+def test_attention_three_waves_of_heads():
+    # 65 to 96 attention heads run three waves of 32 heads per workgroup (at
+    # 72 the third wave has 8 live heads); with FP8 rows each wave gathers
+    # and dequantises rows of its own, 11, 11 and 10 of a 32-row tile.  bf16
+    # and FP8 rows; decode rows split across workgroups, and a prefill chunk.
+    for H in (72, 96):
+        for kv_dtype, tol in (("bf16", U.TOL_BF16), ("fp8_656", U.TOL_FP8)):
+            wl = Workload("H=%d %s" % (H, kv_dtype), [3000, 900, 2049, 1200],
+                          [{"seqs": [0, 1, 2], "q_len": None}, {"seqs": [3], "q_len": [100]}],
+                          H=H, top_k=512, kv_dtype=kv_dtype, seed=50 + H)
+            _parity_all(generate(wl, "cuda"), tol, "H=%d %s" % (H, kv_dtype))
+
+
 def test_fp8_decode_scaled():
     inp = generate(config(4, scale=1 / 32), "cuda")          # B = 4, ctx = 4096, e4m3 keys, FP8 rows
     _parity_all(inp, U.TOL_FP8, "fp8-decode/32")
