@@ -330,9 +330,14 @@ def test_separate_entry_points_match_fused():
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
-def test_attention_skips_invalid_entries_and_empty_rows():
+@pytest.mark.parametrize("kv_dtype,H", [("bf16", 32), ("fp8_656", 32), ("fp8_656", 128)])
+def test_attention_skips_invalid_entries_and_empty_rows(kv_dtype, H):
+    # a row of 6 valid entries (one tile, partly filled) among invalid ones,
+    # and a row with none; FP8 rows at 32 heads (one wave gathers every row
+    # of a tile) and 128 (four waves, 8 rows each)
     import indexer_selected_sparse_idx_amd as lib
-    wl = Workload("attn-only", [100, 50], [{"seqs": [0, 1], "q_len": None}], H=32, top_k=70, seed=26)
+    wl = Workload("attn-only", [100, 50], [{"seqs": [0, 1], "q_len": None}], H=H, top_k=70, kv_dtype=kv_dtype,
+                  seed=26)
     inp = generate(wl, "cuda")
     call = inp.calls[0]
     s = U.lib_seqs(inp, call)
@@ -345,8 +350,9 @@ def test_attention_skips_invalid_entries_and_empty_rows():
     torch.cuda.synchronize()
     osq = U.oracle_seqs(inp, call)
     import oracle
-    w_out, w_lse = oracle.attention(osq, U.bits16(inp.q), U.host_raw(inp.kv), "bf16", idx.cpu().numpy(), U.SCALE)
-    U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), w_out, w_lse, U.TOL_BF16, "invalid entries")
+    w_out, w_lse = oracle.attention(osq, U.bits16(inp.q), U.host_raw(inp.kv), kv_dtype, idx.cpu().numpy(), U.SCALE)
+    tol = U.TOL_BF16 if kv_dtype == "bf16" else U.TOL_FP8
+    U.check_attention(out.cpu().numpy(), lse.cpu().numpy(), w_out, w_lse, tol, "invalid entries %s H=%d" % (kv_dtype, H))
     assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
 
 
