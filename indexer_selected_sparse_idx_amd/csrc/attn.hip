@@ -862,11 +862,21 @@ struct Fp8Rows {
   __device__ __forceinline__ static void convert_own(const uint8_t* raw, uint8_t* buf, int wave, int lane) {
     const uint8_t* own = raw + wave * WAVE_BYTES;
     const int nrows = (TILE - wave + NW - 1) / NW;
-    // (two items at a time: the queries, O^T and P are live around this)
+    constexpr int LAT_IT = (ROWS * 32 + 63) / 64;
+    if constexpr (LAT_IT <= 4) {
+#pragma unroll
+      for (int i = 0; i < LAT_IT; ++i) {
+        const int q = i * 64 + lane;
+        if (q < nrows * 32) lat_item<F16>(own, buf, wave, q >> 5, q & 31);
+      }
+    } else {
+      // (two items at a time: the queries, O^T and P are live around this,
+      // and a full unroll of 6 or more items spills)
 #pragma unroll 2
-    for (int i = 0; i < (ROWS * 32 + 63) / 64; ++i) {
-      const int q = i * 64 + lane;
-      if (q < nrows * 32) lat_item<F16>(own, buf, wave, q >> 5, q & 31);
+      for (int i = 0; i < LAT_IT; ++i) {
+        const int q = i * 64 + lane;
+        if (q < nrows * 32) lat_item<F16>(own, buf, wave, q >> 5, q & 31);
+      }
     }
 #pragma unroll 2
     for (int i = 0; i < (ROWS * 8 + 63) / 64; ++i) {
