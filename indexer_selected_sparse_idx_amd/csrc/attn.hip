@@ -32,9 +32,9 @@
 // tile, and the loop is software-pipelined: iteration k runs S of tile k
 // with the gathers of tile k + 2 spread over its k-steps, then P.V of tile
 // k - 1 with the softmax of tile k in the shadow of those MFMAs.  FP8 rows
-// (656 bytes) go into a raw LDS ring the same way and are dequantised into
-// the tile layout by the workgroup.  Splits (decode occupancy) are merged by
-// combine_kernel.
+// (656 bytes) go into a raw LDS ring the same way, each wave gathering whole
+// rows of its own and dequantising them into the tile layout.  Splits
+// (decode occupancy) are merged by combine_kernel.
 //
 // Products run in fp16: every wave converts the bf16 latent values its own
 // gathers brought into LDS to fp16 in place (exact for |x| in [2^-14,
@@ -42,12 +42,12 @@
 // dequantised to fp16, the queries' latent part is converted once, and the
 // softmax numerators P go into the P.V product as fp16 (11 significant bits,
 // where bf16 carries 8).  The rope part of S (4 of its 36 k-steps) stays in
-// bf16 on both operands.  A
-// value beyond the fp16 range makes the split's softmax sum or maximum
-// non-finite, and a head whose whole output is below 2^-14 was computed from
-// subnormal fp16 values; in both cases the workgroup recomputes the split
-// with bf16 operands (and, for bf16 rows, P split into two bf16 parts, hi +
-// lo, so the product runs twice on each V^T operand).
+// bf16 on both operands.  A value beyond the fp16 range makes the split's
+// softmax sum or maximum non-finite, and a head whose whole output is below
+// 2^-14 was computed from subnormal fp16 values; in both cases the
+// workgroup recomputes the split with bf16 operands (and, for bf16 rows, P
+// split into two bf16 parts, hi + lo, so the product runs twice on each V^T
+// operand).
 #include <math.h>
 
 #include <algorithm>
