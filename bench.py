@@ -788,7 +788,7 @@ def main():
             "indexer_prefill": {"ms_per_step": score_us / 1e3, "tflops": score_tflops,
                                 "mfma_frac": score_tflops / BF16_PEAK_TFLOPS,
                                 "note": "score kernel with its in-kernel Top-K, 16 launches per step"},
-            "north_star_fractions": {
+            "target_fractions": {
                 "decode_attention_hbm_decode_batch": others["decode_batch"]["attention_hbm_frac"],
                 "decode_attention_hbm_fp8_decode": others["fp8_decode"]["attention_hbm_frac"],
                 "indexer_prefill_mfma_long_prefill": score_tflops / BF16_PEAK_TFLOPS},
