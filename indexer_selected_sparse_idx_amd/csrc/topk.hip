@@ -26,8 +26,9 @@
 //    LDS histogram (merged after the pass): integer-valued scores put most
 //    keys into a few bins, and same-address atomics from different waves
 //    would serialise.  A one-wave suffix scan picks the digit whose bucket
-//    holds the m-th largest key; when that bucket is taken whole the passes
-//    stop early.
+//    holds the m-th largest key; when that bucket is taken whole, or when
+//    no counted key has a bit set below the digit (the keys of the bucket
+//    are then all equal), the passes stop early.
 // b. Ordered compaction: each wave owns a contiguous segment of the list,
 //    counts its keys above / equal to the threshold, and after one exclusive
 //    scan over the waves emits them in position order (a wavefront prefix
@@ -123,7 +124,8 @@ template <bool IN_LDS, int FIXED, typename Pos>
 __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out, const Pos& pos, uint32_t* hist,
                            uint32_t* whist, uint32_t* wcnt, uint32_t prefix0) {
   typedef Digits<FIXED> D;
-  __shared__ uint32_t sh_digit, sh_above, sh_whole;
+  __shared__ uint32_t sh_digit, sh_above, sh_whole, sh_zero;
+  __shared__ uint32_t wlow[TOPK_WAVES];  // per wave: OR of the counted keys' bits below the digit
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -137,6 +139,8 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
   for (int pass = 0; pass < D::PASSES; ++pass) {
     const int shift = D::shift(pass);
     const uint32_t dmask = (1u << D::width(pass)) - 1u;
+    const uint32_t lowmask = (1u << shift) - 1u;
+    uint32_t low = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) my_hist[lane + 64 * j] = 0;
     for (int i0 = 4 * tid; i0 < n4; i0 += 4 * TOPK_THREADS * UNROLL) {
@@ -153,10 +157,16 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
         for (int e = 0; e < 4; ++e) {
           const uint32_t key = k[u][e];
           const bool in = i + e < n && (cshift >= 32 || (key >> cshift) == prefix);
-          if (in) atomicAdd(&my_hist[(key >> shift) & dmask], 1u);
+          if (in) {
+            atomicAdd(&my_hist[(key >> shift) & dmask], 1u);
+            low |= key & lowmask;
+          }
         }
       }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) low |= __shfl_xor(low, off);
+    if (lane == 0) wlow[wave] = low;
     __syncthreads();
     if (tid < 256) {
       uint32_t tot = 0;
@@ -185,19 +195,29 @@ __device__ void select_row(const Keys<IN_LDS>& keys, int n, int m, int32_t* out,
       else if (s2 >= rem && s3 < rem) { d = 4 * lane + 2; above = s3; cnt = h2; }
       else if (s1 >= rem && s2 < rem) { d = 4 * lane + 1; above = s2; cnt = h1; }
       else if (s0 >= rem && s1 < rem) { d = 4 * lane; above = s1; cnt = h0; }
+      // no counted key has a bit set below this digit (integer-valued
+      // scores leave the low mantissa bits empty): the later passes would
+      // each pick digit 0 with nothing above it
+      const bool zero = __builtin_amdgcn_ballot_w64(lane < TOPK_WAVES && wlow[lane] != 0u) == 0;
       if (d >= 0) {
         sh_digit = d;
         sh_above = above;
         sh_whole = (cnt == rem - above);  // the whole bucket is taken
+        sh_zero = zero;
       }
     }
     __syncthreads();
     prefix = (prefix << D::width(pass)) | sh_digit;
     rem -= sh_above;
     cshift = shift;
-    const bool whole = sh_whole;
+    const bool whole = sh_whole, zero = sh_zero;
     __syncthreads();
     if (whole) break;
+    if (zero) {  // the keys of the chosen bucket are all equal to prefix << shift
+      prefix <<= shift;
+      cshift = 0;
+      break;
+    }
   }
   // compare keys on their bits >= cshift against `prefix`
   const uint32_t need = rem;       // prefix-equal positions to take
